@@ -1,0 +1,178 @@
+/*
+ * flare.h - C ABI of the MI355X (gfx950) FLARE / FLARE++ token-mixer library.
+ *
+ * The operator (page "FLARE++: Low-Rank Attention with Dynamic Attention
+ * Routing", section 3, Method):
+ *   - every step is one scaled dot-product attention (SDPA) call,
+ *     SDPA(Q, K, V) = softmax(scale * Q K^T) V with the softmax along each
+ *     query's row ("Full self-attention");
+ *   - FLARE encode:  Z_h = SDPA(Q_h, K_h, V_h), M latents gather N tokens;
+ *     FLARE decode:  Y_h = SDPA(K_h, Q_h, Z_h), the latents are sent back
+ *     ("FLARE: fixed-query latent routing", equation 5 is the encoder);
+ *   - FLARE++ query synthesis: Q_h(X) = SDPA(seeds_h, eK_h, eV_h) with learned
+ *     per-head seeds and the extra projections eK = X W_eK, eV = X W_eV
+ *     ("FLARE++: dynamic token routing", equations 7 and 8);
+ *   - the encoder exposes its row log-normaliser, which makes a token-split
+ *     encode mergeable exactly by logsumexp ("Multi-GPU context parallelism").
+ *
+ * Conventions shared by every call:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; scratch comes from a caller
+ *     workspace sized by the matching *_workspace_size function.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream).  Outputs are ready when the stream reaches
+ *     that point.  Calls are thread-safe; the library holds no mutable state.
+ *   - Argument errors are reported synchronously, before anything is
+ *     launched, and leave every output untouched.  FLARE_E_HIP means a launch
+ *     failed; outputs are then undefined.
+ *   - Sizes: B >= 1, H >= 1, 1 <= M <= 512, N >= 1, D in {16, 32}.
+ *   - scale: multiplier of the dot products inside the softmax; 0 selects the
+ *     pages' 1/sqrt(D).  Any other finite value is used as given.
+ *   - Precision: bf16 inputs are multiplied on bf16 matrix cores with fp32
+ *     accumulation and an fp32 softmax; fp32 inputs run an all-fp32 path.
+ */
+#ifndef FLARE_H
+#define FLARE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum flare_status {
+  FLARE_OK = 0,
+  FLARE_E_INVALID = -1,     /* null pointer, size out of range, bad stride/alignment */
+  FLARE_E_UNSUPPORTED = -2, /* valid request outside what this build implements */
+  FLARE_E_WORKSPACE = -3,   /* workspace NULL or smaller than required */
+  FLARE_E_HIP = -4          /* a HIP launch/runtime error */
+} flare_status;
+
+typedef enum flare_dtype { FLARE_F32 = 0, FLARE_BF16 = 1 } flare_dtype;
+
+/* Force the exact running-maximum softmax in every kernel.  Without it the
+ * kernels first try a range-checked form without the maximum and fall back
+ * to the exact form for any tile whose normaliser leaves [2^-100, 2^100];
+ * both give the same softmax up to rounding. */
+#define FLARE_FLAG_EXACT_SOFTMAX 1u
+
+/*
+ * A [B, H, L, D] view of device memory: element (b, h, l, d) lives at
+ *   data + b*stride_b + h*stride_h + l*stride_l + d     (in elements).
+ * The last axis (D) is contiguous.  stride_b may be 0 (one block shared by
+ * the batch, e.g. learned queries or seeds).  Token-major activations
+ * [B, N, H*D] are stride_b = N*H*D, stride_h = D, stride_l = H*D; head-major
+ * [B, H, N, D] are stride_b = H*N*D, stride_h = N*D, stride_l = D.
+ * Requirements: data 16-byte aligned; stride_h and stride_l multiples of 8
+ * elements (bf16) or 4 elements (fp32); stride_b a multiple of the same or 0.
+ */
+typedef struct flare_tensor {
+  void* data;
+  int32_t dtype; /* flare_dtype */
+  int32_t reserved;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_l;
+} flare_tensor;
+
+/* Bytes of workspace flare_encode / flare_route_queries need (split-token
+ * partial outputs and log-normalisers).  Depends only on the sizes. */
+size_t flare_encode_workspace_size(int B, int H, int M, int64_t N, int D);
+
+/*
+ * FLARE encoder, Z[b,h] = SDPA(Q[b,h], K[b,h], V[b,h]): M latent queries
+ * gather N tokens ("FLARE: fixed-query latent routing", equation 5).
+ *   Q   [B, H, M, D]  bf16 or fp32 (stride_b 0 = shared by the batch)
+ *   K,V [B, H, N, D]  bf16 (matrix-core path) or fp32 (fp32 path); same dtype
+ *   Z   [B, H, M, D]  output, bf16 or fp32
+ *   lse [B, H, M]     optional fp32 output (contiguous), the natural-log row
+ *                     normaliser log sum_n exp(scale q_m . k_n); NULL = skip
+ * The tokens are cut into splits that run in parallel; each split's partial
+ * result is merged exactly by logsumexp ("Multi-GPU context parallelism",
+ * applied inside one GPU).  Requires workspace_bytes >=
+ * flare_encode_workspace_size(B, H, M, N, D).
+ */
+flare_status flare_encode(const flare_tensor* Q, const flare_tensor* K,
+                          const flare_tensor* V, const flare_tensor* Z,
+                          float* lse, int B, int H, int M, int64_t N, int D,
+                          float scale, unsigned flags, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * FLARE++ query synthesis, Qx[b,h] = SDPA(seeds[h], eK[b,h], eV[b,h])
+ * ("FLARE++: dynamic token routing", equation 8): the same encoder with the
+ * learned seeds as queries.  seeds [H, M, D] (stride_b normally 0);
+ * eK, eV [B, H, N, D]; Qx [B, H, M, D] output (fp32 keeps the synthesized
+ * queries unrounded for the encode/decode that follow).
+ */
+flare_status flare_route_queries(const flare_tensor* seeds,
+                                 const flare_tensor* eK,
+                                 const flare_tensor* eV,
+                                 const flare_tensor* Qx, int B, int H, int M,
+                                 int64_t N, int D, float scale, unsigned flags,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * FLARE decoder, Y[b,h] = SDPA(K[b,h], Q[b,h], Z[b,h]): every token takes a
+ * softmax over the M latents and gathers their values ("FLARE: fixed-query
+ * latent routing", the second call).
+ *   K [B, H, N, D]  bf16 or fp32;  Q, Z [B, H, M, D] bf16 or fp32
+ *   Y [B, H, N, D]  output, same dtype as K (token-major strides give the
+ *                   concatenated-heads [B, N, H*D] layout directly)
+ * Needs no workspace.
+ */
+flare_status flare_decode(const flare_tensor* K, const flare_tensor* Q,
+                          const flare_tensor* Z, const flare_tensor* Y, int B,
+                          int H, int M, int64_t N, int D, float scale,
+                          unsigned flags, void* stream);
+
+/*
+ * Pointwise projections of one token matrix, Y_p = X W_p for p < n_proj
+ * ("Full self-attention": K = X W_K etc., weights [C_in, C_out] with y = x W,
+ * no bias).  X [R, C_in] row-major bf16; each W_p [C_in, C_out] row-major
+ * bf16; each Y_p bf16 written either row-major [R, C_out]
+ * (out_head_major = 0) or head-major [B, H, N, D] with R = B*N and
+ * C_out = H*D (out_head_major = 1, D = head_dim).  C_in, C_out multiples of
+ * 32 and <= 1024; 1 <= n_proj <= 5.  Workspace holds the transposed weights:
+ * flare_project_workspace_size(C_in, C_out, n_proj) bytes.
+ */
+size_t flare_project_workspace_size(int C_in, int C_out, int n_proj);
+flare_status flare_project(const void* X, const void* const* W, void* const* Y,
+                           int n_proj, int64_t R, int C_in, int C_out,
+                           int out_head_major, int B, int head_dim,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * The whole mixer on a token matrix X [B, N, C], C = H*D, bf16:
+ *   FLARE   (W_eK == NULL): K = X W_K, V = X W_V; Q_or_seeds [H, M, D] are
+ *           the learned queries; Z = SDPA(Q, K, V); Y = SDPA(K, Q, Z).
+ *   FLARE++ (W_eK != NULL): also eK = X W_eK, eV = X W_eV; Q_or_seeds are the
+ *           seeds and Q(X) = SDPA(seeds, eK, eV) replaces the learned queries
+ *           in both the encode and the decode.
+ * Heads are concatenated into out [B, N, C]; if W_O != NULL, out = Y W_O.
+ * All weights [C, C] with y = x W.  Requires workspace_bytes >=
+ * flare_mix_workspace_size(B, N, C, H, M, W_eK != NULL, W_O != NULL).
+ */
+size_t flare_mix_workspace_size(int B, int64_t N, int C, int H, int M,
+                                int dynamic, int has_wo);
+flare_status flare_mix(const void* X, const void* W_K, const void* W_V,
+                       const void* W_eK, const void* W_eV,
+                       const void* Q_or_seeds, const void* W_O, void* out,
+                       int dtype, int B, int64_t N, int C, int H, int M,
+                       float scale, unsigned flags, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* flare_status_string(int status);
+
+/* Library version as "major.minor.patch". */
+const char* flare_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLARE_H */

@@ -127,10 +127,13 @@ int oracle_matmul(const double* x, int64_t x_rs, const double* w, int64_t w_rs,
   for (int64_t r = 0; r < R; ++r) {
     const double* xr = x + r * x_rs;
     double* yr = y + r * y_rs;
-    for (int j = 0; j < Cout; ++j) {
-      double acc = 0.0;
-      for (int c = 0; c < Cin; ++c) acc += xr[c] * w[(int64_t)c * w_rs + j];
-      yr[j] = acc;
+    for (int j = 0; j < Cout; ++j) yr[j] = 0.0;
+    /* y[r][j] accumulates x[r][c] w[c][j] for c = 0, 1, ... in order; the
+       loop over j is innermost only so that W is read along its rows. */
+    for (int c = 0; c < Cin; ++c) {
+      const double xc = xr[c];
+      const double* wc = w + (int64_t)c * w_rs;
+      for (int j = 0; j < Cout; ++j) yr[j] += xc * wc[j];
     }
   }
   return ORACLE_OK;

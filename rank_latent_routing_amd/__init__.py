@@ -1,0 +1,13 @@
+"""MI355X-native FLARE / FLARE++ low-rank token mixer.
+
+The compute lives in a gfx950 HIP library with a plain C ABI
+(include/flare.h): split-token encode with an exact logsumexp merge, a
+decode with a per-token softmax over the latents, FLARE++ query synthesis,
+and bf16 matrix-core projections.  This package holds the ctypes binding
+(argument marshalling only), the library's build script, the seeded input
+generators and the algorithmic cost model used for roofline accounting.
+"""
+from .binding import (  # noqa: F401
+    FLARE_BF16, FLARE_F32, FLARE_FLAG_EXACT_SOFTMAX, FlareError, describe, encode_workspace_size,
+    flare_decode, flare_encode, flare_mix, flare_project, flare_route_queries, lib,
+    mix_workspace_size, project_workspace_size, status_string, token_major, version)

@@ -1,0 +1,247 @@
+"""ctypes binding of the C ABI in include/flare.h.
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the mixer runs in the library's gfx950 kernels.  The
+library must be built (``__graft_entry__.build()`` or
+``python rank_latent_routing_amd/build.py``); without it every call raises.
+
+Tensor arguments are 4-d ``[B, H, L, D]`` views (any strides with a
+contiguous last axis), or 3-d ``[H, L, D]`` for a block shared by the batch.
+``token_major(x, H)`` turns a ``[B, N, H*D]`` activation into such a view
+without copying.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libflare.so")
+
+FLARE_OK = 0
+FLARE_E_INVALID = -1
+FLARE_E_UNSUPPORTED = -2
+FLARE_E_WORKSPACE = -3
+FLARE_E_HIP = -4
+FLARE_F32 = 0
+FLARE_BF16 = 1
+FLARE_FLAG_EXACT_SOFTMAX = 1
+
+EXPORTS = ("flare_encode_workspace_size", "flare_encode", "flare_route_queries",
+           "flare_decode", "flare_project_workspace_size", "flare_project",
+           "flare_mix_workspace_size", "flare_mix", "flare_status_string",
+           "flare_version")
+
+
+class FlareError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class FlareTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_l", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"HIP library not built ({LIB_PATH} missing): run __graft_entry__.build() "
+            "or python rank_latent_routing_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, u32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                  ctypes.c_float, ctypes.c_uint, ctypes.c_size_t)
+    T = ctypes.POINTER(FlareTensor)
+    L.flare_encode_workspace_size.argtypes = [i32, i32, i32, i64, i32]
+    L.flare_encode_workspace_size.restype = sz
+    L.flare_encode.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
+    L.flare_route_queries.argtypes = [T, T, T, T, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
+    L.flare_decode.argtypes = [T, T, T, T, i32, i32, i32, i64, i32, f32, u32, vp]
+    L.flare_project_workspace_size.argtypes = [i32, i32, i32]
+    L.flare_project_workspace_size.restype = sz
+    L.flare_project.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i32,
+                                i32, i32, i32, i32, vp, sz, vp]
+    L.flare_mix_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    L.flare_mix_workspace_size.restype = sz
+    L.flare_mix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32,
+                            f32, u32, vp, sz, vp]
+    for f in ("flare_encode", "flare_route_queries", "flare_decode", "flare_project", "flare_mix"):
+        getattr(L, f).restype = ctypes.c_int
+    L.flare_status_string.argtypes = [i32]
+    L.flare_status_string.restype = ctypes.c_char_p
+    L.flare_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(s: int) -> str:
+    return lib().flare_status_string(int(s)).decode()
+
+
+def version() -> str:
+    return lib().flare_version().decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FLARE_F32
+    if t.dtype == torch.bfloat16:
+        return FLARE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def describe(t: torch.Tensor) -> FlareTensor:
+    """flare_tensor of a [B, H, L, D] (or shared [H, L, D]) view."""
+    if t.dim() == 3:
+        sb, (sh, sl, sd) = 0, t.stride()
+    elif t.dim() == 4:
+        sb, sh, sl, sd = t.stride()
+    else:
+        raise ValueError("expected a [B, H, L, D] or [H, L, D] tensor")
+    if sd != 1 and t.shape[-1] > 1:
+        raise ValueError("the last axis must be contiguous")
+    return FlareTensor(t.data_ptr(), _dtype_code(t), 0, sb, sh, sl)
+
+
+def token_major(x: torch.Tensor, H: int) -> torch.Tensor:
+    """[B, N, H*D] -> [B, H, N, D] view (no copy)."""
+    B, N, C = x.shape
+    return x.view(B, N, H, C // H).permute(0, 2, 1, 3)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(status: int, what: str):
+    if status != FLARE_OK:
+        raise FlareError(status, what)
+
+
+def _dims(k: torch.Tensor):
+    B, H, N, D = k.shape
+    return B, H, N, D
+
+
+def encode_workspace_size(B, H, M, N, D) -> int:
+    return lib().flare_encode_workspace_size(B, H, M, N, D)
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def flare_encode(q, k, v, z=None, want_lse=False, scale=0.0, flags=0, workspace=None,
+                 stream=None, z_dtype=None):
+    """Z = SDPA(Q, K, V) over [B, H, N, D] keys/values; q is [B, H, M, D] or
+    shared [H, M, D].  Returns z (and lse [B, H, M] fp32 when want_lse)."""
+    B, H, N, D = _dims(k)
+    M = q.shape[-2]
+    if z is None:
+        z = torch.empty((B, H, M, D), dtype=z_dtype or k.dtype, device=k.device)
+    lse = torch.empty((B, H, M), dtype=torch.float32, device=k.device) if want_lse else None
+    ws = _workspace(encode_workspace_size(B, H, M, N, D), k.device, workspace)
+    s = lib().flare_encode(describe(q), describe(k), describe(v), describe(z),
+                           ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
+                           B, H, M, N, D, float(scale), int(flags),
+                           ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                           _stream(stream))
+    _check(s, "flare_encode")
+    return (z, lse) if want_lse else z
+
+
+def flare_route_queries(seeds, ek, ev, qx=None, scale=0.0, flags=0, workspace=None,
+                        stream=None):
+    """Q(X) = SDPA(seeds, eK, eV); seeds [H, M, D]; returns qx [B, H, M, D] fp32."""
+    B, H, N, D = _dims(ek)
+    M = seeds.shape[-2]
+    if qx is None:
+        qx = torch.empty((B, H, M, D), dtype=torch.float32, device=ek.device)
+    ws = _workspace(encode_workspace_size(B, H, M, N, D), ek.device, workspace)
+    s = lib().flare_route_queries(describe(seeds), describe(ek), describe(ev), describe(qx),
+                                  B, H, M, N, D, float(scale), int(flags),
+                                  ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    _check(s, "flare_route_queries")
+    return qx
+
+
+def flare_decode(k, q, z, y=None, scale=0.0, flags=0, stream=None):
+    """Y = SDPA(K, Q, Z); k [B, H, N, D]; q, z [B, H, M, D] or shared."""
+    B, H, N, D = _dims(k)
+    M = q.shape[-2]
+    if y is None:
+        y = torch.empty((B, H, N, D), dtype=k.dtype, device=k.device)
+    s = lib().flare_decode(describe(k), describe(q), describe(z), describe(y), B, H, M, N, D,
+                           float(scale), int(flags), _stream(stream))
+    _check(s, "flare_decode")
+    return y
+
+
+def project_workspace_size(C_in, C_out, n_proj) -> int:
+    return lib().flare_project_workspace_size(C_in, C_out, n_proj)
+
+
+def flare_project(x, weights, outs=None, head_dim=None, workspace=None, stream=None):
+    """Y_p = X W_p for x [B, N, C_in] (or [R, C_in]) bf16, weights [C_in, C_out].
+    With head_dim the outputs are head-major [B, H, N, head_dim]."""
+    x2 = x.reshape(-1, x.shape[-1])
+    R, Cin = x2.shape
+    Cout = weights[0].shape[1]
+    B = x.shape[0] if x.dim() == 3 else 1
+    n = len(weights)
+    if outs is None:
+        if head_dim:
+            N = R // B
+            outs = [torch.empty((B, Cout // head_dim, N, head_dim), dtype=x.dtype, device=x.device)
+                    for _ in range(n)]
+        else:
+            outs = [torch.empty((R, Cout), dtype=x.dtype, device=x.device) for _ in range(n)]
+    ws = _workspace(project_workspace_size(Cin, Cout, n), x.device, workspace)
+    warr = (ctypes.c_void_p * n)(*[w.data_ptr() for w in weights])
+    yarr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    s = lib().flare_project(ctypes.c_void_p(x2.data_ptr()), warr, yarr, n, R, Cin, Cout,
+                            1 if head_dim else 0, B, head_dim or 0,
+                            ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                            _stream(stream))
+    _check(s, "flare_project")
+    return outs
+
+
+def mix_workspace_size(B, N, C, H, M, dynamic, has_wo) -> int:
+    return lib().flare_mix_workspace_size(B, N, C, H, M, int(bool(dynamic)), int(bool(has_wo)))
+
+
+def flare_mix(x, w_k, w_v, qs, H, w_ek=None, w_ev=None, w_o=None, out=None, scale=0.0,
+              flags=0, workspace=None, stream=None):
+    """The whole mixer on x [B, N, C] bf16: FLARE with learned queries qs
+    [H, M, D] when w_ek is None, FLARE++ (qs = seeds) otherwise; optional
+    output projection.  Returns out [B, N, C]."""
+    B, N, C = x.shape
+    M = qs.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    dyn, has_wo = w_ek is not None, w_o is not None
+    ws = _workspace(mix_workspace_size(B, N, C, H, M, dyn, has_wo), x.device, workspace)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else None)
+    s = lib().flare_mix(ptr(x), ptr(w_k), ptr(w_v), ptr(w_ek), ptr(w_ev), ptr(qs), ptr(w_o),
+                        ptr(out), _dtype_code(x), B, N, C, H, M, float(scale), int(flags),
+                        ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                        _stream(stream))
+    _check(s, "flare_mix")
+    return out

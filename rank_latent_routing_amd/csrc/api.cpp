@@ -1,0 +1,409 @@
+// C ABI of the FLARE / FLARE++ mixer library (declared in include/flare.h).
+//
+// Host side only: argument validation (done completely before any HIP call,
+// so a rejected call never touches the device), split planning, carving of
+// the caller's workspace, and kernel launches on the caller's stream.  The
+// library allocates nothing and keeps no mutable state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/flare.h"
+#include "launch.hpp"
+
+using namespace flare;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxM = 512;
+constexpr int64_t kMaxBH = 65535;  // grid.y
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_dtype(int32_t d) { return d == FLARE_F32 || d == FLARE_BF16; }
+
+bool sizes_ok(int B, int H, int M, int64_t N, int D) {
+  return B >= 1 && H >= 1 && M >= 1 && N >= 1 && (int64_t)B * H <= kMaxBH && M <= kMaxM &&
+         (D == 16 || D == 32) && N <= (int64_t(1) << 40);
+}
+
+// Token-side tensors are read/written with vector accesses: rows must be
+// 16-byte aligned.
+bool token_tensor_ok(const flare_tensor* t) {
+  if (!t || !t->data || !is_dtype(t->dtype)) return false;
+  if (reinterpret_cast<uintptr_t>(t->data) % 16) return false;
+  const int64_t q = t->dtype == FLARE_BF16 ? 8 : 4;
+  if (t->stride_b < 0 || t->stride_h < 0 || t->stride_l < 0) return false;
+  return t->stride_b % q == 0 && t->stride_h % q == 0 && t->stride_l % q == 0;
+}
+
+// Latent-side tensors (queries, seeds, latent values) are read element-wise.
+bool latent_tensor_ok(const flare_tensor* t) {
+  if (!t || !t->data || !is_dtype(t->dtype)) return false;
+  const size_t el = t->dtype == FLARE_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(t->data) % el) return false;
+  return t->stride_b >= 0 && t->stride_h >= 0 && t->stride_l >= 0;
+}
+
+bool scale_ok(float scale) { return std::isfinite(scale); }
+
+float log2_scale(float scale, int D) {
+  const float s = scale == 0.0f ? 1.0f / std::sqrt((float)D) : scale;
+  return s * 1.4426950408889634f;  // log2(e)
+}
+
+View view_of(const flare_tensor* t) {
+  View v;
+  v.data = t->data;
+  v.is_f32 = t->dtype == FLARE_F32;
+  v.sb = t->stride_b;
+  v.sh = t->stride_h;
+  v.sl = t->stride_l;
+  return v;
+}
+
+flare_status hip_status(hipError_t e) { return e == hipSuccess ? FLARE_OK : FLARE_E_HIP; }
+
+size_t encode_ws(int B, int H, int M, int64_t N, int D, int is_f32) {
+  const EncodePlan pl = plan_encode(B, H, M, N, D, is_f32);
+  const size_t parts = (size_t)B * H * pl.S * M;
+  return align_up(parts * D * sizeof(float)) + align_up(parts * sizeof(float));
+}
+
+// Encoder on validated arguments: split kernel + merge into Z (and lse).
+flare_status encode_impl(const View& q, const View& k, const View& v, void* z, int z_f32,
+                         int64_t z_sb, int64_t z_sh, int64_t z_sl, float* lse, int B, int H, int M,
+                         int64_t N, int D, float c, unsigned flags, void* ws, hipStream_t st) {
+  const EncodePlan pl = plan_encode(B, H, M, N, D, k.is_f32);
+  const size_t parts = (size_t)B * H * pl.S * M;
+  EncodeParams ep;
+  ep.q = q;
+  ep.k = k;
+  ep.v = v;
+  ep.part_o = reinterpret_cast<float*>(ws);
+  ep.part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up(parts * D * sizeof(float)));
+  ep.H = H;
+  ep.M = M;
+  ep.S = pl.S;
+  ep.N = N;
+  ep.tokens_per_split = pl.tokens_per_split;
+  ep.c = c;
+  ep.exact = (flags & FLARE_FLAG_EXACT_SOFTMAX) ? 1 : 0;
+  hipError_t e = k.is_f32 ? launch_encode_f32(ep, D, B, st) : launch_encode_bf16(ep, D, B, pl.waves, st);
+  if (e != hipSuccess) return FLARE_E_HIP;
+  MergeParams mp;
+  mp.part_o = ep.part_o;
+  mp.part_l = ep.part_l;
+  mp.z = z;
+  mp.z_f32 = z_f32;
+  mp.z_sb = z_sb;
+  mp.z_sh = z_sh;
+  mp.z_sl = z_sl;
+  mp.lse = lse;
+  mp.H = H;
+  mp.M = M;
+  mp.S = pl.S;
+  mp.D = D;
+  return hip_status(launch_merge(mp, B, st));
+}
+
+flare_status decode_impl(const View& k, const View& q, const View& z, void* y, int y_f32,
+                         int64_t y_sb, int64_t y_sh, int64_t y_sl, int B, int H, int M, int64_t N,
+                         int D, float c, unsigned flags, hipStream_t st) {
+  DecodeParams dp;
+  dp.k = k;
+  dp.q = q;
+  dp.z = z;
+  dp.y = y;
+  dp.y_f32 = y_f32;
+  dp.y_sb = y_sb;
+  dp.y_sh = y_sh;
+  dp.y_sl = y_sl;
+  dp.H = H;
+  dp.M = M;
+  dp.N = N;
+  dp.c = c;
+  dp.exact = (flags & FLARE_FLAG_EXACT_SOFTMAX) ? 1 : 0;
+  if (k.is_f32) {
+    dp.tokens_per_block = 256;
+    return hip_status(launch_decode_f32(dp, D, B, st));
+  }
+  // 8 waves x 64 tokens per pass; about 1024 workgroups in all, each doing
+  // at least one full pass.
+  const int64_t pass = 512;
+  const int64_t bh = (int64_t)B * H;
+  int64_t per_bh = (1024 + bh - 1) / bh;
+  int64_t tpb = (N + per_bh - 1) / per_bh;
+  tpb = (tpb + pass - 1) / pass * pass;
+  if (tpb < pass) tpb = pass;
+  dp.tokens_per_block = tpb;
+  return hip_status(launch_decode_bf16(dp, D, B, st));
+}
+
+bool proj_shape_ok(int64_t R, int Cin, int Cout, int n_proj) {
+  return R >= 1 && (Cin == 32 || Cin == 64 || Cin == 128 || Cin == 256) && Cout >= 16 &&
+         Cout % 16 == 0 && Cout <= 4096 && n_proj >= 1 && n_proj <= 5 &&
+         (R + 255) / 256 <= 0x7fffffff;
+}
+
+size_t proj_ws(int Cin, int Cout, int n_proj) {
+  return (size_t)n_proj * align_up((size_t)Cin * Cout * 2);
+}
+
+flare_status project_impl(const void* X, const void* const* W, void* const* Y, int n_proj, int64_t R,
+                          int Cin, int Cout, int head_major, int B, int head_dim, void* ws,
+                          hipStream_t st) {
+  GemmParams gp;
+  std::memset(&gp, 0, sizeof(gp));
+  gp.x = X;
+  gp.n_proj = n_proj;
+  gp.R = R;
+  gp.Cin = Cin;
+  gp.Cout = Cout;
+  gp.head_major = head_major;
+  gp.N = head_major ? R / B : R;
+  gp.D = head_major ? head_dim : Cout;
+  for (int i = 0; i < n_proj; ++i) {
+    void* wt = reinterpret_cast<char*>(ws) + i * align_up((size_t)Cin * Cout * 2);
+    hipError_t e = launch_transpose_weights(W[i], wt, Cin, Cout, st);
+    if (e != hipSuccess) return FLARE_E_HIP;
+    gp.wt[i] = wt;
+    gp.y[i] = Y[i];
+  }
+  return hip_status(launch_gemm_bf16(gp, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flare_version(void) { return "0.1.0"; }
+
+const char* flare_status_string(int s) {
+  switch (s) {
+    case FLARE_OK: return "ok";
+    case FLARE_E_INVALID: return "invalid argument";
+    case FLARE_E_UNSUPPORTED: return "unsupported configuration";
+    case FLARE_E_WORKSPACE: return "workspace missing or too small";
+    case FLARE_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t flare_encode_workspace_size(int B, int H, int M, int64_t N, int D) {
+  if (!sizes_ok(B, H, M, N, D)) return 0;
+  const size_t a = encode_ws(B, H, M, N, D, 0), b = encode_ws(B, H, M, N, D, 1);
+  return a > b ? a : b;
+}
+
+static flare_status encode_checked(const flare_tensor* Q, const flare_tensor* K, const flare_tensor* V,
+                                   const flare_tensor* Z, float* lse, int B, int H, int M, int64_t N,
+                                   int D, float scale, unsigned flags, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!sizes_ok(B, H, M, N, D)) {
+    if (B >= 1 && H >= 1 && M >= 1 && N >= 1 && (M > kMaxM || !(D == 16 || D == 32)))
+      return FLARE_E_UNSUPPORTED;
+    return FLARE_E_INVALID;
+  }
+  if (!latent_tensor_ok(Q) || !token_tensor_ok(K) || !token_tensor_ok(V) || !latent_tensor_ok(Z))
+    return FLARE_E_INVALID;
+  if (K->dtype != V->dtype) return FLARE_E_INVALID;
+  if (!scale_ok(scale) || (flags & ~FLARE_FLAG_EXACT_SOFTMAX)) return FLARE_E_INVALID;
+  if (lse && reinterpret_cast<uintptr_t>(lse) % 4) return FLARE_E_INVALID;
+  const size_t need = encode_ws(B, H, M, N, D, K->dtype == FLARE_F32);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16)
+    return FLARE_E_WORKSPACE;
+  return encode_impl(view_of(Q), view_of(K), view_of(V), Z->data, Z->dtype == FLARE_F32, Z->stride_b,
+                     Z->stride_h, Z->stride_l, lse, B, H, M, N, D, log2_scale(scale, D), flags,
+                     workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+flare_status flare_encode(const flare_tensor* Q, const flare_tensor* K, const flare_tensor* V,
+                          const flare_tensor* Z, float* lse, int B, int H, int M, int64_t N, int D,
+                          float scale, unsigned flags, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return encode_checked(Q, K, V, Z, lse, B, H, M, N, D, scale, flags, workspace, workspace_bytes,
+                        stream);
+}
+
+flare_status flare_route_queries(const flare_tensor* seeds, const flare_tensor* eK,
+                                 const flare_tensor* eV, const flare_tensor* Qx, int B, int H,
+                                 int M, int64_t N, int D, float scale, unsigned flags,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return encode_checked(seeds, eK, eV, Qx, nullptr, B, H, M, N, D, scale, flags, workspace,
+                        workspace_bytes, stream);
+}
+
+flare_status flare_decode(const flare_tensor* K, const flare_tensor* Q, const flare_tensor* Z,
+                          const flare_tensor* Y, int B, int H, int M, int64_t N, int D, float scale,
+                          unsigned flags, void* stream) {
+  if (!sizes_ok(B, H, M, N, D)) {
+    if (B >= 1 && H >= 1 && M >= 1 && N >= 1 && (M > kMaxM || !(D == 16 || D == 32)))
+      return FLARE_E_UNSUPPORTED;
+    return FLARE_E_INVALID;
+  }
+  if (!token_tensor_ok(K) || !latent_tensor_ok(Q) || !latent_tensor_ok(Z) || !token_tensor_ok(Y))
+    return FLARE_E_INVALID;
+  if (!scale_ok(scale) || (flags & ~FLARE_FLAG_EXACT_SOFTMAX)) return FLARE_E_INVALID;
+  return decode_impl(view_of(K), view_of(Q), view_of(Z), Y->data, Y->dtype == FLARE_F32, Y->stride_b,
+                     Y->stride_h, Y->stride_l, B, H, M, N, D, log2_scale(scale, D), flags,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t flare_project_workspace_size(int C_in, int C_out, int n_proj) {
+  if (!proj_shape_ok(1, C_in, C_out, n_proj)) return 0;
+  return proj_ws(C_in, C_out, n_proj);
+}
+
+flare_status flare_project(const void* X, const void* const* W, void* const* Y, int n_proj, int64_t R,
+                           int C_in, int C_out, int out_head_major, int B, int head_dim,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!proj_shape_ok(R, C_in, C_out, n_proj)) {
+    if (R >= 1 && n_proj >= 1 && n_proj <= 5 && C_in > 0 && C_out > 0) return FLARE_E_UNSUPPORTED;
+    return FLARE_E_INVALID;
+  }
+  if (!X || !W || !Y || reinterpret_cast<uintptr_t>(X) % 16) return FLARE_E_INVALID;
+  for (int i = 0; i < n_proj; ++i)
+    if (!W[i] || !Y[i] || reinterpret_cast<uintptr_t>(W[i]) % 2 || reinterpret_cast<uintptr_t>(Y[i]) % 8)
+      return FLARE_E_INVALID;
+  if (out_head_major) {
+    if (B < 1 || R % B || (head_dim != 16 && head_dim != 32) || C_out % head_dim) return FLARE_E_INVALID;
+  }
+  if (!workspace || workspace_bytes < proj_ws(C_in, C_out, n_proj) ||
+      reinterpret_cast<uintptr_t>(workspace) % 16)
+    return FLARE_E_WORKSPACE;
+  return project_impl(X, W, Y, n_proj, R, C_in, C_out, out_head_major, B, head_dim, workspace,
+                      reinterpret_cast<hipStream_t>(stream));
+}
+
+// Workspace of flare_mix, in order: K, V (, eK, eV) head-major bf16;
+// Q(X) fp32 (dynamic); Z fp32; Y bf16 (with W_O); swizzled input weights;
+// swizzled W_O; encoder split partials.
+namespace {
+struct MixLayout {
+  size_t kv, qx, z, y, wsw, wosw, enc, total;
+};
+MixLayout mix_layout(int B, int64_t N, int C, int H, int M, int dynamic, int has_wo) {
+  MixLayout L;
+  const int D = C / H;
+  const size_t act = align_up((size_t)B * N * C * 2);
+  const int n_in = dynamic ? 4 : 2;
+  const size_t lat = align_up((size_t)B * H * M * D * 4);
+  size_t off = 0;
+  L.kv = off;
+  off += n_in * act;
+  L.qx = off;
+  off += dynamic ? lat : 0;
+  L.z = off;
+  off += lat;
+  L.y = off;
+  off += has_wo ? act : 0;
+  L.wsw = off;
+  off += proj_ws(C, C, n_in);
+  L.wosw = off;
+  off += has_wo ? proj_ws(C, C, 1) : 0;
+  L.enc = off;
+  off += encode_ws(B, H, M, N, D, 0);
+  L.total = off;
+  return L;
+}
+bool mix_shape_ok(int B, int64_t N, int C, int H, int M) {
+  if (B < 1 || N < 1 || C < 1 || H < 1 || M < 1 || C % H) return false;
+  return sizes_ok(B, H, M, N, C / H) && (C == 32 || C == 64 || C == 128 || C == 256) &&
+         ((int64_t)B * N + 255) / 256 <= 0x7fffffff;
+}
+}  // namespace
+
+size_t flare_mix_workspace_size(int B, int64_t N, int C, int H, int M, int dynamic, int has_wo) {
+  if (!mix_shape_ok(B, N, C, H, M)) return 0;
+  return mix_layout(B, N, C, H, M, dynamic != 0, has_wo != 0).total;
+}
+
+flare_status flare_mix(const void* X, const void* W_K, const void* W_V, const void* W_eK,
+                       const void* W_eV, const void* Q_or_seeds, const void* W_O, void* out,
+                       int dtype, int B, int64_t N, int C, int H, int M, float scale,
+                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || N < 1 || C < 1 || H < 1 || M < 1 || C % H) return FLARE_E_INVALID;
+  if (!is_dtype(dtype)) return FLARE_E_INVALID;
+  if (dtype != FLARE_BF16 || !mix_shape_ok(B, N, C, H, M)) return FLARE_E_UNSUPPORTED;
+  if (!X || !W_K || !W_V || !Q_or_seeds || !out) return FLARE_E_INVALID;
+  if ((W_eK == nullptr) != (W_eV == nullptr)) return FLARE_E_INVALID;
+  if (reinterpret_cast<uintptr_t>(X) % 16 || reinterpret_cast<uintptr_t>(out) % 16) return FLARE_E_INVALID;
+  if (!scale_ok(scale) || (flags & ~FLARE_FLAG_EXACT_SOFTMAX)) return FLARE_E_INVALID;
+  const int dynamic = W_eK != nullptr, has_wo = W_O != nullptr;
+  const MixLayout L = mix_layout(B, N, C, H, M, dynamic, has_wo);
+  if (!workspace || workspace_bytes < L.total || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return FLARE_E_WORKSPACE;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int D = C / H;
+  const float c = log2_scale(scale, D);
+  char* ws = reinterpret_cast<char*>(workspace);
+  const size_t act = align_up((size_t)B * N * C * 2);
+  void* kp = ws + L.kv;
+  void* vp = ws + L.kv + act;
+  void* ekp = ws + L.kv + 2 * act;
+  void* evp = ws + L.kv + 3 * act;
+
+  // (a) projections, written head-major [B, H, N, D]
+  const void* w_in[4] = {W_K, W_V, W_eK, W_eV};
+  void* y_in[4] = {kp, vp, ekp, evp};
+  flare_status s = project_impl(X, w_in, y_in, dynamic ? 4 : 2, (int64_t)B * N, C, C, 1, B, D,
+                                ws + L.wsw, st);
+  if (s != FLARE_OK) return s;
+
+  auto head_major = [&](void* p) {
+    View v;
+    v.data = p;
+    v.is_f32 = 0;
+    v.sb = (int64_t)H * N * D;
+    v.sh = N * D;
+    v.sl = D;
+    return v;
+  };
+  View qs;
+  qs.data = Q_or_seeds;
+  qs.is_f32 = 0;
+  qs.sb = 0;
+  qs.sh = (int64_t)M * D;
+  qs.sl = D;
+  View q = qs;
+  const int64_t lat_sb = (int64_t)H * M * D, lat_sh = (int64_t)M * D, lat_sl = D;
+  // (b) FLARE++: Q(X) = SDPA(seeds, eK, eV), kept in fp32
+  if (dynamic) {
+    s = encode_impl(qs, head_major(ekp), head_major(evp), ws + L.qx, 1, lat_sb, lat_sh, lat_sl, nullptr,
+                    B, H, M, N, D, c, flags, ws + L.enc, st);
+    if (s != FLARE_OK) return s;
+    q.data = ws + L.qx;
+    q.is_f32 = 1;
+    q.sb = lat_sb;
+    q.sh = lat_sh;
+    q.sl = lat_sl;
+  }
+  // (c) Z = SDPA(Q, K, V)
+  s = encode_impl(q, head_major(kp), head_major(vp), ws + L.z, 1, lat_sb, lat_sh, lat_sl, nullptr, B,
+                  H, M, N, D, c, flags, ws + L.enc, st);
+  if (s != FLARE_OK) return s;
+  View z;
+  z.data = ws + L.z;
+  z.is_f32 = 1;
+  z.sb = lat_sb;
+  z.sh = lat_sh;
+  z.sl = lat_sl;
+  // (d) Y = SDPA(K, Q, Z), heads concatenated into [B, N, C]
+  void* ydst = has_wo ? (void*)(ws + L.y) : out;
+  s = decode_impl(head_major(kp), q, z, ydst, 0, N * C, D, C, B, H, M, N, D, c, flags, st);
+  if (s != FLARE_OK) return s;
+  // (e) out = Y W_O
+  if (has_wo) {
+    const void* wo[1] = {W_O};
+    void* yo[1] = {out};
+    s = project_impl(ws + L.y, wo, yo, 1, (int64_t)B * N, C, C, 0, B, D, ws + L.wosw, st);
+  }
+  return s;
+}
+
+}  // extern "C"

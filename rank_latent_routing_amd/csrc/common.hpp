@@ -1,0 +1,92 @@
+// Device-side types and helpers shared by the gfx950 kernels.
+//
+// Matrix-core layouts used throughout (CDNA3/CDNA4 MFMA, wave64):
+//   v_mfma_f32_16x16x32_bf16  A: lane l holds A[l%16][8*(l/16) + j], j < 8
+//                             B: lane l holds B[8*(l/16) + j][l%16]
+//                             C/D: lane l holds C[4*(l/16) + i][l%16], i < 4
+//   v_mfma_f32_16x16x16_bf16  same with 4 K-elements per lane: k = 4*(l/16) + j
+// We write g = l/16 (lane group) and r = l%16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flare {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Range inside which a softmax normaliser computed without the running
+// maximum is accepted (see the encode and decode kernels).
+constexpr float kSafeLo = 7.888609052210118e-31f;  // 2^-100
+constexpr float kSafeHi = 1.2676506002282294e30f;  // 2^100
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Operand vector of a QK^T product: 8 bf16 for D = 32 (16x16x32), 4 for D = 16 (16x16x16).
+template <int D> struct QkOp;
+template <> struct QkOp<32> {
+  typedef bf16x8 type;
+  static constexpr int per_lane = 8;
+  __device__ static __forceinline__ f32x4 mma(type a, type b, f32x4 c) { return mfma_16x16x32(a, b, c); }
+};
+template <> struct QkOp<16> {
+  typedef bf16x4 type;
+  static constexpr int per_lane = 4;
+  __device__ static __forceinline__ f32x4 mma(type a, type b, f32x4 c) { return mfma_16x16x16(a, b, c); }
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+  r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
+  r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
+  return r;
+}
+
+// Split x into bf16 hi + lo with hi + lo = x to about 2^-17 relative.
+__device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
+  hi = (bf16)x;
+  lo = (bf16)(x - (float)hi);
+}
+
+// Load n consecutive elements (bf16 or fp32) starting at element offset
+// `off` of `base` and return them as floats.
+template <int n>
+__device__ __forceinline__ void load_as_f32(const void* base, int is_f32, int64_t off, float* out) {
+  if (is_f32) {
+    const float* p = reinterpret_cast<const float*>(base) + off;
+#pragma unroll
+    for (int j = 0; j < n; ++j) out[j] = p[j];
+  } else {
+    const bf16* p = reinterpret_cast<const bf16*>(base) + off;
+#pragma unroll
+    for (int j = 0; j < n; ++j) out[j] = (float)p[j];
+  }
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace flare

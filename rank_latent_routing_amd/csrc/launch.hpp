@@ -1,0 +1,78 @@
+// Parameter blocks and launchers of the gfx950 kernels (internal to the
+// library; the public surface is include/flare.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flare {
+
+// Strided [B, H, L, D] view in elements, D contiguous.
+struct View {
+  const void* data;
+  int is_f32;
+  int64_t sb, sh, sl;
+};
+
+struct EncodeParams {
+  View q;             // [B, H, M, D] (sb may be 0)
+  View k, v;          // [B, H, N, D]
+  float* part_o;      // [B*H, S, M, D] normalised split outputs
+  float* part_l;      // [B*H, S, M] split log2-normalisers (of scale*log2e*q.k)
+  int H, M, S;
+  int64_t N, tokens_per_split;
+  float c;            // scale * log2(e)
+  int exact;          // 1: running-maximum softmax only
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_l;
+  void* z;            // [B, H, M, D]
+  int z_f32;
+  int64_t z_sb, z_sh, z_sl;
+  float* lse;         // [B, H, M] natural log, may be null
+  int H, M, S, D;
+};
+
+struct DecodeParams {
+  View k;             // [B, H, N, D]
+  View q, z;          // [B, H, M, D]
+  void* y;            // [B, H, N, D]
+  int y_f32;
+  int64_t y_sb, y_sh, y_sl;
+  int H, M;
+  int64_t N, tokens_per_block;
+  float c;
+  int exact;
+};
+
+struct GemmParams {
+  const void* x;      // [R, Cin] bf16 row-major
+  const void* wt[5];  // transposed weights [Cout, Cin] bf16
+  void* y[5];         // outputs
+  int n_proj;
+  int64_t R;
+  int Cin, Cout;
+  int head_major;     // 1: y is [B, H, N, D] with R = B*N, Cout = H*D
+  int64_t N;          // tokens per batch element (head_major)
+  int D;              // head width (head_major)
+};
+
+// Split planning shared by the workspace-size query and the launcher.
+struct EncodePlan {
+  int S;                    // number of token splits
+  int64_t tokens_per_split; // multiple of 64
+  int waves;                // waves per workgroup (bf16 path)
+};
+EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32);
+
+hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, hipStream_t s);
+hipError_t launch_encode_f32(const EncodeParams& p, int D, int B, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, int B, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeParams& p, int D, int B, hipStream_t s);
+hipError_t launch_transpose_weights(const void* w, void* wt, int Cin, int Cout, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
+
+}  // namespace flare

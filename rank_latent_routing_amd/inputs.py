@@ -90,15 +90,17 @@ def _cast(a: np.ndarray, dtype: str) -> torch.Tensor:
     return torch.from_numpy(a).to(torch_dtype(dtype))
 
 
-def make_encdec(w: Workload, seed: int = 0, q_mult: float = 1.0, synth: bool = False):
+def make_encdec(w: Workload, seed: int = 0, q_mult: float = 1.0, synth: bool = False,
+                per_batch_q: bool = False):
     """Inputs of an encode/decode workload, token-major.
 
-    Returns a dict of CPU tensors: q [H, M, D], k, v [B, N, H, D]; with
+    Returns a dict of CPU tensors: q [H, M, D] (or [B, H, M, D] with
+    per_batch_q), k, v [B, N, H, D]; with
     ``synth`` also ek, ev [B, N, H, D] and seeds [H, M, D] (drawn after q, k, v)
     for the variant that synthesizes the queries first.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
-    q = _normal(rng, (w.H, w.M, w.D))
+    q = _normal(rng, (w.B, w.H, w.M, w.D) if per_batch_q else (w.H, w.M, w.D))
     k = _normal(rng, (w.B, w.N, w.H, w.D))
     v = _normal(rng, (w.B, w.N, w.H, w.D))
     if q_mult != 1.0:

@@ -1,0 +1,291 @@
+"""GPU tier: the HIP library through its C ABI against the fp64 oracle.
+
+Tolerances (stated for the two number paths of the library):
+  * bf16 inputs, matrix cores, fp32 accumulation: relative L2 error of the
+    whole output tensor <= 1e-2 (also checked per (batch, head));
+  * fp32 path: normwise max relative error ||y - r||_inf / ||r||_inf <= 1e-4.
+The oracle reads exactly the rounded inputs the GPU reads, widened to fp64.
+"Sharp" cases scale the queries so that scores span tens of units, which
+also drives the kernels' exact-softmax fallback; FLARE_FLAG_EXACT_SOFTMAX
+forces that path everywhere.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_latent_routing_amd as rl
+from rank_latent_routing_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF16_TOL = 1e-2
+F32_TOL = 1e-4
+EXACT = rl.FLARE_FLAG_EXACT_SOFTMAX
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300))
+
+
+def max_rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def hm(t):
+    """[B, N, H, D] -> [B, H, N, D] view."""
+    return t.permute(0, 2, 1, 3)
+
+
+def check_bf16(got, ref, what, per_bh_axes=None):
+    e = rel_l2(got, ref)
+    say(f"  {what}: rel-L2 {e:.3e}")
+    assert e <= BF16_TOL, what
+    if per_bh_axes is not None:
+        B, H = ref.shape[0], ref.shape[1]
+        for b in range(B):
+            for h in range(H):
+                assert rel_l2(got[b, h], ref[b, h]) <= BF16_TOL, (what, b, h)
+
+
+# (B, H, N, D, M, layout, q_mult, flags, per_batch_q, z_dtype)
+ENCDEC_CASES = [
+    (1, 8, 5000, 32, 256, "token", 1.0, 0, False, torch.float32),
+    (2, 4, 3001, 32, 64, "head", 8.0, 0, True, torch.bfloat16),
+    (2, 4, 3001, 32, 64, "head", 8.0, EXACT, True, torch.float32),
+    (1, 2, 1, 32, 32, "token", 1.0, 0, False, torch.float32),
+    (1, 2, 63, 16, 17, "token", 4.0, 0, False, torch.float32),
+    (3, 2, 700, 16, 64, "head", 1.0, 0, False, torch.float32),
+    (1, 1, 2000, 32, 1, "token", 2.0, 0, False, torch.float32),
+    (1, 2, 4096, 32, 512, "head", 1.0, 0, False, torch.float32),
+    (1, 2, 4096, 16, 512, "token", 8.0, 0, False, torch.float32),
+    (2, 3, 1500, 32, 128, "token", 8.0, EXACT, False, torch.float32),
+    (1, 1, 70000, 32, 48, "head", 30.0, 0, False, torch.float32),
+    (1, 2, 20000, 32, 200, "token", 1.0, EXACT, False, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", ENCDEC_CASES, ids=lambda c: "B{}H{}N{}D{}M{}-{}-q{}-f{}-pb{}".format(*c[:9]))
+def test_encode_decode_bf16(case):
+    B, H, N, D, M, layout, qm, flags, pbq, zdt = case
+    say(f"case {case}")
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=N + M, q_mult=qm, per_batch_q=pbq)
+    q = x["q"].to(DEV)
+    if layout == "head":
+        k = hm(x["k"]).contiguous().to(DEV)
+        v = hm(x["v"]).contiguous().to(DEV)
+        kv, vv = k, v
+        y = torch.empty_like(k)
+        yv = y
+    else:
+        k, v = x["k"].to(DEV), x["v"].to(DEV)
+        kv, vv = hm(k), hm(v)
+        y = torch.empty_like(k)
+        yv = hm(y)
+    z, lse = rl.flare_encode(q, kv, vv, want_lse=True, flags=flags, z_dtype=zdt)
+    rl.flare_decode(kv, q, z, y=yv, flags=flags)
+    torch.cuda.synchronize()
+    qo = f64(x["q"])
+    ko, vo = f64(hm(x["k"])), f64(hm(x["v"]))
+    zr, lr = oracle.encode(qo, ko, vo)
+    yr = oracle.decode(ko, qo, zr)
+    check_bf16(f64(z), zr, "Z", per_bh_axes=True)
+    el = float(np.max(np.abs(f64(lse) - lr)))
+    say(f"  lse: max abs err {el:.3e}")
+    assert el <= 1e-2 * max(1.0, float(np.max(np.abs(lr))))
+    check_bf16(f64(yv), yr, "Y", per_bh_axes=True)
+
+
+def test_decode_alone_with_oracle_latents():
+    # The decoder fed the oracle's own latent values (rounded to fp32): its
+    # error is then the decoder's alone.
+    B, H, N, D, M = 2, 3, 3000, 32, 96
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=5, q_mult=3.0)
+    ko, vo, qo = f64(hm(x["k"])), f64(hm(x["v"])), f64(x["q"])
+    zr, _ = oracle.encode(qo, ko, vo)
+    z32 = torch.from_numpy(zr).float()
+    yr = oracle.decode(ko, qo, f64(z32))
+    k = hm(x["k"]).contiguous().to(DEV)
+    y = rl.flare_decode(k, x["q"].to(DEV), z32.to(DEV))
+    torch.cuda.synchronize()
+    check_bf16(f64(y), yr, "Y(decode only)", per_bh_axes=True)
+
+
+@pytest.mark.parametrize("qm", [1.0, 6.0])
+def test_route_queries_shared_seeds(qm):
+    B, H, N, D, M = 3, 4, 2500, 32, 64
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=7, q_mult=qm, synth=True)
+    ek, ev = hm(x["ek"]).to(DEV), hm(x["ev"]).to(DEV)
+    qx = rl.flare_route_queries(x["seeds"].to(DEV), ek, ev)
+    torch.cuda.synchronize()
+    qr, _ = oracle.encode(f64(x["seeds"]), f64(hm(x["ek"])), f64(hm(x["ev"])))
+    check_bf16(f64(qx), qr, "Q(X)", per_bh_axes=True)
+
+
+@pytest.mark.parametrize("flags", [0, EXACT])
+def test_fp32_path_encdec_n1k(flags):
+    # FLARE encode/decode in fp32: B=1, H=4, D=16, N=1024, M=32, seed 0.
+    w = inputs.WORKLOADS["encdec_f32_n1k"]
+    x = inputs.make_encdec(w, seed=0)
+    q = x["q"].to(DEV)
+    k, v = x["k"].to(DEV), x["v"].to(DEV)
+    z, lse = rl.flare_encode(q, hm(k), hm(v), want_lse=True, flags=flags)
+    y = torch.empty_like(k)
+    rl.flare_decode(hm(k), q, z, y=hm(y), flags=flags)
+    torch.cuda.synchronize()
+    yr, zr, lr = oracle.flare_encdec(f64(x["q"]), f64(x["k"]).reshape(1, 1024, 64),
+                                     f64(x["v"]).reshape(1, 1024, 64), 4, want_latents=True)
+    ez, ey = max_rel(f64(z), zr), max_rel(f64(y).reshape(1, 1024, 64), yr)
+    el = float(np.max(np.abs(f64(lse) - lr)))
+    say(f"  fp32: Z max-rel {ez:.2e}, Y max-rel {ey:.2e}, lse abs {el:.2e}")
+    assert ez <= F32_TOL and ey <= F32_TOL and el <= 1e-4
+
+
+def test_fp32_path_ragged_and_sharp():
+    B, H, N, D, M = 2, 3, 777, 32, 40
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "f32")
+    x = inputs.make_encdec(w, seed=3, q_mult=6.0)
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    z = rl.flare_encode(q, hm(k), hm(v))
+    y = torch.empty_like(k)
+    rl.flare_decode(hm(k), q, z, y=hm(y))
+    torch.cuda.synchronize()
+    ko, vo, qo = f64(hm(x["k"])), f64(hm(x["v"])), f64(x["q"])
+    zr, _ = oracle.encode(qo, ko, vo)
+    yr = oracle.decode(ko, qo, zr)
+    assert max_rel(f64(z), zr) <= F32_TOL
+    assert max_rel(f64(hm(y)), yr) <= F32_TOL
+
+
+@pytest.mark.parametrize("R,Cin,Cout,nproj,head_dim", [
+    (1000, 128, 128, 4, 16), (4096, 256, 256, 2, 32), (333, 256, 256, 5, None),
+    (64, 64, 96, 1, None), (2048, 32, 64, 3, 32)])
+def test_projection_gemm(R, Cin, Cout, nproj, head_dim):
+    B = 2 if head_dim and R % 2 == 0 else 1
+    xs = inputs.normal_tensor((B, R // B, Cin), "bf16", seed=R)
+    ws = [inputs.normal_tensor((Cin, Cout), "bf16", seed=100 + i, std=1 / math.sqrt(Cin))
+          for i in range(nproj)]
+    outs = rl.flare_project(xs.to(DEV), [w.to(DEV) for w in ws], head_dim=head_dim)
+    torch.cuda.synchronize()
+    x2 = f64(xs).reshape(R, Cin)
+    for i, w in enumerate(ws):
+        ref = oracle.matmul(x2, f64(w))
+        got = f64(outs[i])
+        if head_dim:
+            Hh = Cout // head_dim
+            got = got.reshape(B, Hh, R // B, head_dim).transpose(0, 2, 1, 3).reshape(R, Cout)
+        check_bf16(got, ref, f"projection {i}")
+
+
+def _oracle_mix(m, H, batches=None):
+    sel = (lambda a: a[batches]) if batches is not None else (lambda a: a)
+    return oracle.flare_mix(sel(f64(m["x"])), f64(m["w_k"]), f64(m["w_v"]), f64(m["qs"]), H,
+                            w_ek=f64(m["w_ek"]) if "w_ek" in m else None,
+                            w_ev=f64(m["w_ev"]) if "w_ev" in m else None,
+                            w_o=f64(m["w_o"]) if "w_o" in m else None)[0]
+
+
+def _gpu_mix(m, H, flags=0):
+    g = {n: t.to(DEV) for n, t in m.items()}
+    out = rl.flare_mix(g["x"], g["w_k"], g["w_v"], g["qs"], H, w_ek=g.get("w_ek"),
+                       w_ev=g.get("w_ev"), w_o=g.get("w_o"), flags=flags)
+    torch.cuda.synchronize()
+    return f64(out)
+
+
+@pytest.mark.parametrize("qm", [1.0, 8.0])
+def test_mix_flarepp_n4k_c128(qm):
+    # FLARE++ mixer, B=8, C=128, H=8 (D=16), N=4096, M=64, full size.
+    w = inputs.WORKLOADS["mix_bf16_n4k_c128"]
+    m = inputs.make_mix(w, seed=0, q_mult=qm)
+    check_bf16(_gpu_mix(m, w.H), _oracle_mix(m, w.H), f"FLARE++ mix (seed x{qm})")
+
+
+def test_mix_seq_b32_sampled_batches():
+    # Sequence-shaped FLARE++ (B=32, N=4096, C=256, M=128) at full size; the
+    # oracle checks batch elements 0 and 31 (batch elements are independent).
+    w = inputs.WORKLOADS["seq_bf16_b32_n4k"]
+    m = inputs.make_mix(w, seed=0)
+    got = _gpu_mix(m, w.H)
+    check_bf16(got[[0, 31]], _oracle_mix(m, w.H, batches=[0, 31]), "FLARE++ seq mix")
+
+
+@pytest.mark.parametrize("dynamic,has_wo,qm,flags", [
+    (True, True, 1.0, 0), (True, True, 8.0, 0), (False, True, 2.0, 0), (False, False, 1.0, EXACT),
+    (True, False, 8.0, EXACT)])
+def test_mix_block_reduced(dynamic, has_wo, qm, flags):
+    # The block workload's shape (C=256, H=8, M=512) at N = 3000 tokens.
+    w = inputs.Workload("t", "mix", 2, 3000, 8, 32, 512, "bf16", dynamic=dynamic, has_wo=has_wo)
+    m = inputs.make_mix(w, seed=2, q_mult=qm)
+    check_bf16(_gpu_mix(m, w.H, flags), _oracle_mix(m, w.H), f"mix dyn={dynamic} wo={has_wo}")
+
+
+def test_deterministic_repeat():
+    w = inputs.Workload("t", "encdec", 1, 4000, 4, 32, 256, "bf16")
+    x = inputs.make_encdec(w, seed=9, q_mult=2.0)
+    q, k, v = x["q"].to(DEV), hm(x["k"]).to(DEV), hm(x["v"]).to(DEV)
+    outs = []
+    for _ in range(2):
+        z = rl.flare_encode(q, k, v, z_dtype=torch.float32)
+        outs.append((z.clone(), rl.flare_decode(k, q, z).clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_metric_workload_full_size_sampled():
+    # FLARE encode/decode at N = 1,048,576, H=8, D=32, M=256 (bf16), in the
+    # launch configuration the benchmark times.  The oracle computes every
+    # latent of heads 0 and 5 and 4096 sampled tokens of their decode.
+    w = inputs.WORKLOADS["encdec_bf16_n1m"]
+    x = inputs.make_encdec(w, seed=0)
+    q = x["q"].to(DEV)
+    k = hm(x["k"]).contiguous().to(DEV)
+    v = hm(x["v"]).contiguous().to(DEV)
+    z = rl.flare_encode(q, k, v, z_dtype=torch.bfloat16)
+    y = rl.flare_decode(k, q, z)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(0).choice(w.N, 4096, replace=False)
+    for h in (0, 5):
+        kh = f64(x["k"][0, :, h])
+        vh = f64(x["v"][0, :, h])
+        qh = f64(x["q"][h])
+        zr = oracle.sdpa(qh, kh, vh)
+        check_bf16(f64(z[0, h]), zr, f"Z head {h}")
+        yr = oracle.sdpa(kh[rows], qh, zr)
+        check_bf16(f64(y[0, h])[rows], yr, f"Y head {h} (4096 sampled tokens)")
+
+
+def test_block_workload_full_size_sampled():
+    # FLARE++ block with all projections (B=4, N=262,144, C=256, H=8, M=512)
+    # at full size; the oracle computes batch element 3 at 2048 sampled output
+    # tokens from oracle primitives (projections, the three SDPA calls per
+    # head, the output projection).
+    w = inputs.WORKLOADS["block_bf16_n256k"]
+    m = inputs.make_mix(w, seed=0)
+    got = _gpu_mix(m, w.H)
+    b = 3
+    X = f64(m["x"][b])
+    K, V, eK, eV = (oracle.matmul(X, f64(m[n])) for n in ("w_k", "w_v", "w_ek", "w_ev"))
+    rows = np.sort(np.random.default_rng(1).choice(w.N, 2048, replace=False))
+    D = w.D
+    Y = np.empty((len(rows), w.C))
+    for h in range(w.H):
+        sl = slice(h * D, (h + 1) * D)
+        Qh = oracle.sdpa(f64(m["qs"][h]), eK[:, sl], eV[:, sl])
+        Zh = oracle.sdpa(Qh, K[:, sl], V[:, sl])
+        Y[:, sl] = oracle.sdpa(K[rows, sl], Qh, Zh)
+    ref = oracle.matmul(Y, f64(m["w_o"]))
+    check_bf16(got[b][rows], ref, "FLARE++ block out (sampled)")

@@ -92,7 +92,7 @@ flare_status encode_impl(const View& q, const View& k, const View& v, void* z, i
   ep.tokens_per_split = pl.tokens_per_split;
   ep.c = c;
   ep.exact = (flags & FLARE_FLAG_EXACT_SOFTMAX) ? 1 : 0;
-  hipError_t e = k.is_f32 ? launch_encode_f32(ep, D, B, st) : launch_encode_bf16(ep, D, B, pl.waves, st);
+  hipError_t e = k.is_f32 ? launch_encode_f32(ep, D, B, st) : launch_encode_bf16(ep, D, B, pl.waves, pl.lat_blocks, st);
   if (e != hipSuccess) return FLARE_E_HIP;
   MergeParams mp;
   mp.part_o = ep.part_o;
@@ -131,11 +131,11 @@ flare_status decode_impl(const View& k, const View& q, const View& z, void* y, i
     dp.tokens_per_block = 256;
     return hip_status(launch_decode_f32(dp, D, B, st));
   }
-  // 8 waves x 64 tokens per pass; about 1024 workgroups in all, each doing
-  // at least one full pass.
-  const int64_t pass = 512;
+  // 4 waves x 64 tokens per pass; about 2048 workgroups in all (several per
+  // compute unit), each doing at least one full pass.
+  const int64_t pass = 256;
   const int64_t bh = (int64_t)B * H;
-  int64_t per_bh = (1024 + bh - 1) / bh;
+  int64_t per_bh = (2048 + bh - 1) / bh;
   int64_t tpb = (N + per_bh - 1) / per_bh;
   tpb = (tpb + pass - 1) / pass * pass;
   if (tpb < pass) tpb = pass;

@@ -53,6 +53,24 @@ template <> struct QkOp<16> {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + p.lo + p.hi for a dword holding two bf16 weights: v_dot2c_f32_bf16
+// against the constant pair (1.0, 1.0), exact in fp32.  Written as inline asm
+// (an ALU instruction, no memory access) because the ROCm 7.2 compiler picks
+// the wrong source sub-register when __builtin_amdgcn_fdot2_f32_bf16 is fed
+// pairs extracted from an 8-wide bf16 vector (every pair sums the first one).
+__device__ __forceinline__ float dot2_ones(uint32_t pair, float acc) {
+  asm("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(pair));
+  return acc;
+}
+
+// Sum of the 8 bf16 weights of a matrix-core operand, added to acc.
+__device__ __forceinline__ float rowsum_bf16x8(bf16x8 p, float acc) {
+  const u32x4 w = __builtin_bit_cast(u32x4, p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = dot2_ones(w[j], acc);
+  return acc;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }

@@ -5,13 +5,14 @@
 // the synthesized Q_h(X) here).
 //
 // A workgroup stages its head's latent side once in LDS, already in matrix-core
-// operand order: scale*log2(e)*Q as a bf16 hi/lo pair (A operand of
-// S^T = Q K^T) and Z transposed (A operand of Y^T = Z^T P^T).  Each wave then
-// streams 64-token groups of K straight from HBM into registers (one 16-byte
-// load per lane and 16-token block), walks the latents 32 at a time, and keeps
-// the whole per-token softmax inside the wave: a token's 32 latent scores of a
-// chunk sit in 4 lanes x (2 blocks x 4 rows), the normaliser comes out of the
-// matrix core through a ones row block, and no score is ever written out.
+// operand order: Q in bf16 (A operand of S^T = Q K^T) and Z transposed (A
+// operand of Y^T = Z^T P^T).  Each wave then streams 64-token groups of K
+// straight from HBM into registers (one 16-byte load per lane and 16-token
+// block), walks the latents 32 at a time and keeps every token's softmax
+// inside the wave: a token's 32 scores of a chunk sit in 4 lanes x 8
+// registers, the weights are packed to bf16 in place as the B operand of the
+// Z^T P^T product, and the normaliser is the dot2 sum of those packed
+// weights, reduced over the 4 lanes at the end.  No score leaves registers.
 //
 // As in the encoder, the first pass uses weights 2^x without a maximum; a
 // 64-token group whose normaliser leaves [2^-100, 2^100] (or whose output is
@@ -28,11 +29,14 @@ __device__ __forceinline__ int chunk_latent(int c, int g, int j) {
   return 32 * c + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeParams p) {
+constexpr int kDecWaves = 4;
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecWaves, 4) void decode_bf16_kernel(DecodeParams p) {
   using Op = QkOp<D>;
   using op_t = typename Op::type;
   constexpr int PL = Op::per_lane;
+  constexpr int NW = kDecWaves;
   constexpr int NT = 64 * NW;
   constexpr int DB = D / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -42,8 +46,9 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeParams p) {
   const int b = bh / p.H, h = bh - b * p.H;
   const int MC = (p.M + 31) / 32;  // 32-latent chunks
   const int MB = 2 * MC;           // 16-latent blocks
-  op_t* q_lds = reinterpret_cast<op_t*>(smem);                              // [MB][2][64]
-  bf16x8* z_lds = reinterpret_cast<bf16x8*>(smem + (size_t)MB * 2 * 64 * sizeof(op_t));  // [MC][DB][64]
+  const bool m_ragged = p.M != 32 * MC;
+  op_t* q_lds = reinterpret_cast<op_t*>(smem);                                           // [MB][64]
+  bf16x8* z_lds = reinterpret_cast<bf16x8*>(smem + (size_t)MB * 64 * sizeof(op_t));  // [MC][DB][64]
 
   // Stage Q: lane (g, r) of block nb holds latent 16nb + r, columns g*PL...
   for (int u = tid; u < MB * 64; u += NT) {
@@ -53,16 +58,10 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeParams p) {
 #pragma unroll
     for (int j = 0; j < PL; ++j) qv[j] = 0.f;
     if (m < p.M) load_as_f32<PL>(p.q.data, p.q.is_f32, b * p.q.sb + h * p.q.sh + (int64_t)m * p.q.sl + gg * PL, qv);
-    op_t hi, lo;
+    op_t qb;
 #pragma unroll
-    for (int j = 0; j < PL; ++j) {
-      bf16 a, c2;
-      split_bf16(qv[j] * p.c, a, c2);
-      hi[j] = a;
-      lo[j] = c2;
-    }
-    q_lds[(nb * 2 + 0) * 64 + ln] = hi;
-    q_lds[(nb * 2 + 1) * 64 + ln] = lo;
+    for (int j = 0; j < PL; ++j) qb[j] = (bf16)qv[j];
+    q_lds[nb * 64 + ln] = qb;
   }
   // Stage Z^T: row r of column block e is feature d = sigma(e, r), chosen so
   // that the output tile rows 4g..4g+3 of both blocks are 8 contiguous
@@ -82,76 +81,88 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
-  bf16x8 ones_full, ones_last;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    ones_full[j] = one;
-    ones_last[j] = chunk_latent(MC - 1, g, j) < p.M ? one : zero;
-  }
-
+  const bf16 zero = (bf16)0.0f;
+  const float cs = p.c;
   const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + h * p.k.sh;
   const int64_t n_begin = (int64_t)blockIdx.x * p.tokens_per_block;
   const int64_t n_end = min(p.N, n_begin + p.tokens_per_block);
 
-  for (int64_t base = n_begin + 64 * wave; base < n_end; base += 64 * NW) {
-    // B operands of S^T = Q K^T: lane (g, r) holds token base + 16t + r,
-    // features g*PL ...
-    op_t kb[4];
+  const int MCF = p.M / 32;  // chunks with all 32 latents valid
+
+  // B operands of S^T = Q K^T: lane (g, r) holds token base + 16t + r,
+  // features g*PL ...; the next 64-token group is loaded while the current
+  // one is computed.
+  auto load_k = [&](op_t (&kk)[4], int64_t base) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int64_t n = base + 16 * t + r;
       if (n < n_end) {
-        kb[t] = *reinterpret_cast<const op_t*>(kbase + n * p.k.sl + g * PL);
+        kk[t] = *reinterpret_cast<const op_t*>(kbase + n * p.k.sl + g * PL);
       } else {
 #pragma unroll
-        for (int j = 0; j < PL; ++j) kb[t][j] = zero;
+        for (int j = 0; j < PL; ++j) kk[t][j] = zero;
       }
     }
+  };
+  op_t kb[4], kn[4];
+  load_k(kb, n_begin + 64 * wave);
+  // Wait for the first group here, outside the loop: vmcnt counts loads and
+  // stores in order, and without this the compiler waits for everything
+  // (the next group's prefetch included) at the head of the latent loop.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
 
-    f32x4 yacc[4][DB], y1[4];
-    float mx[4];
-    auto pass = [&](auto exact_tag) {
+  for (int64_t base = n_begin + 64 * wave; base < n_end; base += 64 * NW) {
+    load_k(kn, base + 64 * NW);
+
+    f32x4 yacc[4][DB];
+    float lsum[4], mx[4];
+    // One 32-latent chunk against the 64 tokens.  MASK (only the last chunk
+    // when M is not a multiple of 32) gives padded latents weight 0.
+    auto chunk = [&](auto exact_tag, auto mask_tag, int c) {
       constexpr bool EXACT = decltype(exact_tag)::value;
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const op_t q0 = q_lds[(2 * c) * 64 + lane];
+      const op_t q1 = q_lds[(2 * c + 1) * 64 + lane];
+      bf16x8 za[DB];
+#pragma unroll
+      for (int e = 0; e < DB; ++e) za[e] = z_lds[(c * DB + e) * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x4 s0 = Op::mma(q0, kb[t], f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 s1 = Op::mma(q1, kb[t], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (EXACT) {
+            s0[i] = exp2_fast(s0[i] * cs - mx[t]);
+            s1[i] = exp2_fast(s1[i] * cs - mx[t]);
+          } else {
+            s0[i] = exp2_fast(s0[i] * cs);
+            s1[i] = exp2_fast(s1[i] * cs);
+          }
+          if constexpr (MASK) {
+            if (32 * c + 4 * g + i >= p.M) s0[i] = 0.f;
+            if (32 * c + 16 + 4 * g + i >= p.M) s1[i] = 0.f;
+          }
+        }
+        const bf16x8 pb = pack8(s0, s1);
+        lsum[t] = rowsum_bf16x8(pb, lsum[t]);
+#pragma unroll
+        for (int e = 0; e < DB; ++e) yacc[t][e] = mfma_16x16x32(za[e], pb, yacc[t][e]);
+      }
+    };
+    auto pass = [&](auto exact_tag) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
 #pragma unroll
         for (int e = 0; e < DB; ++e) yacc[t][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-        y1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lsum[t] = 0.f;
       }
-      for (int c = 0; c < MC; ++c) {
-        const op_t qh0 = q_lds[((2 * c) * 2 + 0) * 64 + lane];
-        const op_t ql0 = q_lds[((2 * c) * 2 + 1) * 64 + lane];
-        const op_t qh1 = q_lds[((2 * c + 1) * 2 + 0) * 64 + lane];
-        const op_t ql1 = q_lds[((2 * c + 1) * 2 + 1) * 64 + lane];
-        bf16x8 za[DB];
+      for (int c = 0; c < MCF; ++c) chunk(exact_tag, std::integral_constant<bool, false>(), c);
+      if (m_ragged) chunk(exact_tag, std::integral_constant<bool, true>(), MC - 1);
 #pragma unroll
-        for (int e = 0; e < DB; ++e) za[e] = z_lds[(c * DB + e) * 64 + lane];
-        const bf16x8 on = c == MC - 1 ? ones_last : ones_full;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
-          s0 = Op::mma(qh0, kb[t], s0);
-          s0 = Op::mma(ql0, kb[t], s0);
-          s1 = Op::mma(qh1, kb[t], s1);
-          s1 = Op::mma(ql1, kb[t], s1);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (EXACT) {
-              // padded latents (m >= M) carry weight 0; left unmasked,
-              // 2^(0 - max) could overflow and turn 0 * inf into NaN
-              s0[i] = 32 * c + 4 * g + i < p.M ? exp2_fast(s0[i] - mx[t]) : 0.f;
-              s1[i] = 32 * c + 16 + 4 * g + i < p.M ? exp2_fast(s1[i] - mx[t]) : 0.f;
-            } else {
-              s0[i] = exp2_fast(s0[i]);
-              s1[i] = exp2_fast(s1[i]);
-            }
-          }
-          const bf16x8 pb = pack8(s0, s1);
-#pragma unroll
-          for (int e = 0; e < DB; ++e) yacc[t][e] = mfma_16x16x32(za[e], pb, yacc[t][e]);
-          y1[t] = mfma_16x16x32(on, pb, y1[t]);
-        }
+      for (int t = 0; t < 4; ++t) {
+        lsum[t] += shfl_xor_f(lsum[t], 16);
+        lsum[t] += shfl_xor_f(lsum[t], 32);
       }
     };
 
@@ -161,7 +172,7 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeParams p) {
       bool bad = false;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float l = y1[t][0];
+        const float l = lsum[t];
         bool ok = l >= kSafeLo && l <= kSafeHi;
 #pragma unroll
         for (int e = 0; e < DB; ++e)
@@ -172,23 +183,17 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeParams p) {
       exact = __any(bad);
     }
     if (exact) {
-      // Row maximum of every token over all latents (padded latents masked).
+      // Row maximum of every token over all valid latents.
 #pragma unroll
       for (int t = 0; t < 4; ++t) mx[t] = -INFINITY;
-      for (int c = 0; c < MC; ++c) {
+      for (int nb = 0; nb < MB; ++nb) {
+        const op_t qb = q_lds[nb * 64 + lane];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const op_t qh = q_lds[((2 * c + half) * 2 + 0) * 64 + lane];
-          const op_t ql = q_lds[((2 * c + half) * 2 + 1) * 64 + lane];
+        for (int t = 0; t < 4; ++t) {
+          const f32x4 sc = Op::mma(qb, kb[t], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-            s = Op::mma(qh, kb[t], s);
-            s = Op::mma(ql, kb[t], s);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (16 * (2 * c + half) + 4 * g + i < p.M) mx[t] = fmaxf(mx[t], s[i]);
-          }
+          for (int i = 0; i < 4; ++i)
+            if (16 * nb + 4 * g + i < p.M) mx[t] = fmaxf(mx[t], sc[i] * cs);
         }
       }
 #pragma unroll
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeParams p) {
     for (int t = 0; t < 4; ++t) {
       const int64_t n = base + 16 * t + r;
       if (n >= n_end) continue;
-      const float inv = 1.0f / y1[t][0];
+      const float inv = 1.0f / lsum[t];
       float out[4 * DB];
 #pragma unroll
       for (int e = 0; e < DB; ++e)
@@ -232,6 +237,8 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeParams p) {
         }
       }
     }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kb[t] = kn[t];
   }
 }
 
@@ -294,10 +301,10 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------- launchers
 
-static size_t decode_bf16_lds(int M, int D) {
+size_t decode_bf16_lds(int M, int D) {
   const int MC = (M + 31) / 32;
   const size_t op_bytes = D == 32 ? 16 : 8;
-  return (size_t)2 * MC * 2 * 64 * op_bytes + (size_t)MC * (D / 16) * 64 * 16;
+  return (size_t)2 * MC * 64 * op_bytes + (size_t)MC * (D / 16) * 64 * 16;
 }
 
 // Kernels that stage more than 64 KB of LDS must opt in to the larger limit.
@@ -313,11 +320,11 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t s
   const size_t lds = decode_bf16_lds(p.M, D);
   hipError_t e;
   if (D == 32) {
-    if ((e = allow_lds(decode_bf16_kernel<32, 8>, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_bf16_kernel<32, 8>), grid, dim3(512), lds, st, p);
+    if ((e = allow_lds(decode_bf16_kernel<32>, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_bf16_kernel<32>), grid, dim3(64 * kDecWaves), lds, st, p);
   } else {
-    if ((e = allow_lds(decode_bf16_kernel<16, 8>, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_bf16_kernel<16, 8>), grid, dim3(512), lds, st, p);
+    if ((e = allow_lds(decode_bf16_kernel<16>, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_bf16_kernel<16>), grid, dim3(64 * kDecWaves), lds, st, p);
   }
   return hipGetLastError();
 }

@@ -6,29 +6,35 @@
 // synthesis (equation 8) is the same call with learned seeds as Q.
 //
 // The N tokens of each (batch, head) are cut into S contiguous splits.  One
-// workgroup owns one split and every latent of its head: it streams 64-token
-// K/V tiles from HBM into LDS (double buffered, one barrier per tile) and each
-// wave multiplies them against its 64 latents on bf16 matrix cores.  Per split
-// it emits the normalised partial output and the split's log-normaliser; the
-// merge kernel combines splits exactly by logsumexp, the reduction the pages
-// give for token-sharded encoders ("Multi-GPU context parallelism").
+// workgroup owns one split and all latents of its head (64 per wave): it
+// streams 64-token K/V tiles from HBM into LDS (double buffered, one barrier
+// per tile) and every wave multiplies them against its latents on bf16
+// matrix cores, 32 tokens at a time.  Per split it writes the normalised
+// partial output and the split's log-normaliser; the merge kernel combines
+// the splits exactly by logsumexp, the reduction the pages give for
+// token-sharded encoders ("Multi-GPU context parallelism").
 //
-// Softmax: scores are formed directly in log2 units by splitting
-// scale*log2(e)*Q into a bf16 hi + lo pair (two MFMAs, ~2^-17 relative), so
-// p = exp2(x) needs no multiply.  The first pass runs without a running
-// maximum (weights relative to 2^0); a split is accepted when every latent's
-// normaliser lies in [2^-100, 2^100] and its output is finite, which rules
-// out overflow and underflow, and the weights then equal the max-shifted ones
-// up to rounding.  Otherwise the workgroup reruns the split with the exact
-// running-maximum online softmax (always used with FLARE_FLAG_EXACT_SOFTMAX).
+// On gfx950 matrix-core and vector work largely add up rather than overlap,
+// so the per-score instruction count is what the design minimises:
+//   scores   s = K Q^T on v_mfma_f32_16x16x32_bf16 (bf16 Q, fp32 accumulate),
+//   weights  p = exp2(s * scale*log2 e): one v_mul, one v_exp_f32,
+//   packing  two weights per v_cvt_pk_bf16_f32 (the A operand of P V),
+//   row sums v_dot2c_f32_bf16 of the packed weights against (1, 1), i.e. the
+//            normaliser sums exactly the rounded weights the numerator uses.
+// The first pass runs without a running maximum (weights relative to 2^0);
+// a split is accepted when every latent's normaliser lies in [2^-100, 2^100]
+// and its output is finite, which rules out overflow and underflow, and the
+// weights are then the max-shifted ones up to rounding.  Otherwise the
+// workgroup reruns the split with the exact running-maximum online softmax
+// (always used with FLARE_FLAG_EXACT_SOFTMAX).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace flare {
 
-constexpr int kEncT = 64;  // tokens per tile
+constexpr int kEncT = 128;  // tokens per LDS tile (four 32-token quarters)
 
-template <int D, int NW>
+template <int D, int NW, int NB_>
 struct EncodeKernel {
   using Op = QkOp<D>;
   using op_t = typename Op::type;
@@ -36,38 +42,67 @@ struct EncodeKernel {
   static constexpr int NT = 64 * NW;
   static constexpr int KROW = D + 8;  // padded LDS row: conflict-free operand reads
   static constexpr int DB = D / 16;   // 16-wide column blocks of D
-  static constexpr int NB = 4;        // 16-latent blocks per wave (64 latents)
+  static constexpr int NB = NB_;      // 16-latent blocks per wave
+  static constexpr int NQ = kEncT / 32;                  // 32-token quarters per tile
   static constexpr int K_UNITS = kEncT * D / 8;          // 16-byte chunks of a K tile
   static constexpr int V_UNITS = (kEncT / 4) * (D / 2);  // (token quad, d pair) of a V tile
   static constexpr int K_PER = (K_UNITS + NT - 1) / NT;
   static constexpr int V_PER = (V_UNITS + NT - 1) / NT;
   static constexpr int K_ELEMS = kEncT * KROW;
-  static constexpr int V_ELEMS = 2 * DB * 64 * 8;
+  static constexpr int V_ELEMS = NQ * DB * 64 * 8;
 };
 
-template <int D, int NW, bool EXACT>
+// V staging unit u -> (token quad q4 of the tile, column pair dp, which of the
+// pair's two rows is written first).  The destination bank of a V write
+// depends only on (column r = d % 16, half = which 4 of the lane's 8 tokens),
+// so the mapping spreads every wave's 64 lanes over all 32 (r, half) slots,
+// twice: a 2-way access, the minimum for 512 bytes.
+template <int D>
+__device__ __forceinline__ void v_unit(int u, int& q4, int& dp, int& par) {
+  if constexpr (D == 32) {
+    dp = u & 15;
+    const int j = (u >> 4) & 3, w = u >> 6;
+    const int half = j & 1, c = ((w >> 2) << 1) | (j >> 1), gg = w & 3;
+    q4 = c * 8 + half * 4 + gg;
+    par = dp >> 3;
+  } else {
+    dp = u & 7;
+    const int b3 = (u >> 3) & 1, half = (u >> 4) & 1, b5 = (u >> 5) & 1, c = u >> 6;
+    const int gg = b3 | (b5 << 1);
+    q4 = c * 8 + half * 4 + gg;
+    par = b3;
+  }
+}
+
+template <int D, int NW, int NB_, bool EXACT>
 __device__ __forceinline__ void encode_pass(
     const EncodeParams& p, const bf16* __restrict__ kbase, const bf16* __restrict__ vbase,
     int64_t n_begin, int64_t n_end, int ntiles, bf16* k_lds, bf16* v_lds,
-    const typename QkOp<D>::type (&qhi)[4], const typename QkOp<D>::type (&qlo)[4],
-    f32x4 (&o)[4][D / 16], f32x4 (&o1)[4], float (&mrun)[4]) {
-  using KC = EncodeKernel<D, NW>;
+    const typename QkOp<D>::type (&qop)[NB_], f32x4 (&o)[NB_][D / 16], float (&lsum)[NB_],
+    float (&mrun)[NB_]) {
+  using KC = EncodeKernel<D, NW, NB_>;
   using op_t = typename KC::op_t;
-  constexpr int PL = KC::PL, NT = KC::NT, KROW = KC::KROW, DB = KC::DB, NB = KC::NB;
+  constexpr int PL = KC::PL, NT = KC::NT, KROW = KC::KROW, DB = KC::DB, NB = KC::NB, NQ = KC::NQ;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const float cs = p.c;
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
     for (int e = 0; e < DB; ++e) o[nb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    o1[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lsum[nb] = 0.f;
     mrun[nb] = -INFINITY;
   }
 
-  u32x4 kreg[KC::K_PER];
-  uint32_t vreg[KC::V_PER][4];
+  struct Stage {
+    u32x4 k[KC::K_PER];
+    uint32_t v[KC::V_PER][4];
+  };
+  Stage sa, sb;
 
-  auto load_tile = [&](int it) {
+  auto load_tile = [&](Stage& st, int it) {
+    u32x4 (&kreg)[KC::K_PER] = st.k;
+    uint32_t (&vreg)[KC::V_PER][4] = st.v;
     const int64_t t0 = n_begin + (int64_t)it * kEncT;
 #pragma unroll
     for (int ui = 0; ui < KC::K_PER; ++ui) {
@@ -76,8 +111,7 @@ __device__ __forceinline__ void encode_pass(
       if (u < KC::K_UNITS) {
         const int n = u / (D / 8), dc = u % (D / 8);
         const int64_t tok = t0 + n;
-        if (tok < n_end)
-          kreg[ui] = *reinterpret_cast<const u32x4*>(kbase + tok * p.k.sl + dc * 8);
+        if (tok < n_end) kreg[ui] = *reinterpret_cast<const u32x4*>(kbase + tok * p.k.sl + dc * 8);
       }
     }
 #pragma unroll
@@ -86,22 +120,24 @@ __device__ __forceinline__ void encode_pass(
 #pragma unroll
       for (int i = 0; i < 4; ++i) vreg[ui][i] = 0u;
       if (u < KC::V_UNITS) {
-        const int q4 = u / (D / 2), dp = u % (D / 2);
+        int q4, dp, par;
+        v_unit<D>(u, q4, dp, par);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t tok = t0 + 4 * q4 + i;
-          if (tok < n_end)
-            vreg[ui][i] = *reinterpret_cast<const uint32_t*>(vbase + tok * p.v.sl + 2 * dp);
+          if (tok < n_end) vreg[ui][i] = *reinterpret_cast<const uint32_t*>(vbase + tok * p.v.sl + 2 * dp);
         }
       }
     }
   };
 
   // K tile: plain rows [token][d] (padded).  V tile: the B operand of the
-  // P V product, transposed so that lane (g, r) of chunk c and column block e
-  // finds its 8 tokens contiguous: j < 4 -> token 32c + 4g + j,
+  // P V product, transposed so that lane (g, r) of quarter c and column block
+  // e finds its 8 tokens contiguous: j < 4 -> token 32c + 4g + j,
   // j >= 4 -> token 32c + 16 + 4g + (j - 4), column d = 16e + r.
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](const Stage& st, int buf) {
+    const u32x4 (&kreg)[KC::K_PER] = st.k;
+    const uint32_t (&vreg)[KC::V_PER][4] = st.v;
     bf16* kt = k_lds + buf * KC::K_ELEMS;
     bf16* vt = v_lds + buf * KC::V_ELEMS;
 #pragma unroll
@@ -116,62 +152,55 @@ __device__ __forceinline__ void encode_pass(
     for (int ui = 0; ui < KC::V_PER; ++ui) {
       const int u = tid + ui * NT;
       if (u < KC::V_UNITS) {
-        const int q4 = u / (D / 2), dp = u % (D / 2);
+        int q4, dp, par;
+        v_unit<D>(u, q4, dp, par);
         const uint32_t* w = vreg[ui];
-        // (token i, d even) halves and (token i, d odd) halves, paired by token
-        const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+        // the four tokens' even-d halves, and their odd-d halves, paired
+        const u32x2 even = {__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
+                            __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)};
+        const u32x2 odd = {__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
+                           __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)};
         const int c = q4 >> 3, qq = q4 & 7, gg = qq & 3, half = qq >> 2;
         const int d0 = 2 * dp, e0 = d0 >> 4, rr0 = d0 & 15;
         const int off0 = ((c * DB + e0) * 64 + 16 * gg + rr0) * 8 + half * 4;
-        *reinterpret_cast<u32x2*>(vt + off0) = u32x2{lo01, lo23};
-        *reinterpret_cast<u32x2*>(vt + off0 + 8) = u32x2{hi01, hi23};
+        if (par) {
+          *reinterpret_cast<u32x2*>(vt + off0 + 8) = odd;
+          *reinterpret_cast<u32x2*>(vt + off0) = even;
+        } else {
+          *reinterpret_cast<u32x2*>(vt + off0) = even;
+          *reinterpret_cast<u32x2*>(vt + off0 + 8) = odd;
+        }
       }
     }
   };
 
-  const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
-
-  auto compute_tile = [&](int buf, int it) {
-    const bf16* kt = k_lds + buf * KC::K_ELEMS;
-    const bf16* vt = v_lds + buf * KC::V_ELEMS;
-    const int64_t t0 = n_begin + (int64_t)it * kEncT;
-    const bool ragged = t0 + kEncT > n_end;
-
-    // scores S^T[token][latent] in log2 units: lane (g, r) of tile (t, nb)
-    // holds token 16t + 4g + i against latent 16nb + r
-    f32x4 sc[4][NB];
+  // 32 tokens (quarter c of the tile) against the wave's 64 latents.  The
+  // RAGGED variant (only the last tile of a split) gives the tokens past the
+  // end weight 0.
+  auto compute_quarter = [&](auto ragged_tag, const bf16* kt, const bf16* vt, int64_t t0, int c) {
+    constexpr bool RAGGED = decltype(ragged_tag)::value;
+    // S^T tiles: lane (g, r) of (tt, nb) holds token 32c + 16tt + 4g + i
+    // against latent 16nb + r (raw dot products).
+    f32x4 s[2][NB];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const op_t ka = *reinterpret_cast<const op_t*>(kt + (16 * t + r) * KROW + g * PL);
+    for (int tt = 0; tt < 2; ++tt) {
+      const op_t ka = *reinterpret_cast<const op_t*>(kt + (32 * c + 16 * tt + r) * KROW + g * PL);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-        a = KC::Op::mma(ka, qhi[nb], a);
-        a = KC::Op::mma(ka, qlo[nb], a);
-        sc[t][nb] = a;
-      }
+      for (int nb = 0; nb < NB; ++nb) s[tt][nb] = KC::Op::mma(ka, qop[nb], f32x4{0.f, 0.f, 0.f, 0.f});
     }
-
     if constexpr (EXACT) {
-      if (ragged) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t0 + 16 * t + 4 * g + i >= n_end)
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = !RAGGED || t0 + 32 * c + 16 * tt + 4 * g + i < n_end;
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb) sc[t][nb][i] = -INFINITY;
-      }
+          for (int nb = 0; nb < NB; ++nb) s[tt][nb][i] = valid ? s[tt][nb][i] * cs : -INFINITY;
+        }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][nb][i]);
+        float mx = fmaxf(fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3])),
+                         fmaxf(fmaxf(s[1][nb][0], s[1][nb][1]), fmaxf(s[1][nb][2], s[1][nb][3])));
         mx = fmaxf(mx, shfl_xor_f(mx, 16));
         mx = fmaxf(mx, shfl_xor_f(mx, 32));
         const float mnew = fmaxf(mrun[nb], mx);
@@ -179,66 +208,89 @@ __device__ __forceinline__ void encode_pass(
         const float alpha = exp2_fast(mrun[nb] - mref);
         mrun[nb] = mnew;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[t][nb][i] = exp2_fast(sc[t][nb][i] - mref);
-        // accumulator row 4g + i belongs to latent 16nb + 4g + i, whose
-        // factor sits in lane r = 4g + i
+          for (int i = 0; i < 4; ++i) s[tt][nb][i] = exp2_fast(s[tt][nb][i] - mref);
+        lsum[nb] *= alpha;
+        // accumulator row 4g + i is latent 16nb + 4g + i, whose factor sits in
+        // lane r = 4g + i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float ai = __shfl(alpha, 4 * g + i, 64);
 #pragma unroll
           for (int e = 0; e < DB; ++e) o[nb][e][i] *= ai;
-          o1[nb][i] *= ai;
         }
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[t][nb][i] = exp2_fast(sc[t][nb][i]);
+          for (int i = 0; i < 4; ++i) s[tt][nb][i] = exp2_fast(s[tt][nb][i] * cs);
+      if constexpr (RAGGED) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool valid = t0 + 32 * c + 16 * tt + 4 * g + i < n_end;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) s[tt][nb][i] = valid ? s[tt][nb][i] : 0.f;
+          }
+      }
     }
-
-    // O[latent][d] += P V and the normaliser via a ones column block;
-    // padded tokens carry V = 0 and a 0 in the ones operand.
+    bf16x8 vb[DB];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8 vb[DB];
+    for (int e = 0; e < DB; ++e) vb[e] = *reinterpret_cast<const bf16x8*>(vt + ((c * DB + e) * 64 + lane) * 8);
 #pragma unroll
-      for (int e = 0; e < DB; ++e)
-        vb[e] = *reinterpret_cast<const bf16x8*>(vt + ((c * DB + e) * 64 + lane) * 8);
-      bf16x8 ones;
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8 pa = pack8(s[0][nb], s[1][nb]);
+      lsum[nb] = rowsum_bf16x8(pa, lsum[nb]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = 32 * c + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
-        ones[j] = (!ragged || t0 + n < n_end) ? one : zero;
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 pa = pack8(sc[2 * c][nb], sc[2 * c + 1][nb]);
-#pragma unroll
-        for (int e = 0; e < DB; ++e) o[nb][e] = mfma_16x16x32(pa, vb[e], o[nb][e]);
-        o1[nb] = mfma_16x16x32(pa, ones, o1[nb]);
-      }
+      for (int e = 0; e < DB; ++e) o[nb][e] = mfma_16x16x32(pa, vb[e], o[nb][e]);
     }
   };
 
-  load_tile(0);
-  store_tile(0);
+  auto compute_tile = [&](int it) {
+    const int buf = it & 1;
+    const bf16* kt = k_lds + buf * KC::K_ELEMS;
+    const bf16* vt = v_lds + buf * KC::V_ELEMS;
+    const int64_t t0 = n_begin + (int64_t)it * kEncT;
+    if (t0 + kEncT <= n_end) {
+#pragma unroll 1
+      for (int c = 0; c < NQ; ++c) compute_quarter(std::integral_constant<bool, false>(), kt, vt, t0, c);
+    } else {
+#pragma unroll 1
+      for (int c = 0; c < NQ; ++c) compute_quarter(std::integral_constant<bool, true>(), kt, vt, t0, c);
+    }
+  };
+
+  // Two-deep prefetch: while tile it is computed from LDS buffer it % 2, the
+  // loads of tile it + 2 are in flight into one register set and tile it + 1
+  // (loaded one tile earlier) is written from the other set into the free
+  // buffer.  The loop is unrolled by two so both register sets are static.
+  load_tile(sa, 0);
+  if (ntiles > 1) load_tile(sb, 1);
+  store_tile(sa, 0);
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) load_tile(it + 1);
-    compute_tile(it & 1, it);
-    if (it + 1 < ntiles) store_tile((it + 1) & 1);
+  for (int it = 0; it < ntiles; it += 2) {
+    // even tile: compute it, stream it + 2 into sa, write it + 1 from sb
+    if (it + 2 < ntiles) load_tile(sa, it + 2);
+    compute_tile(it);
+    if (it + 1 < ntiles) store_tile(sb, 1);
+    __syncthreads();
+    if (it + 1 >= ntiles) break;
+    // odd tile: compute it + 1, stream it + 3 into sb, write it + 2 from sa
+    if (it + 3 < ntiles) load_tile(sb, it + 3);
+    compute_tile(it + 1);
+    if (it + 2 < ntiles) store_tile(sa, 0);
     __syncthreads();
   }
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void encode_bf16_kernel(EncodeParams p) {
-  using KC = EncodeKernel<D, NW>;
+template <int D, int NW, int NB_>
+__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 4 : 3)) void encode_bf16_kernel(EncodeParams p) {
+  using KC = EncodeKernel<D, NW, NB_>;
   using op_t = typename KC::op_t;
   constexpr int PL = KC::PL, DB = KC::DB, NB = KC::NB;
   __shared__ __attribute__((aligned(16))) bf16 k_lds[2 * KC::K_ELEMS];
@@ -255,69 +307,70 @@ __global__ __launch_bounds__(64 * NW) void encode_bf16_kernel(EncodeParams p) {
   const bf16* vbase = reinterpret_cast<const bf16*>(p.v.data) + b * p.v.sb + h * p.v.sh;
 
   // B operands of S^T = K Q^T: lane (g, r) holds latent 16nb + r, columns
-  // g*PL .. g*PL+PL-1 of scale*log2(e)*Q as a bf16 hi/lo pair.
-  op_t qhi[NB], qlo[NB];
+  // g*PL .. g*PL + PL - 1 of Q in bf16 (fp32 queries are rounded once).
+  op_t qop[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int m = wave * 64 + nb * 16 + r;
+    const int m = wave * 16 * NB + nb * 16 + r;
     float qv[PL];
 #pragma unroll
     for (int j = 0; j < PL; ++j) qv[j] = 0.f;
     if (m < p.M) load_as_f32<PL>(p.q.data, p.q.is_f32, b * p.q.sb + h * p.q.sh + m * p.q.sl + g * PL, qv);
 #pragma unroll
-    for (int j = 0; j < PL; ++j) {
-      bf16 hi, lo;
-      split_bf16(qv[j] * p.c, hi, lo);
-      qhi[nb][j] = hi;
-      qlo[nb][j] = lo;
-    }
+    for (int j = 0; j < PL; ++j) qop[nb][j] = (bf16)qv[j];
   }
 
-  f32x4 o[NB][DB], o1[NB];
-  float mrun[NB];
+  f32x4 o[NB][DB];
+  float lsum[NB], mrun[NB];
   if (tid == 0) need_exact = p.exact;
   __syncthreads();
   bool exact = need_exact != 0;
   if (!exact) {
-    encode_pass<D, NW, false>(p, kbase, vbase, n_begin, n_end, ntiles, k_lds, v_lds, qhi, qlo, o, o1, mrun);
+    encode_pass<D, NW, NB_, false>(p, kbase, vbase, n_begin, n_end, ntiles, k_lds, v_lds, qop, o, lsum, mrun);
     bool bad = false;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+      float l = lsum[nb];
+      l += shfl_xor_f(l, 16);
+      l += shfl_xor_f(l, 32);
+      const bool ok_l = l >= kSafeLo && l <= kSafeHi;
+      bool ok_o = true;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wave * 64 + nb * 16 + 4 * g + i;
-        const float l = o1[nb][i];
-        bool ok = l >= kSafeLo && l <= kSafeHi;
+      for (int e = 0; e < DB; ++e)
 #pragma unroll
-        for (int e = 0; e < DB; ++e) ok = ok && __builtin_isfinite(o[nb][e][i]);
-        bad = bad || (m < p.M && n_end > n_begin && !ok);
-      }
+        for (int i = 0; i < 4; ++i) ok_o = ok_o && __builtin_isfinite(o[nb][e][i]);
+      bad = bad || (wave * 16 * NB + nb * 16 + r < p.M && !ok_l) || (wave * 16 * NB + nb * 16 + 4 * g < p.M && !ok_o);
+    }
     if (__any(bad) && lane == 0) need_exact = 1;
     __syncthreads();
-    exact = need_exact != 0;
+    exact = need_exact != 0 && n_end > n_begin;
   }
   if (exact)
-    encode_pass<D, NW, true>(p, kbase, vbase, n_begin, n_end, ntiles, k_lds, v_lds, qhi, qlo, o, o1, mrun);
+    encode_pass<D, NW, NB_, true>(p, kbase, vbase, n_begin, n_end, ntiles, k_lds, v_lds, qop, o, lsum, mrun);
 
   // Epilogue: normalised split output and log2-normaliser of every latent.
   float* po = p.part_o + ((int64_t)bh * p.S + s) * p.M * D;
   float* pl = p.part_l + ((int64_t)bh * p.S + s) * p.M;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NB; ++nb) {
+    float l = lsum[nb];  // score layout: lane (g, r) holds latent 16nb + r
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    const float mr = exact ? mrun[nb] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float mr_lane = exact ? mrun[nb] : 0.f;
-      const float mref = __shfl(mr_lane, 4 * g + i, 64);
-      const int m = wave * 64 + nb * 16 + 4 * g + i;
-      const float l = o1[nb][i];
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      const float lse2 = l > 0.f ? __log2f(l) + (mref == -INFINITY ? 0.f : mref) : -INFINITY;
+      const float li = __shfl(l, 4 * g + i, 64);  // output layout: row 4g + i
+      const float mi = __shfl(mr, 4 * g + i, 64);
+      const int m = wave * 16 * NB + nb * 16 + 4 * g + i;
+      const float inv = li > 0.f ? 1.0f / li : 0.f;
+      const float lse2 = li > 0.f ? __log2f(li) + (mi == -INFINITY ? 0.f : mi) : -INFINITY;
       if (m < p.M) {
 #pragma unroll
         for (int e = 0; e < DB; ++e) po[(int64_t)m * D + 16 * e + r] = o[nb][e][i] * inv;
         if (r == 0) pl[m] = lse2;
       }
     }
+  }
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -384,33 +437,56 @@ __global__ __launch_bounds__(256) void encode_f32_kernel(EncodeParams p) {
 
 // ------------------------------------------------------------------- merge
 // L = log2 sum_s 2^{L_s};  Z = sum_s 2^{L_s - L} O_s  (the exact combination
-// of split encoders; an empty split has L_s = -inf and weight 0).
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  const int bh = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= p.M * p.D) return;
-  const int m = idx / p.D, d = idx - m * p.D;
+// of split encoders; an empty split has L_s = -inf and weight 0).  One
+// workgroup per (batch*head, latent): 256 threads = G split groups x D
+// features; every thread folds its splits with an online logsumexp, and the
+// G partial results are combined through LDS.
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
+  __shared__ float sm_m[kMergeThreads], sm_l[kMergeThreads], sm_a[kMergeThreads];
+  const int bh = blockIdx.y, m = blockIdx.x, tid = threadIdx.x;
+  const int G = kMergeThreads / p.D;  // split groups
+  const int grp = tid / p.D, d = tid - grp * p.D;
   const float* pl = p.part_l + (int64_t)bh * p.S * p.M + m;
-  const float* po = p.part_o + (int64_t)bh * p.S * p.M * p.D + idx;
-  float mx = -INFINITY;
-  for (int s = 0; s < p.S; ++s) mx = fmaxf(mx, pl[(int64_t)s * p.M]);
-  float sum = 0.f;
-  if (mx != -INFINITY)
-    for (int s = 0; s < p.S; ++s) sum += exp2f(pl[(int64_t)s * p.M] - mx);
-  const float L = mx != -INFINITY ? mx + log2f(sum) : -INFINITY;
-  float z = 0.f;
-  if (mx != -INFINITY)
-    for (int s = 0; s < p.S; ++s) {
-      const float w = exp2f(pl[(int64_t)s * p.M] - L);
-      z = fmaf(w, po[(int64_t)s * p.M * p.D], z);
+  const float* po = p.part_o + ((int64_t)bh * p.S * p.M + m) * p.D + d;
+  float mx = -INFINITY, sum = 0.f, acc = 0.f;
+  for (int s = grp; s < p.S; s += G) {
+    const float ls = pl[(int64_t)s * p.M];
+    const float os = po[(int64_t)s * p.M * p.D];
+    if (ls == -INFINITY) continue;
+    if (ls > mx) {
+      const float a = exp2f(mx - ls);
+      sum *= a;
+      acc *= a;
+      mx = ls;
     }
+    const float w = exp2f(ls - mx);
+    sum += w;
+    acc = fmaf(w, os, acc);
+  }
+  sm_m[tid] = mx;
+  sm_l[tid] = sum;
+  sm_a[tid] = acc;
+  __syncthreads();
+  if (grp != 0) return;
+  float M_ = -INFINITY;
+  for (int q = 0; q < G; ++q) M_ = fmaxf(M_, sm_m[q * p.D + d]);
+  float L = 0.f, A = 0.f;
+  if (M_ != -INFINITY)
+    for (int q = 0; q < G; ++q) {
+      const float w = exp2f(sm_m[q * p.D + d] - M_);
+      L += w * sm_l[q * p.D + d];
+      A += w * sm_a[q * p.D + d];
+    }
+  const float z = L > 0.f ? A / L : 0.f;
   const int b = bh / p.H, h = bh - b * p.H;
   const int64_t off = b * p.z_sb + h * p.z_sh + (int64_t)m * p.z_sl + d;
   if (p.z_f32)
     reinterpret_cast<float*>(p.z)[off] = z;
   else
     reinterpret_cast<bf16*>(p.z)[off] = (bf16)z;
-  if (p.lse && d == 0) p.lse[(int64_t)bh * p.M + m] = L * kLn2;
+  if (p.lse && d == 0) p.lse[(int64_t)bh * p.M + m] = L > 0.f ? (M_ + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -419,10 +495,12 @@ EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32) {
   (void)D;
   EncodePlan pl;
   const int64_t bh = (int64_t)B * H;
-  pl.waves = M <= 64 ? 1 : M <= 128 ? 2 : M <= 256 ? 4 : 8;
-  // Fill the 256 compute units several times over; a split holds at least
-  // 256 tokens (4 tiles) so per-split overheads stay small.
-  const int64_t target = is_f32 ? 512 : (pl.waves == 8 ? 512 : 1024);
+  // 32 latents per wave; all latents of a head in one workgroup.
+  pl.waves = M <= 64 ? 2 : M <= 128 ? 4 : M <= 256 ? 8 : 16;
+  pl.lat_blocks = 2;
+  // About two workgroups per compute unit at a time, a few rounds in all; a
+  // split holds at least 256 tokens (2 tiles) so per-split overheads stay small.
+  const int64_t target = is_f32 ? 512 : 1024;
   int64_t S = (target + bh - 1) / bh;
   const int64_t max_s = (N + 255) / 256;
   if (S > max_s) S = max_s;
@@ -434,24 +512,21 @@ EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32) {
   return pl;
 }
 
-hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, hipStream_t st) {
+hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, int lat_blocks, hipStream_t st) {
   dim3 grid(p.S, B * p.H);
-#define FLARE_ENC(DD, NW) \
-  hipLaunchKernelGGL((encode_bf16_kernel<DD, NW>), grid, dim3(64 * NW), 0, st, p)
+#define FLARE_ENC(DD, NW, NB) \
+  hipLaunchKernelGGL((encode_bf16_kernel<DD, NW, NB>), grid, dim3(64 * NW), 0, st, p)
+  (void)lat_blocks;
   if (D == 32) {
-    switch (waves) {
-      case 1: FLARE_ENC(32, 1); break;
-      case 2: FLARE_ENC(32, 2); break;
-      case 4: FLARE_ENC(32, 4); break;
-      default: FLARE_ENC(32, 8); break;
-    }
+    if (waves == 2) FLARE_ENC(32, 2, 2);
+    else if (waves == 4) FLARE_ENC(32, 4, 2);
+    else if (waves == 8) FLARE_ENC(32, 8, 2);
+    else FLARE_ENC(32, 16, 2);
   } else {
-    switch (waves) {
-      case 1: FLARE_ENC(16, 1); break;
-      case 2: FLARE_ENC(16, 2); break;
-      case 4: FLARE_ENC(16, 4); break;
-      default: FLARE_ENC(16, 8); break;
-    }
+    if (waves == 2) FLARE_ENC(16, 2, 2);
+    else if (waves == 4) FLARE_ENC(16, 4, 2);
+    else if (waves == 8) FLARE_ENC(16, 8, 2);
+    else FLARE_ENC(16, 16, 2);
   }
 #undef FLARE_ENC
   return hipGetLastError();
@@ -467,8 +542,8 @@ hipError_t launch_encode_f32(const EncodeParams& p, int D, int B, hipStream_t st
 }
 
 hipError_t launch_merge(const MergeParams& p, int B, hipStream_t st) {
-  dim3 grid((p.M * p.D + 255) / 256, B * p.H);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, st, p);
+  dim3 grid(p.M, B * p.H);
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(kMergeThreads), 0, st, p);
   return hipGetLastError();
 }
 

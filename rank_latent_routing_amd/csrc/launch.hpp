@@ -64,10 +64,11 @@ struct EncodePlan {
   int S;                    // number of token splits
   int64_t tokens_per_split; // multiple of 64
   int waves;                // waves per workgroup (bf16 path)
+  int lat_blocks;           // 16-latent blocks per wave (bf16 path)
 };
 EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32);
 
-hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, hipStream_t s);
+hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, int lat_blocks, hipStream_t s);
 hipError_t launch_encode_f32(const EncodeParams& p, int D, int B, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int B, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t s);

@@ -37,6 +37,8 @@ bool token_tensor_ok(const flare_tensor* t) {
   if (reinterpret_cast<uintptr_t>(t->data) % 16) return false;
   const int64_t q = t->dtype == FLARE_BF16 ? 8 : 4;
   if (t->stride_b < 0 || t->stride_h < 0 || t->stride_l < 0) return false;
+  // the kernels address a 128-token tile with 32-bit byte offsets
+  if (t->stride_l >= (int64_t(1) << 22)) return false;
   return t->stride_b % q == 0 && t->stride_h % q == 0 && t->stride_l % q == 0;
 }
 
@@ -131,15 +133,7 @@ flare_status decode_impl(const View& k, const View& q, const View& z, void* y, i
     dp.tokens_per_block = 256;
     return hip_status(launch_decode_f32(dp, D, B, st));
   }
-  // 4 waves x 64 tokens per pass; about 2048 workgroups in all (several per
-  // compute unit), each doing at least one full pass.
-  const int64_t pass = 256;
-  const int64_t bh = (int64_t)B * H;
-  int64_t per_bh = (2048 + bh - 1) / bh;
-  int64_t tpb = (N + per_bh - 1) / per_bh;
-  tpb = (tpb + pass - 1) / pass * pass;
-  if (tpb < pass) tpb = pass;
-  dp.tokens_per_block = tpb;
+  dp.tokens_per_block = plan_decode_bf16(B, H, M, N, D);  // workgroups per head
   return hip_status(launch_decode_bf16(dp, D, B, st));
 }
 

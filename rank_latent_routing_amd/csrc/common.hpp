@@ -1,11 +1,17 @@
 // Device-side types and helpers shared by the gfx950 kernels.
 //
 // Matrix-core layouts used throughout (CDNA3/CDNA4 MFMA, wave64):
+//   v_mfma_f32_32x32x16_bf16  A: lane l holds A[l%32][8*(l/32) + j], j < 8
+//                             B: lane l holds B[8*(l/32) + j][l%32]
+//                             C/D: lane l holds C[8*(i/4) + 4*(l/32) + i%4][l%32], i < 16
 //   v_mfma_f32_16x16x32_bf16  A: lane l holds A[l%16][8*(l/16) + j], j < 8
 //                             B: lane l holds B[8*(l/16) + j][l%16]
 //                             C/D: lane l holds C[4*(l/16) + i][l%16], i < 4
 //   v_mfma_f32_16x16x16_bf16  same with 4 K-elements per lane: k = 4*(l/16) + j
-// We write g = l/16 (lane group) and r = l%16.
+// With 32x32 tiles we write h = l/32 and c = l%32; with 16x16 tiles g = l/16
+// and r = l%16.  Only the (row, column) placement matters for correctness:
+// both operands of a product always put the same reduction index in the same
+// (lane group, element) slot.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,6 +24,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -31,6 +38,10 @@ constexpr float kSafeHi = 1.2676506002282294e30f;  // 2^100
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma_16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
@@ -82,10 +93,18 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
   return r;
 }
 
-// Split x into bf16 hi + lo with hi + lo = x to about 2^-17 relative.
-__device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
-  hi = (bf16)x;
-  lo = (bf16)(x - (float)hi);
+__device__ __forceinline__ bf16x8 pack8_16(const f32x16& v, int half) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)v[8 * half + j];
+  return r;
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
 }
 
 // Load n consecutive elements (bf16 or fp32) starting at element offset
@@ -102,6 +121,26 @@ __device__ __forceinline__ void load_as_f32(const void* base, int is_f32, int64_
     for (int j = 0; j < n; ++j) out[j] = (float)p[j];
   }
 }
+
+// Workgroup barrier that keeps global loads and LDS-DMA transfers in flight.
+// __syncthreads() is a workgroup release/acquire fence around s_barrier, and
+// on gfx9 that fence waits for every outstanding vector-memory operation
+// (vmcnt(0)), which would drain a prefetch pipeline at every tile.  Here the
+// caller first waits explicitly for exactly the transfers the other waves
+// need (s_waitcnt vmcnt(n) lgkmcnt(0)); the empty asm statements only stop
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediates for gfx9: vmcnt(n) lgkmcnt(0) (expcnt left at 7).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Word 3 of a raw (stride 0) buffer descriptor on CDNA: 32-bit data format,
+// no swizzle; reads past num_records return zero.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);

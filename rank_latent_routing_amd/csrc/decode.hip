@@ -7,162 +7,228 @@
 // A workgroup stages its head's latent side once in LDS, already in matrix-core
 // operand order: Q in bf16 (A operand of S^T = Q K^T) and Z transposed (A
 // operand of Y^T = Z^T P^T).  Each wave then streams 64-token groups of K
-// straight from HBM into registers (one 16-byte load per lane and 16-token
-// block), walks the latents 32 at a time and keeps every token's softmax
-// inside the wave: a token's 32 scores of a chunk sit in 4 lanes x 8
-// registers, the weights are packed to bf16 in place as the B operand of the
-// Z^T P^T product, and the normaliser is the dot2 sum of those packed
-// weights, reduced over the 4 lanes at the end.  No score leaves registers.
+// straight from HBM into registers (prefetching the next group while it
+// computes the current one) and walks the latents 32 at a time with
+// v_mfma_f32_32x32x16_bf16.  A lane's 16 scores of a chunk all belong to its
+// token, so every token's softmax stays in two lanes: the weights are packed
+// to bf16 in place as the B operand of Z^T P^T, the normaliser is the dot2 sum
+// of those packed weights, and the two lane halves are added at the end.  No
+// score leaves registers, and each lane writes 16 contiguous features of its
+// token.
 //
 // As in the encoder, the first pass uses weights 2^x without a maximum; a
 // 64-token group whose normaliser leaves [2^-100, 2^100] (or whose output is
 // not finite) is recomputed with the exact two-pass softmax (row maximum
-// across the lanes of the token first).  FLARE_FLAG_EXACT_SOFTMAX forces it.
+// first).  FLARE_FLAG_EXACT_SOFTMAX forces it.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace flare {
 
-// Latent row m of chunk c that lane group g, element j of a B/A operand with
-// K = 32 latents refers to (the layout the S^T output tiles produce).
-__device__ __forceinline__ int chunk_latent(int c, int g, int j) {
-  return 32 * c + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+// Latent of element j (K slot (h, j)) of 16-latent group u in 32-latent chunk
+// ch: the rows the 32x32 score tile gives lane half h.
+__device__ __forceinline__ int chunk_latent(int ch, int u, int h, int j) {
+  return 32 * ch + 16 * u + (j < 4 ? 4 * h + j : 8 + 4 * h + (j - 4));
 }
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 12;  // one workgroup per compute unit, 3 waves per SIMD
+constexpr int kDecGroup = 64;  // tokens per wave per step
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Position of 16-byte chunk dc of token t in a wave's K slot: the chunk index
+// is XOR-swizzled with bits 2..3 of the token so that the operand reads (32
+// lanes = 32 consecutive tokens, one chunk each) hit distinct bank groups.
+template <int D>
+__device__ __forceinline__ int dec_k_pos(int token, int dc) {
+  if constexpr (D == 32) return token * 4 + (dc ^ ((token >> 2) & 3));
+  else return token * 2 + (dc ^ ((token >> 2) & 1));
+}
 
 template <int D>
-__global__ __launch_bounds__(64 * kDecWaves, 4) void decode_bf16_kernel(DecodeParams p) {
-  using Op = QkOp<D>;
-  using op_t = typename Op::type;
-  constexpr int PL = Op::per_lane;
+__global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodeParams p) {
   constexpr int NW = kDecWaves;
   constexpr int NT = 64 * NW;
-  constexpr int DB = D / 16;
+  constexpr int SD = D / 16;
+  constexpr int ROWC = D / 8;                       // 16-byte chunks per token row
+  constexpr int KOPS = kDecGroup * ROWC / 64;       // wave-wide DMA loads per group
+  constexpr int KSLOT = kDecGroup * D;              // bf16 elements of a wave's K slot
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
   const int bh = blockIdx.y;
-  const int b = bh / p.H, h = bh - b * p.H;
+  const int b = bh / p.H, hd = bh - b * p.H;
   const int MC = (p.M + 31) / 32;  // 32-latent chunks
-  const int MB = 2 * MC;           // 16-latent blocks
   const bool m_ragged = p.M != 32 * MC;
-  op_t* q_lds = reinterpret_cast<op_t*>(smem);                                           // [MB][64]
-  bf16x8* z_lds = reinterpret_cast<bf16x8*>(smem + (size_t)MB * 64 * sizeof(op_t));  // [MC][DB][64]
+  bf16x8* q_lds = reinterpret_cast<bf16x8*>(smem);                                          // [MC][SD][64]
+  bf16x8* z_lds = reinterpret_cast<bf16x8*>(smem + (size_t)MC * SD * 64 * sizeof(bf16x8));  // [MC][2][64]
+  bf16* kslot = reinterpret_cast<bf16*>(smem + (size_t)MC * (SD + 2) * 64 * sizeof(bf16x8)) + wave * KSLOT;
 
-  // Stage Q: lane (g, r) of block nb holds latent 16nb + r, columns g*PL...
-  for (int u = tid; u < MB * 64; u += NT) {
-    const int nb = u >> 6, ln = u & 63, gg = ln >> 4, rr = ln & 15;
-    const int m = 16 * nb + rr;
-    float qv[PL];
+  // Stage Q: lane (h, c) of chunk ch, slice sd holds latent 32ch + c,
+  // features 16sd + 8h .. +7 in bf16; the scale multiplies the fp32 scores.
+  for (int u = tid; u < MC * SD * 64; u += NT) {
+    const int ch = u / (SD * 64), sd = (u >> 6) % SD, ln = u & 63, hh = ln >> 5, cc = ln & 31;
+    const int m = 32 * ch + cc;
+    float qv[8];
 #pragma unroll
-    for (int j = 0; j < PL; ++j) qv[j] = 0.f;
-    if (m < p.M) load_as_f32<PL>(p.q.data, p.q.is_f32, b * p.q.sb + h * p.q.sh + (int64_t)m * p.q.sl + gg * PL, qv);
-    op_t qb;
+    for (int j = 0; j < 8; ++j) qv[j] = 0.f;
+    if (m < p.M) load_as_f32<8>(p.q.data, p.q.is_f32, b * p.q.sb + hd * p.q.sh + (int64_t)m * p.q.sl + 16 * sd + 8 * hh, qv);
+    bf16x8 qb;
 #pragma unroll
-    for (int j = 0; j < PL; ++j) qb[j] = (bf16)qv[j];
-    q_lds[nb * 64 + ln] = qb;
+    for (int j = 0; j < 8; ++j) qb[j] = (bf16)qv[j];
+    q_lds[(ch * SD + sd) * 64 + ln] = qb;
   }
-  // Stage Z^T: row r of column block e is feature d = sigma(e, r), chosen so
-  // that the output tile rows 4g..4g+3 of both blocks are 8 contiguous
-  // features 8g..8g+7 (D = 32) or 4g..4g+3 (D = 16) of one token.
-  for (int u = tid; u < MC * DB * 64; u += NT) {
-    const int c = u / (DB * 64), e = (u >> 6) % DB, ln = u & 63, gg = ln >> 4, rr = ln & 15;
-    const int d = D == 32 ? 8 * (rr >> 2) + 4 * e + (rr & 3) : rr;
+  // Stage Z^T: row r (lane c = r) of the A operand is feature
+  // sigma(r) = 16((r >> 2) & 1) + 4(r >> 3) + (r & 3), chosen so that the
+  // output rows lane half h receives (8q + 4h + i%4) are the 16 contiguous
+  // features 16h .. 16h + 15 of its token; rows with sigma(r) >= D are zero.
+  for (int u = tid; u < MC * 2 * 64; u += NT) {
+    const int ch = u >> 7, ug = (u >> 6) & 1, ln = u & 63, hh = ln >> 5, r = ln & 31;
+    const int d = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
     bf16x8 val;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int m = chunk_latent(c, gg, j);
+      const int m = chunk_latent(ch, ug, hh, j);
       float zv = 0.f;
-      if (m < p.M) load_as_f32<1>(p.z.data, p.z.is_f32, b * p.z.sb + h * p.z.sh + (int64_t)m * p.z.sl + d, &zv);
+      if (m < p.M && d < D) load_as_f32<1>(p.z.data, p.z.is_f32, b * p.z.sb + hd * p.z.sh + (int64_t)m * p.z.sl + d, &zv);
       val[j] = (bf16)zv;
     }
-    z_lds[(c * DB + e) * 64 + ln] = val;
+    z_lds[(ch * 2 + ug) * 64 + ln] = val;
+  }
+  // Zero this wave's K slot: lanes past the last token may leave their chunk
+  // unwritten, and the stale data must be finite (its scores are discarded).
+  {
+    const bf16x8 z8 = {};
+    for (int u = lane; u < KSLOT / 8; u += 64) reinterpret_cast<bf16x8*>(kslot)[u] = z8;
   }
   __syncthreads();
 
   const bf16 zero = (bf16)0.0f;
   const float cs = p.c;
-  const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + h * p.k.sh;
-  const int64_t n_begin = (int64_t)blockIdx.x * p.tokens_per_block;
-  const int64_t n_end = min(p.N, n_begin + p.tokens_per_block);
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + hd * p.k.sh;
+  // Workgroup b takes the (NW x 64)-token passes b, b + G, b + 2G, ... of its
+  // head (G = gridDim.x), so the resident workgroups sweep one window of K;
+  // wave w takes tokens 64w .. 64w + 63 of each pass.
+  const int64_t n_end = p.N;
+  const int64_t pass_stride = (int64_t)gridDim.x * kDecGroup * NW;
 
-  const int MCF = p.M / 32;  // chunks with all 32 latents valid
-
-  // B operands of S^T = Q K^T: lane (g, r) holds token base + 16t + r,
-  // features g*PL ...; the next 64-token group is loaded while the current
-  // one is computed.
-  auto load_k = [&](op_t (&kk)[4], int64_t base) {
+  // K of a 64-token group comes by buffer loads straight into the wave's LDS
+  // slot (uniform descriptor, loop-invariant 32-bit lane offsets; tokens past
+  // the end fall outside the descriptor's range).  The next group's load is in
+  // flight while the current group is computed.
+  // Load t covers tokens 16t/ROWC*4 ..: its lane offset is the same for every
+  // t (the swizzle depends on token bits 2..3 only) plus a uniform part.
+  const int k_tok = lane / ROWC, k_sw = lane % ROWC;
+  const int k_dc = D == 32 ? (k_sw ^ ((k_tok >> 2) & 3)) : (k_sw ^ ((k_tok >> 2) & 1));
+  const uint32_t k_off = (uint32_t)((k_tok * p.k.sl + k_dc * 8) * (int64_t)sizeof(bf16));
+  const int k_step = (int)((64 / ROWC) * p.k.sl * (int64_t)sizeof(bf16));  // bytes per load
+  auto issue_k = [&](int64_t g0) {
+    const int64_t rows = g0 < n_end ? min((int64_t)kDecGroup, n_end - g0) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>(kbase + (g0 < n_end ? g0 : 0) * p.k.sl), (short)0,
+        (int)(rows * p.k.sl * (int64_t)sizeof(bf16)), kBufferFlags);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t n = base + 16 * t + r;
-      if (n < n_end) {
-        kk[t] = *reinterpret_cast<const op_t*>(kbase + n * p.k.sl + g * PL);
-      } else {
-#pragma unroll
-        for (int j = 0; j < PL; ++j) kk[t][j] = zero;
-      }
-    }
+    for (int t = 0; t < KOPS; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(kslot + t * 512), 16, k_off, t * k_step, 0, 0);
   };
-  op_t kb[4], kn[4];
-  load_k(kb, n_begin + 64 * wave);
-  // Wait for the first group here, outside the loop: vmcnt counts loads and
-  // stores in order, and without this the compiler waits for everything
-  // (the next group's prefetch included) at the head of the latent loop.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
 
-  for (int64_t base = n_begin + 64 * wave; base < n_end; base += 64 * NW) {
-    load_k(kn, base + 64 * NW);
+  int64_t base = (int64_t)blockIdx.x * kDecGroup * NW + kDecGroup * wave;
+  if (base < n_end) issue_k(base);
+  for (; base < n_end; base += pass_stride) {
+    // B operands of S^T = Q K^T: lane (h, c) holds token base + 32tb + c,
+    // features 16sd + 8h .. +7.
+    bf16x8 kb[2][SD];
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int sd = 0; sd < SD; ++sd)
+        kb[tb][sd] = *reinterpret_cast<const bf16x8*>(kslot + 8 * dec_k_pos<D>(32 * tb + c, 2 * sd + h));
+    // the slot is read before the next group's load may overwrite it
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    if (base + pass_stride < n_end) issue_k(base + pass_stride);
 
-    f32x4 yacc[4][DB];
-    float lsum[4], mx[4];
-    // One 32-latent chunk against the 64 tokens.  MASK (only the last chunk
-    // when M is not a multiple of 32) gives padded latents weight 0.
-    auto chunk = [&](auto exact_tag, auto mask_tag, int c) {
+    f32x16 yacc[2];
+    float lsum[2], mx[2];
+    // S^T of 32-latent chunk ch against token block tb (32 tokens) with the
+    // chunk's Q operands qa.  Element i of a score tile is latent
+    // 32ch + 8(i/4) + 4h + i%4 of token c.
+    auto load_q = [&](bf16x8 (&qa)[SD], int ch) {
+#pragma unroll
+      for (int sd = 0; sd < SD; ++sd) qa[sd] = q_lds[(ch * SD + sd) * 64 + lane];
+    };
+    auto qk = [&](const bf16x8 (&qa)[SD], int tb) {
+      f32x16 sc = zero16();
+#pragma unroll
+      for (int sd = 0; sd < SD; ++sd) sc = mfma_32x32x16(qa[sd], kb[tb][sd], sc);
+      return sc;
+    };
+    // Weights of one score tile, their row sums (two independent
+    // accumulators) and Y^T += Z^T P^T.  MASK (only the last chunk when M is
+    // not a multiple of 32) gives padded latents weight 0.
+    auto softmax_pv = [&](auto exact_tag, auto mask_tag, f32x16 sc, int ch, int tb, float (&ls)[2][2]) {
       constexpr bool EXACT = decltype(exact_tag)::value;
       constexpr bool MASK = decltype(mask_tag)::value;
-      const op_t q0 = q_lds[(2 * c) * 64 + lane];
-      const op_t q1 = q_lds[(2 * c + 1) * 64 + lane];
-      bf16x8 za[DB];
+      const bf16x8 za0 = z_lds[(ch * 2 + 0) * 64 + lane];
+      const bf16x8 za1 = z_lds[(ch * 2 + 1) * 64 + lane];
+      // latent 32ch + 8(i/4) + 4h + i%4 is valid iff 8(i/4) + i%4 < rel
+      const int rel = p.M - 32 * ch - 4 * h;
 #pragma unroll
-      for (int e = 0; e < DB; ++e) za[e] = z_lds[(c * DB + e) * 64 + lane];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4 s0 = Op::mma(q0, kb[t], f32x4{0.f, 0.f, 0.f, 0.f});
-        f32x4 s1 = Op::mma(q1, kb[t], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (EXACT) {
-            s0[i] = exp2_fast(s0[i] * cs - mx[t]);
-            s1[i] = exp2_fast(s1[i] * cs - mx[t]);
-          } else {
-            s0[i] = exp2_fast(s0[i] * cs);
-            s1[i] = exp2_fast(s1[i] * cs);
-          }
-          if constexpr (MASK) {
-            if (32 * c + 4 * g + i >= p.M) s0[i] = 0.f;
-            if (32 * c + 16 + 4 * g + i >= p.M) s1[i] = 0.f;
-          }
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (EXACT)
+          sc[i] = exp2_fast(sc[i] * cs - mx[tb]);
+        else
+          sc[i] = exp2_fast(sc[i] * cs);
+        if constexpr (MASK) {
+          if (8 * (i >> 2) + (i & 3) >= rel) sc[i] = 0.f;
         }
-        const bf16x8 pb = pack8(s0, s1);
-        lsum[t] = rowsum_bf16x8(pb, lsum[t]);
+      }
 #pragma unroll
-        for (int e = 0; e < DB; ++e) yacc[t][e] = mfma_16x16x32(za[e], pb, yacc[t][e]);
+      for (int ug = 0; ug < 2; ++ug) {
+        const bf16x8 pb = pack8_16(sc, ug);
+        const u32x4 w = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ls[tb][j & 1] = dot2_ones(w[j], ls[tb][j & 1]);
+        yacc[tb] = mfma_32x32x16(ug == 0 ? za0 : za1, pb, yacc[tb]);
       }
     };
+    // All chunks, software-pipelined over the units (chunk, token block):
+    // the S^T product of the next unit is issued before the softmax of the
+    // current one, so the matrix cores run under the exponentials.  The last
+    // chunk is peeled off (it carries the padding mask when M is not a
+    // multiple of 32).
     auto pass = [&](auto exact_tag) {
+      float ls[2][2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int e = 0; e < DB; ++e) yacc[t][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-        lsum[t] = 0.f;
+      for (int tb = 0; tb < 2; ++tb) {
+        yacc[tb] = zero16();
+        ls[tb][0] = ls[tb][1] = 0.f;
       }
-      for (int c = 0; c < MCF; ++c) chunk(exact_tag, std::integral_constant<bool, false>(), c);
-      if (m_ragged) chunk(exact_tag, std::integral_constant<bool, true>(), MC - 1);
+      bf16x8 qa[SD];
+      load_q(qa, 0);
+      f32x16 s0 = qk(qa, 0);
+      for (int ch = 0; ch + 1 < MC; ++ch) {
+        load_q(qa, ch);
+        const f32x16 s1 = qk(qa, 1);
+        softmax_pv(exact_tag, std::integral_constant<bool, false>(), s0, ch, 0, ls);
+        load_q(qa, ch + 1);
+        s0 = qk(qa, 0);
+        softmax_pv(exact_tag, std::integral_constant<bool, false>(), s1, ch, 1, ls);
+      }
+      load_q(qa, MC - 1);
+      const f32x16 s1 = qk(qa, 1);
+      if (m_ragged) {
+        softmax_pv(exact_tag, std::integral_constant<bool, true>(), s0, MC - 1, 0, ls);
+        softmax_pv(exact_tag, std::integral_constant<bool, true>(), s1, MC - 1, 1, ls);
+      } else {
+        softmax_pv(exact_tag, std::integral_constant<bool, false>(), s0, MC - 1, 0, ls);
+        softmax_pv(exact_tag, std::integral_constant<bool, false>(), s1, MC - 1, 1, ls);
+      }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        lsum[t] += shfl_xor_f(lsum[t], 16);
-        lsum[t] += shfl_xor_f(lsum[t], 32);
+      for (int tb = 0; tb < 2; ++tb) {
+        lsum[tb] = ls[tb][0] + ls[tb][1];
+        lsum[tb] += shfl_xor_f(lsum[tb], 32);
       }
     };
 
@@ -171,74 +237,58 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void decode_bf16_kernel(DecodePa
       pass(std::integral_constant<bool, false>());
       bool bad = false;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float l = lsum[t];
-        bool ok = l >= kSafeLo && l <= kSafeHi;
+      for (int tb = 0; tb < 2; ++tb) {
+        bool ok = lsum[tb] >= kSafeLo && lsum[tb] <= kSafeHi;
 #pragma unroll
-        for (int e = 0; e < DB; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ok = ok && __builtin_isfinite(yacc[t][e][i]);
-        bad = bad || (base + 16 * t + r < n_end && !ok);
+        for (int i = 0; i < 16; ++i) ok = ok && __builtin_isfinite(yacc[tb][i]);
+        bad = bad || (base + 32 * tb + c < n_end && !ok);
       }
       exact = __any(bad);
     }
     if (exact) {
       // Row maximum of every token over all valid latents.
 #pragma unroll
-      for (int t = 0; t < 4; ++t) mx[t] = -INFINITY;
-      for (int nb = 0; nb < MB; ++nb) {
-        const op_t qb = q_lds[nb * 64 + lane];
+      for (int tb = 0; tb < 2; ++tb) mx[tb] = -INFINITY;
+      for (int ch = 0; ch < MC; ++ch) {
+        bf16x8 qa[SD];
+        load_q(qa, ch);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const f32x4 sc = Op::mma(qb, kb[t], f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int tb = 0; tb < 2; ++tb) {
+          const f32x16 sc = qk(qa, tb);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * nb + 4 * g + i < p.M) mx[t] = fmaxf(mx[t], sc[i] * cs);
+          for (int i = 0; i < 16; ++i)
+            if (32 * ch + 8 * (i >> 2) + 4 * h + (i & 3) < p.M) mx[tb] = fmaxf(mx[tb], sc[i] * cs);
         }
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        mx[t] = fmaxf(mx[t], shfl_xor_f(mx[t], 16));
-        mx[t] = fmaxf(mx[t], shfl_xor_f(mx[t], 32));
-      }
+      for (int tb = 0; tb < 2; ++tb) mx[tb] = fmaxf(mx[tb], shfl_xor_f(mx[tb], 32));
       pass(std::integral_constant<bool, true>());
     }
 
-    // Output: lane (g, r) holds token base + 16t + r, features 8g..8g+7
-    // (D = 32: rows 4g..4g+3 of block 0 then of block 1) or 4g..4g+3 (D = 16).
+    // Output: lane (h, c) holds token base + 32tb + c, features 16h .. 16h+15.
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t n = base + 16 * t + r;
-      if (n >= n_end) continue;
-      const float inv = 1.0f / lsum[t];
-      float out[4 * DB];
-#pragma unroll
-      for (int e = 0; e < DB; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[4 * e + i] = yacc[t][e][i] * inv;
-      const int64_t off = b * p.y_sb + h * p.y_sh + n * p.y_sl + g * 4 * DB;
+    for (int tb = 0; tb < 2; ++tb) {
+      const int64_t n = base + 32 * tb + c;
+      if (n >= n_end || 16 * h >= D) continue;
+      const float inv = 1.0f / lsum[tb];
+      const int64_t off = b * p.y_sb + hd * p.y_sh + n * p.y_sl + 16 * h;
       if (p.y_f32) {
         float* yp = reinterpret_cast<float*>(p.y) + off;
 #pragma unroll
-        for (int j = 0; j < 4 * DB; j += 4)
-          *reinterpret_cast<f32x4*>(yp + j) = f32x4{out[j], out[j + 1], out[j + 2], out[j + 3]};
+        for (int j = 0; j < 16; j += 4)
+          *reinterpret_cast<f32x4*>(yp + j) =
+              f32x4{yacc[tb][j] * inv, yacc[tb][j + 1] * inv, yacc[tb][j + 2] * inv, yacc[tb][j + 3] * inv};
       } else {
         bf16* yp = reinterpret_cast<bf16*>(p.y) + off;
-        if constexpr (DB == 2) {
+#pragma unroll
+        for (int j = 0; j < 16; j += 8) {
           bf16x8 v;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = (bf16)out[j];
-          *reinterpret_cast<bf16x8*>(yp) = v;
-        } else {
-          bf16x4 v;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = (bf16)out[j];
-          *reinterpret_cast<bf16x4*>(yp) = v;
+          for (int k = 0; k < 8; ++k) v[k] = (bf16)(yacc[tb][j + k] * inv);
+          *reinterpret_cast<bf16x8*>(yp + j) = v;
         }
       }
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) kb[t] = kn[t];
   }
 }
 
@@ -303,8 +353,25 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
 
 size_t decode_bf16_lds(int M, int D) {
   const int MC = (M + 31) / 32;
-  const size_t op_bytes = D == 32 ? 16 : 8;
-  return (size_t)2 * MC * 64 * op_bytes + (size_t)MC * (D / 16) * 64 * 16;
+  return (size_t)MC * (D / 16) * 64 * 16 + (size_t)MC * 2 * 64 * 16 +
+         (size_t)kDecWaves * kDecGroup * D * sizeof(bf16);
+}
+
+// A persistent grid: as many workgroups as fit on the 256 compute units at
+// once (LDS and the 3-waves-per-SIMD register budget decide), spread evenly
+// over the heads; each takes every G-th pass of its head.
+int64_t plan_decode_bf16(int B, int H, int M, int64_t N, int D) {
+  const int64_t lds = (int64_t)decode_bf16_lds(M, D);
+  int64_t per_cu = (160 * 1024) / lds;
+  if (per_cu > 12 / kDecWaves) per_cu = 12 / kDecWaves;
+  if (per_cu < 1) per_cu = 1;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t pass = (int64_t)kDecWaves * kDecGroup;
+  const int64_t passes = (N + pass - 1) / pass;
+  int64_t per_bh = (256 * per_cu + bh - 1) / bh;
+  if (per_bh > passes) per_bh = passes;
+  if (per_bh < 1) per_bh = 1;
+  return per_bh;
 }
 
 // Kernels that stage more than 64 KB of LDS must opt in to the larger limit.
@@ -315,7 +382,7 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
 }
 
 hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t st) {
-  const int64_t blocks = (p.N + p.tokens_per_block - 1) / p.tokens_per_block;
+  const int64_t blocks = p.tokens_per_block;  // workgroups per head
   dim3 grid((unsigned)blocks, B * p.H);
   const size_t lds = decode_bf16_lds(p.M, D);
   hipError_t e;

@@ -6,21 +6,26 @@
 // synthesis (equation 8) is the same call with learned seeds as Q.
 //
 // The N tokens of each (batch, head) are cut into S contiguous splits.  One
-// workgroup owns one split and all latents of its head (64 per wave): it
-// streams 64-token K/V tiles from HBM into LDS (double buffered, one barrier
-// per tile) and every wave multiplies them against its latents on bf16
-// matrix cores, 32 tokens at a time.  Per split it writes the normalised
-// partial output and the split's log-normaliser; the merge kernel combines
-// the splits exactly by logsumexp, the reduction the pages give for
+// workgroup owns one split and all latents of its head, 32 per wave: it
+// streams 128-token K/V tiles from HBM straight into LDS with
+// global_load_lds_dwordx4 (three LDS stages, two tiles in flight, one barrier
+// per tile, no registers or vector instructions spent on staging) and every
+// wave multiplies them against its latents on bf16 matrix cores, 32 tokens at
+// a time.  V stays token-major in LDS; the transposed B operand of P V comes
+// from ds_read_b64_tr_b16.  Per split it writes the
+// normalised partial output and the split's log-normaliser; the merge kernel
+// combines the splits exactly by logsumexp, the reduction the pages give for
 // token-sharded encoders ("Multi-GPU context parallelism").
 //
-// On gfx950 matrix-core and vector work largely add up rather than overlap,
-// so the per-score instruction count is what the design minimises:
-//   scores   s = K Q^T on v_mfma_f32_16x16x32_bf16 (bf16 Q, fp32 accumulate),
-//   weights  p = exp2(s * scale*log2 e): one v_mul, one v_exp_f32,
-//   packing  two weights per v_cvt_pk_bf16_f32 (the A operand of P V),
-//   row sums v_dot2c_f32_bf16 of the packed weights against (1, 1), i.e. the
-//            normaliser sums exactly the rounded weights the numerator uses.
+// Per 32 tokens x 32 latents a wave runs four v_mfma_f32_32x32x16_bf16 (two
+// for S^T = K Q^T, two for O += P V).  A lane's 16 scores all belong to its
+// latent, so the softmax stays in the lane: one v_mul by scale*log2(e), one
+// v_exp_f32, a v_cvt_pk_bf16_f32 per pair (which is directly the A operand of
+// P V), and v_dot2c_f32_bf16 row sums of those packed weights (the
+// normaliser sums exactly the rounded weights the numerator uses).  On gfx950
+// matrix-core and vector work largely add up rather than overlap, so this
+// per-score instruction count is what the design minimises.
+//
 // The first pass runs without a running maximum (weights relative to 2^0);
 // a split is accepted when every latent's normaliser lies in [2^-100, 2^100]
 // and its output is finite, which rules out overflow and underflow, and the
@@ -33,343 +38,362 @@
 namespace flare {
 
 constexpr int kEncT = 128;  // tokens per LDS tile (four 32-token quarters)
+constexpr int kStages = 4;   // LDS tiles: one computed, three in flight
 
-template <int D, int NW, int NB_>
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+template <int D, int NW>
 struct EncodeKernel {
-  using Op = QkOp<D>;
-  using op_t = typename Op::type;
-  static constexpr int PL = Op::per_lane;
   static constexpr int NT = 64 * NW;
-  static constexpr int KROW = D + 8;  // padded LDS row: conflict-free operand reads
-  static constexpr int DB = D / 16;   // 16-wide column blocks of D
-  static constexpr int NB = NB_;      // 16-latent blocks per wave
-  static constexpr int NQ = kEncT / 32;                  // 32-token quarters per tile
-  static constexpr int K_UNITS = kEncT * D / 8;          // 16-byte chunks of a K tile
-  static constexpr int V_UNITS = (kEncT / 4) * (D / 2);  // (token quad, d pair) of a V tile
-  static constexpr int K_PER = (K_UNITS + NT - 1) / NT;
-  static constexpr int V_PER = (V_UNITS + NT - 1) / NT;
-  static constexpr int K_ELEMS = kEncT * KROW;
-  static constexpr int V_ELEMS = NQ * DB * 64 * 8;
+  static constexpr int SD = D / 16;                 // 16-wide d slices (K dim of S^T)
+  static constexpr int NQ = kEncT / 32;             // 32-token quarters per tile
+  static constexpr int ROWC = D / 8;                // 16-byte chunks per token row
+  static constexpr int TILE_ELEMS = kEncT * D;      // bf16 elements of one K (or V) tile
+  static constexpr int TILE_CHUNKS = kEncT * ROWC;  // 16-byte chunks of one tile
+  // Each tile is brought in by TILE_CHUNKS / 64 wave-wide 16-byte DMA loads
+  // for K and as many for V, spread evenly over the waves.
+  static constexpr int OPS = 2 * TILE_CHUNKS / 64;
+  static constexpr int OPS_PER_WAVE = (OPS + NW - 1) / NW;
+  static_assert(OPS % NW == 0 || NW > OPS, "uneven DMA split");
 };
 
-// V staging unit u -> (token quad q4 of the tile, column pair dp, which of the
-// pair's two rows is written first).  The destination bank of a V write
-// depends only on (column r = d % 16, half = which 4 of the lane's 8 tokens),
-// so the mapping spreads every wave's 64 lanes over all 32 (r, half) slots,
-// twice: a 2-way access, the minimum for 512 bytes.
+// K tile chunk position of (token, 16-byte chunk dc): the chunk index is
+// XOR-swizzled with bits 2..3 of the token so that the A-operand reads
+// (lanes of a 16-lane group = 16 consecutive tokens, one chunk each) touch
+// 16 distinct bank groups.
 template <int D>
-__device__ __forceinline__ void v_unit(int u, int& q4, int& dp, int& par) {
-  if constexpr (D == 32) {
-    dp = u & 15;
-    const int j = (u >> 4) & 3, w = u >> 6;
-    const int half = j & 1, c = ((w >> 2) << 1) | (j >> 1), gg = w & 3;
-    q4 = c * 8 + half * 4 + gg;
-    par = dp >> 3;
-  } else {
-    dp = u & 7;
-    const int b3 = (u >> 3) & 1, half = (u >> 4) & 1, b5 = (u >> 5) & 1, c = u >> 6;
-    const int gg = b3 | (b5 << 1);
-    q4 = c * 8 + half * 4 + gg;
-    par = b3;
-  }
+__device__ __forceinline__ int k_chunk_pos(int token, int dc) {
+  if constexpr (D == 32) return token * 4 + (dc ^ ((token >> 2) & 3));
+  else return token * 2 + (dc ^ ((token >> 2) & 1));
 }
 
-template <int D, int NW, int NB_, bool EXACT>
+template <int D, int NW, bool EXACT>
 __device__ __forceinline__ void encode_pass(
     const EncodeParams& p, const bf16* __restrict__ kbase, const bf16* __restrict__ vbase,
-    int64_t n_begin, int64_t n_end, int ntiles, bf16* k_lds, bf16* v_lds,
-    const typename QkOp<D>::type (&qop)[NB_], f32x4 (&o)[NB_][D / 16], float (&lsum)[NB_],
-    float (&mrun)[NB_]) {
-  using KC = EncodeKernel<D, NW, NB_>;
-  using op_t = typename KC::op_t;
-  constexpr int PL = KC::PL, NT = KC::NT, KROW = KC::KROW, DB = KC::DB, NB = KC::NB, NQ = KC::NQ;
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+    int64_t tile0, int64_t tstride, int64_t n_end, int ntiles, bf16* k0, bf16* k1, bf16* k2, bf16* k3,
+    bf16* v0, bf16* v1, bf16* v2, bf16* v3, const bf16x8 (&qop)[D / 16], f32x16& o,
+    float (&ls)[4], float& mrun) {
+  using KC = EncodeKernel<D, NW>;
+  constexpr int SD = KC::SD, NQ = KC::NQ, ROWC = KC::ROWC;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
+  const int i16 = lane & 15;
   const float cs = p.c;
+  const bf16 zero = (bf16)0.0f;
 
+  o = zero16();
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+  for (int a = 0; a < 4; ++a) ls[a] = 0.f;
+  mrun = -INFINITY;
+
+  // DMA of tile it into stage S: wave-wide 16-byte buffer loads straight
+  // into LDS, lane l of load t filling chunk (t * 64 + l) of the stage.  K
+  // chunks are swizzled; V chunks stay in token-major order.  Which load a
+  // wave issues, and so its source tensor, is uniform across the wave: the
+  // buffer descriptor (tile base, valid byte range) lives in scalar registers
+  // and each lane adds a loop-invariant 32-bit offset.  In the ragged last
+  // tile, lanes past the end fall outside the descriptor's range and read
+  // zeros (finite data whose weight is then set to 0).
+  uint32_t op_off[KC::OPS_PER_WAVE];
 #pragma unroll
-    for (int e = 0; e < DB; ++e) o[nb][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    lsum[nb] = 0.f;
-    mrun[nb] = -INFINITY;
+  for (int q = 0; q < KC::OPS_PER_WAVE; ++q) {
+    const int op = wave * KC::OPS_PER_WAVE + q;
+    const bool is_v = op >= KC::OPS / 2;
+    const int t = is_v ? op - KC::OPS / 2 : op;
+    const int pos = t * 64 + lane;
+    const int token = pos / ROWC, sw = pos % ROWC;
+    const int dc = is_v ? sw : D == 32 ? (sw ^ ((token >> 2) & 3)) : (sw ^ ((token >> 2) & 1));
+    op_off[q] = (uint32_t)((token * (is_v ? p.v.sl : p.k.sl) + dc * 8) * (int64_t)sizeof(bf16));
   }
-
-  struct Stage {
-    u32x4 k[KC::K_PER];
-    uint32_t v[KC::V_PER][4];
-  };
-  Stage sa, sb;
-
-  auto load_tile = [&](Stage& st, int it) {
-    u32x4 (&kreg)[KC::K_PER] = st.k;
-    uint32_t (&vreg)[KC::V_PER][4] = st.v;
-    const int64_t t0 = n_begin + (int64_t)it * kEncT;
+  auto issue = [&](auto stage_tag, int it) {
+    constexpr int S = decltype(stage_tag)::value;
+    bf16* kd = S == 0 ? k0 : S == 1 ? k1 : S == 2 ? k2 : k3;
+    bf16* vd = S == 0 ? v0 : S == 1 ? v1 : S == 2 ? v2 : v3;
+    const int64_t t0 = (tile0 + (int64_t)it * tstride) * kEncT;
+    const int64_t rows = min((int64_t)kEncT, n_end - t0);
 #pragma unroll
-    for (int ui = 0; ui < KC::K_PER; ++ui) {
-      const int u = tid + ui * NT;
-      kreg[ui] = u32x4{0u, 0u, 0u, 0u};
-      if (u < KC::K_UNITS) {
-        const int n = u / (D / 8), dc = u % (D / 8);
-        const int64_t tok = t0 + n;
-        if (tok < n_end) kreg[ui] = *reinterpret_cast<const u32x4*>(kbase + tok * p.k.sl + dc * 8);
-      }
-    }
-#pragma unroll
-    for (int ui = 0; ui < KC::V_PER; ++ui) {
-      const int u = tid + ui * NT;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[ui][i] = 0u;
-      if (u < KC::V_UNITS) {
-        int q4, dp, par;
-        v_unit<D>(u, q4, dp, par);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t tok = t0 + 4 * q4 + i;
-          if (tok < n_end) vreg[ui][i] = *reinterpret_cast<const uint32_t*>(vbase + tok * p.v.sl + 2 * dp);
-        }
+    for (int q = 0; q < KC::OPS_PER_WAVE; ++q) {
+      const int op = wave * KC::OPS_PER_WAVE + q;
+      if (op < KC::OPS) {
+        const bool is_v = op >= KC::OPS / 2;
+        const int t = is_v ? op - KC::OPS / 2 : op;
+        const int64_t sl = is_v ? p.v.sl : p.k.sl;
+        const bf16* base = (is_v ? vbase : kbase) + t0 * sl;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16*>(base), (short)0, (int)(rows * sl * (int64_t)sizeof(bf16)), kBufferFlags);
+        bf16* dst = (is_v ? vd : kd) + t * 512;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, op_off[q], 0, 0, 0);
       }
     }
   };
 
-  // K tile: plain rows [token][d] (padded).  V tile: the B operand of the
-  // P V product, transposed so that lane (g, r) of quarter c and column block
-  // e finds its 8 tokens contiguous: j < 4 -> token 32c + 4g + j,
-  // j >= 4 -> token 32c + 16 + 4g + (j - 4), column d = 16e + r.
-  auto store_tile = [&](const Stage& st, int buf) {
-    const u32x4 (&kreg)[KC::K_PER] = st.k;
-    const uint32_t (&vreg)[KC::V_PER][4] = st.v;
-    bf16* kt = k_lds + buf * KC::K_ELEMS;
-    bf16* vt = v_lds + buf * KC::V_ELEMS;
+  // S^T for quarter qt (32 tokens) of a tile against the wave's 32 latents:
+  // the K operands (LDS reads) and the two products.  Element i of the score
+  // tile is token 32qt + 8(i/4) + 4h + i%4 of latent c.
+  auto k_operands = [&](const bf16* kt, int qt, bf16x8 (&ka)[SD]) {
 #pragma unroll
-    for (int ui = 0; ui < KC::K_PER; ++ui) {
-      const int u = tid + ui * NT;
-      if (u < KC::K_UNITS) {
-        const int n = u / (D / 8), dc = u % (D / 8);
-        *reinterpret_cast<u32x4*>(kt + n * KROW + dc * 8) = kreg[ui];
-      }
-    }
+    for (int sd = 0; sd < SD; ++sd)
+      ka[sd] = *reinterpret_cast<const bf16x8*>(kt + 8 * k_chunk_pos<D>(32 * qt + c, 2 * sd + h));
+  };
+  auto qk = [&](const bf16x8 (&ka)[SD]) {
+    f32x16 sc = zero16();
 #pragma unroll
-    for (int ui = 0; ui < KC::V_PER; ++ui) {
-      const int u = tid + ui * NT;
-      if (u < KC::V_UNITS) {
-        int q4, dp, par;
-        v_unit<D>(u, q4, dp, par);
-        const uint32_t* w = vreg[ui];
-        // the four tokens' even-d halves, and their odd-d halves, paired
-        const u32x2 even = {__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
-                            __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)};
-        const u32x2 odd = {__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
-                           __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)};
-        const int c = q4 >> 3, qq = q4 & 7, gg = qq & 3, half = qq >> 2;
-        const int d0 = 2 * dp, e0 = d0 >> 4, rr0 = d0 & 15;
-        const int off0 = ((c * DB + e0) * 64 + 16 * gg + rr0) * 8 + half * 4;
-        if (par) {
-          *reinterpret_cast<u32x2*>(vt + off0 + 8) = odd;
-          *reinterpret_cast<u32x2*>(vt + off0) = even;
-        } else {
-          *reinterpret_cast<u32x2*>(vt + off0) = even;
-          *reinterpret_cast<u32x2*>(vt + off0 + 8) = odd;
-        }
-      }
-    }
+    for (int sd = 0; sd < SD; ++sd) sc = mfma_32x32x16(ka[sd], qop[sd], sc);
+    return sc;
   };
 
-  // 32 tokens (quarter c of the tile) against the wave's 64 latents.  The
-  // RAGGED variant (only the last tile of a split) gives the tokens past the
-  // end weight 0.
-  auto compute_quarter = [&](auto ragged_tag, const bf16* kt, const bf16* vt, int64_t t0, int c) {
+  // B operand V[token slot (h, j)][d = c] of the 16-token group ug of quarter
+  // qt by two transposing reads: lane i of a 16-lane group points at row
+  // 16ug + 8(j0/4) + 4h + i/4, features 16(c/16) + 4(i%4) .. +3, and receives
+  // rows +0..+3 of feature c.
+  auto v_operand = [&](const bf16* vt, int qt, int ug) {
+    // With D = 16 the columns c >= 16 of the product are padding: those lanes
+    // read the same (valid) addresses as lane c - 16 and zero the operand,
+    // without a divergent branch.
+    bf16x8 vb;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 32 * qt + 16 * ug + 8 * half + 4 * h + (i16 >> 2);
+      const int col = (D == 32 ? 16 * (c >> 4) : 0) + 4 * (i16 & 3);
+      const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)((lds_void_t*)(vt + row * D + col)));
+      const bf16x4 b4 = __builtin_bit_cast(bf16x4, v4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vb[4 * half + j] = b4[j];
+    }
+    if constexpr (D == 16) {
+      const u32x4 bits = __builtin_bit_cast(u32x4, vb);
+      const uint32_t keep = c < 16 ? 0xffffffffu : 0u;
+      vb = __builtin_bit_cast(bf16x8, u32x4{bits[0] & keep, bits[1] & keep, bits[2] & keep, bits[3] & keep});
+    }
+    return vb;
+  };
+
+  // Weights of the scores sc of quarter qt, their row sums, and O += P V
+  // with the V operands vb0, vb1.  The row sums go to four independent
+  // accumulators (no serial chain of dependent dot products).  rem: tokens
+  // of the tile before the end (only read for the ragged tile).
+  auto softmax_pv = [&](auto ragged_tag, f32x16 sc, bf16x8 vb0, bf16x8 vb1, int rem, int qt) {
     constexpr bool RAGGED = decltype(ragged_tag)::value;
-    // S^T tiles: lane (g, r) of (tt, nb) holds token 32c + 16tt + 4g + i
-    // against latent 16nb + r (raw dot products).
-    f32x4 s[2][NB];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const op_t ka = *reinterpret_cast<const op_t*>(kt + (32 * c + 16 * tt + r) * KROW + g * PL);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) s[tt][nb] = KC::Op::mma(ka, qop[nb], f32x4{0.f, 0.f, 0.f, 0.f});
-    }
+    // token 32qt + 8(i/4) + 4h + i%4 is valid iff 8(i/4) + i%4 < rel
+    const int rel = rem - 32 * qt - 4 * h;
     if constexpr (EXACT) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool valid = !RAGGED || t0 + 32 * c + 16 * tt + 4 * g + i < n_end;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) s[tt][nb][i] = valid ? s[tt][nb][i] * cs : -INFINITY;
-        }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float mx = fmaxf(fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3])),
-                         fmaxf(fmaxf(s[1][nb][0], s[1][nb][1]), fmaxf(s[1][nb][2], s[1][nb][3])));
-        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-        const float mnew = fmaxf(mrun[nb], mx);
-        const float mref = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2_fast(mrun[nb] - mref);
-        mrun[nb] = mnew;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[tt][nb][i] = exp2_fast(s[tt][nb][i] - mref);
-        lsum[nb] *= alpha;
-        // accumulator row 4g + i is latent 16nb + 4g + i, whose factor sits in
-        // lane r = 4g + i
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float ai = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-          for (int e = 0; e < DB; ++e) o[nb][e][i] *= ai;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const bool valid = !RAGGED || 8 * (i >> 2) + (i & 3) < rel;
+        sc[i] = valid ? sc[i] * cs : -INFINITY;
       }
+      float mx = sc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float mnew = fmaxf(mrun, mx);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2_fast(mrun - mref);
+      mrun = mnew;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = exp2_fast(sc[i] - mref);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) ls[a] *= alpha;
+      // accumulator row i is latent 8(i/4) + 4h + i%4, whose factor sits in
+      // the lanes of that latent
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] *= __shfl(alpha, 8 * (i >> 2) + 4 * h + (i & 3), 64);
     } else {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[tt][nb][i] = exp2_fast(s[tt][nb][i] * cs);
+      for (int i = 0; i < 16; ++i) sc[i] = exp2_fast(sc[i] * cs);
       if constexpr (RAGGED) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool valid = t0 + 32 * c + 16 * tt + 4 * g + i < n_end;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) s[tt][nb][i] = valid ? s[tt][nb][i] : 0.f;
-          }
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) >= rel) sc[i] = 0.f;
       }
     }
-    bf16x8 vb[DB];
 #pragma unroll
-    for (int e = 0; e < DB; ++e) vb[e] = *reinterpret_cast<const bf16x8*>(vt + ((c * DB + e) * 64 + lane) * 8);
+    for (int ug = 0; ug < 2; ++ug) {
+      const bf16x8 pa = pack8_16(sc, ug);
+      const u32x4 w = __builtin_bit_cast(u32x4, pa);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8 pa = pack8(s[0][nb], s[1][nb]);
-      lsum[nb] = rowsum_bf16x8(pa, lsum[nb]);
-#pragma unroll
-      for (int e = 0; e < DB; ++e) o[nb][e] = mfma_16x16x32(pa, vb[e], o[nb][e]);
+      for (int a = 0; a < 4; ++a) ls[a] = dot2_ones(w[a], ls[a]);
+      o = mfma_32x32x16(pa, ug == 0 ? vb0 : vb1, o);
     }
   };
 
-  auto compute_tile = [&](int it) {
-    const int buf = it & 1;
-    const bf16* kt = k_lds + buf * KC::K_ELEMS;
-    const bf16* vt = v_lds + buf * KC::V_ELEMS;
-    const int64_t t0 = n_begin + (int64_t)it * kEncT;
-    if (t0 + kEncT <= n_end) {
+  // One tile.  On the fast path its quarters are software-pipelined: the
+  // S^T product of quarter qt + 1 is issued before the softmax of quarter
+  // qt, so the matrix cores work while the same wave computes exponentials.
+  // The exact fallback keeps one quarter in flight (fewer live registers).
+  auto compute_tile = [&](auto stage_tag, int it) {
+    constexpr int S = decltype(stage_tag)::value;
+    const bf16* kt = S == 0 ? k0 : S == 1 ? k1 : S == 2 ? k2 : k3;
+    const bf16* vt = S == 0 ? v0 : S == 1 ? v1 : S == 2 ? v2 : v3;
+    const int64_t t0 = (tile0 + (int64_t)it * tstride) * kEncT;
+    const int rem = (int)min((int64_t)kEncT, n_end - t0);
+    auto run = [&](auto ragged_tag) {
+      if constexpr (EXACT) {
 #pragma unroll 1
-      for (int c = 0; c < NQ; ++c) compute_quarter(std::integral_constant<bool, false>(), kt, vt, t0, c);
-    } else {
-#pragma unroll 1
-      for (int c = 0; c < NQ; ++c) compute_quarter(std::integral_constant<bool, true>(), kt, vt, t0, c);
-    }
+        for (int qt = 0; qt < NQ; ++qt) {
+          bf16x8 ka[SD];
+          k_operands(kt, qt, ka);
+          softmax_pv(ragged_tag, qk(ka), v_operand(vt, qt, 0), v_operand(vt, qt, 1), rem, qt);
+        }
+      } else {
+        bf16x8 ka[SD];
+        k_operands(kt, 0, ka);
+        f32x16 sc = qk(ka);
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) {
+          f32x16 nx;
+          if (qt + 1 < NQ) {
+            k_operands(kt, qt + 1, ka);
+            nx = qk(ka);
+          }
+          softmax_pv(ragged_tag, sc, v_operand(vt, qt, 0), v_operand(vt, qt, 1), rem, qt);
+          if (qt + 1 < NQ) sc = nx;
+        }
+      }
+    };
+    if (rem == kEncT)
+      run(std::integral_constant<bool, false>());
+    else
+      run(std::integral_constant<bool, true>());
   };
 
-  // Two-deep prefetch: while tile it is computed from LDS buffer it % 2, the
-  // loads of tile it + 2 are in flight into one register set and tile it + 1
-  // (loaded one tile earlier) is written from the other set into the free
-  // buffer.  The loop is unrolled by two so both register sets are static.
-  load_tile(sa, 0);
-  if (ntiles > 1) load_tile(sb, 1);
-  store_tile(sa, 0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; it += 2) {
-    // even tile: compute it, stream it + 2 into sa, write it + 1 from sb
-    if (it + 2 < ntiles) load_tile(sa, it + 2);
-    compute_tile(it);
-    if (it + 1 < ntiles) store_tile(sb, 1);
-    __syncthreads();
+  // Tile it lives in stage it % 4.  Step it: start the DMA of tile it + 3,
+  // compute tile it, then wait for this wave's DMA of tile it + 1 (the loads
+  // of tiles it + 2 and it + 3 may still be outstanding) and meet at the
+  // barrier, after which every wave's part of tile it + 1 is in LDS and every
+  // wave is done reading tile it (whose stage the next step refills).
+  auto step = [&](auto stage_tag, int it) {
+    constexpr int S = decltype(stage_tag)::value;
+    if (it + 3 < ntiles) issue(std::integral_constant<int, (S + 3) % 4>(), it + 3);
+    compute_tile(stage_tag, it);
+    const int later = (it + 3 < ntiles) + (it + 2 < ntiles);  // tiles issued after it + 1
+    if (later == 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * KC::OPS_PER_WAVE));
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KC::OPS_PER_WAVE));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    barrier_keep_loads();
+  };
+
+  issue(std::integral_constant<int, 0>(), 0);
+  if (ntiles > 1) issue(std::integral_constant<int, 1>(), 1);
+  if (ntiles > 2) issue(std::integral_constant<int, 2>(), 2);
+  if (ntiles > 2)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * KC::OPS_PER_WAVE));
+  else if (ntiles > 1)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KC::OPS_PER_WAVE));
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  barrier_keep_loads();
+  for (int it = 0; it < ntiles; it += 4) {
+    step(std::integral_constant<int, 0>(), it);
     if (it + 1 >= ntiles) break;
-    // odd tile: compute it + 1, stream it + 3 into sb, write it + 2 from sa
-    if (it + 3 < ntiles) load_tile(sb, it + 3);
-    compute_tile(it + 1);
-    if (it + 2 < ntiles) store_tile(sa, 0);
-    __syncthreads();
+    step(std::integral_constant<int, 1>(), it + 1);
+    if (it + 2 >= ntiles) break;
+    step(std::integral_constant<int, 2>(), it + 2);
+    if (it + 3 >= ntiles) break;
+    step(std::integral_constant<int, 3>(), it + 3);
   }
 }
 
-template <int D, int NW, int NB_>
+template <int D, int NW>
+// Eight waves (256 latents) run at four waves per SIMD, two workgroups per
+// compute unit (128 VGPRs); narrower workgroups are limited by LDS.
 __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 4 : 3)) void encode_bf16_kernel(EncodeParams p) {
-  using KC = EncodeKernel<D, NW, NB_>;
-  using op_t = typename KC::op_t;
-  constexpr int PL = KC::PL, DB = KC::DB, NB = KC::NB;
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2 * KC::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2 * KC::V_ELEMS];
+  using KC = EncodeKernel<D, NW>;
+  constexpr int SD = KC::SD;
+  // Separate arrays per stage, so that the compiler can tell a DMA into one
+  // stage from reads of another and adds no waits between them.
+  __shared__ __attribute__((aligned(16))) bf16 k0[KC::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 k1[KC::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 k2[KC::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 k3[KC::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v0[KC::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v1[KC::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v2[KC::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v3[KC::TILE_ELEMS];
   __shared__ int need_exact;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
   const int s = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / p.H, h = bh - b * p.H;
-  const int64_t n_begin = (int64_t)s * p.tokens_per_split;
-  const int64_t n_end = min(p.N, n_begin + p.tokens_per_split);
-  const int ntiles = n_end > n_begin ? (int)((n_end - n_begin + kEncT - 1) / kEncT) : 0;
-  const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + h * p.k.sh;
-  const bf16* vbase = reinterpret_cast<const bf16*>(p.v.data) + b * p.v.sb + h * p.v.sh;
+  const int b = bh / p.H, hd = bh - b * p.H;
+  // Split s takes the tiles s, s + S, s + 2S, ... of its head: at any time
+  // the workgroups of a head stream one contiguous window of K and V instead
+  // of S scattered regions (the merge is exact for any assignment of tokens
+  // to splits).
+  const int64_t n_end = p.N;
+  const int64_t tiles_all = (p.N + kEncT - 1) / kEncT;
+  const int ntiles = tiles_all > s ? (int)((tiles_all - 1 - s) / p.S + 1) : 0;
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + hd * p.k.sh;
+  const bf16* vbase = reinterpret_cast<const bf16*>(p.v.data) + b * p.v.sb + hd * p.v.sh;
+  const int lat0 = blockIdx.z * 32 * NW;  // first latent of this workgroup
+  const int m_lane = lat0 + wave * 32 + c;  // this lane's latent in the score tiles
 
-  // B operands of S^T = K Q^T: lane (g, r) holds latent 16nb + r, columns
-  // g*PL .. g*PL + PL - 1 of Q in bf16 (fp32 queries are rounded once).
-  op_t qop[NB];
+  // B operands of S^T = K Q^T: lane (h, c) holds latent m_lane, features
+  // 16 sd + 8h .. +7 of Q in bf16 (fp32 queries are rounded once).  The
+  // scale multiplies the fp32 scores: folding it into bf16 Q would add a
+  // rounding whose score error grows with the score.
+  bf16x8 qop[SD];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int m = wave * 16 * NB + nb * 16 + r;
-    float qv[PL];
+  for (int sd = 0; sd < SD; ++sd) {
+    float qv[8];
 #pragma unroll
-    for (int j = 0; j < PL; ++j) qv[j] = 0.f;
-    if (m < p.M) load_as_f32<PL>(p.q.data, p.q.is_f32, b * p.q.sb + h * p.q.sh + m * p.q.sl + g * PL, qv);
+    for (int j = 0; j < 8; ++j) qv[j] = 0.f;
+    if (m_lane < p.M)
+      load_as_f32<8>(p.q.data, p.q.is_f32, b * p.q.sb + hd * p.q.sh + m_lane * p.q.sl + 16 * sd + 8 * h, qv);
 #pragma unroll
-    for (int j = 0; j < PL; ++j) qop[nb][j] = (bf16)qv[j];
+    for (int j = 0; j < 8; ++j) qop[sd][j] = (bf16)qv[j];
   }
 
-  f32x4 o[NB][DB];
-  float lsum[NB], mrun[NB];
+  // Zero the stages once: a lane past the end of the tokens may leave its
+  // chunk unwritten, and stale data must be finite (its weight is 0).
+  {
+    bf16* stages[8] = {k0, k1, k2, k3, v0, v1, v2, v3};
+    const bf16x8 z8 = {};
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      for (int u = tid; u < KC::TILE_CHUNKS; u += KC::NT) reinterpret_cast<bf16x8*>(stages[st])[u] = z8;
+  }
+  f32x16 o;
+  float ls[4], mrun;
   if (tid == 0) need_exact = p.exact;
   __syncthreads();
   bool exact = need_exact != 0;
   if (!exact) {
-    encode_pass<D, NW, NB_, false>(p, kbase, vbase, n_begin, n_end, ntiles, k_lds, v_lds, qop, o, lsum, mrun);
-    bool bad = false;
+    encode_pass<D, NW, false>(p, kbase, vbase, s, p.S, n_end, ntiles, k0, k1, k2, k3, v0, v1, v2, v3, qop, o, ls, mrun);
+    const float lp = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    float l = lp + shfl_xor_f(lp, 32);
+    bool ok = l >= kSafeLo && l <= kSafeHi;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float l = lsum[nb];
-      l += shfl_xor_f(l, 16);
-      l += shfl_xor_f(l, 32);
-      const bool ok_l = l >= kSafeLo && l <= kSafeHi;
-      bool ok_o = true;
-#pragma unroll
-      for (int e = 0; e < DB; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ok_o = ok_o && __builtin_isfinite(o[nb][e][i]);
-      bad = bad || (wave * 16 * NB + nb * 16 + r < p.M && !ok_l) || (wave * 16 * NB + nb * 16 + 4 * g < p.M && !ok_o);
-    }
+    for (int i = 0; i < 16; ++i) ok = ok && __builtin_isfinite(o[i]);
+    const bool bad = m_lane < p.M && !ok;
     if (__any(bad) && lane == 0) need_exact = 1;
     __syncthreads();
-    exact = need_exact != 0 && n_end > n_begin;
+    exact = need_exact != 0 && ntiles > 0;
   }
   if (exact)
-    encode_pass<D, NW, NB_, true>(p, kbase, vbase, n_begin, n_end, ntiles, k_lds, v_lds, qop, o, lsum, mrun);
+    encode_pass<D, NW, true>(p, kbase, vbase, s, p.S, n_end, ntiles, k0, k1, k2, k3, v0, v1, v2, v3, qop, o, ls, mrun);
 
   // Epilogue: normalised split output and log2-normaliser of every latent.
+  // Accumulator row i of lane (h, c) is latent wave*32 + 8(i/4) + 4h + i%4,
+  // feature c; the normaliser of latent r sits in lanes r and r + 32.
   float* po = p.part_o + ((int64_t)bh * p.S + s) * p.M * D;
   float* pl = p.part_l + ((int64_t)bh * p.S + s) * p.M;
+  const float lp = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  const float l = lp + shfl_xor_f(lp, 32);
+  const float mr = exact ? mrun : 0.f;
+  if (h == 0 && m_lane < p.M)  // lanes 0..31 own the latent scalars
+    pl[m_lane] = l > 0.f ? __log2f(l) + (mr == -INFINITY ? 0.f : mr) : -INFINITY;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float l = lsum[nb];  // score layout: lane (g, r) holds latent 16nb + r
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
-    const float mr = exact ? mrun[nb] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float li = __shfl(l, 4 * g + i, 64);  // output layout: row 4g + i
-      const float mi = __shfl(mr, 4 * g + i, 64);
-      const int m = wave * 16 * NB + nb * 16 + 4 * g + i;
-      const float inv = li > 0.f ? 1.0f / li : 0.f;
-      const float lse2 = li > 0.f ? __log2f(li) + (mi == -INFINITY ? 0.f : mi) : -INFINITY;
-      if (m < p.M) {
-#pragma unroll
-        for (int e = 0; e < DB; ++e) po[(int64_t)m * D + 16 * e + r] = o[nb][e][i] * inv;
-        if (r == 0) pl[m] = lse2;
-      }
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+    const float li = __shfl(l, r, 64);
+    const int m = lat0 + wave * 32 + r;
+    if (m < p.M && c < D) po[(int64_t)m * D + c] = li > 0.f ? o[i] / li : 0.f;
   }
 }
 
@@ -493,40 +517,41 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
 
 EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32) {
   (void)D;
+  (void)is_f32;
   EncodePlan pl;
   const int64_t bh = (int64_t)B * H;
-  // 32 latents per wave; all latents of a head in one workgroup.
-  pl.waves = M <= 64 ? 2 : M <= 128 ? 4 : M <= 256 ? 8 : 16;
-  pl.lat_blocks = 2;
-  // About two workgroups per compute unit at a time, a few rounds in all; a
-  // split holds at least 256 tokens (2 tiles) so per-split overheads stay small.
-  const int64_t target = is_f32 ? 512 : 1024;
-  int64_t S = (target + bh - 1) / bh;
-  const int64_t max_s = (N + 255) / 256;
+  // 32 latents per wave, up to 256 latents (8 waves) per workgroup; more
+  // latents take further workgroups along grid.z.
+  pl.waves = M <= 64 ? 2 : M <= 128 ? 4 : 8;
+  pl.lat_blocks = (M + 255) / 256;
+  // About 1024 workgroups in all (a few per compute unit, a few rounds), at
+  // least two 128-token tiles per split when there are enough tokens.  The
+  // matrix-core path gives split s the tiles s, s + S, ...; the fp32 path
+  // takes S contiguous ranges of tokens_per_split tokens (the last ones may
+  // be empty and merge with weight 0).
+  const int64_t tiles = (N + kEncT - 1) / kEncT;
+  int64_t S = (1024 + bh - 1) / bh;
+  int64_t max_s = tiles / 2;
+  if (max_s < 1) max_s = 1;
   if (S > max_s) S = max_s;
   if (S < 1) S = 1;
-  int64_t tps = (N + S - 1) / S;
-  tps = (tps + kEncT - 1) / kEncT * kEncT;
-  pl.tokens_per_split = tps;
-  pl.S = (int)((N + tps - 1) / tps);
+  pl.S = (int)S;
+  pl.tokens_per_split = (tiles + S - 1) / S * kEncT;
   return pl;
 }
 
 hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, int lat_blocks, hipStream_t st) {
-  dim3 grid(p.S, B * p.H);
-#define FLARE_ENC(DD, NW, NB) \
-  hipLaunchKernelGGL((encode_bf16_kernel<DD, NW, NB>), grid, dim3(64 * NW), 0, st, p)
-  (void)lat_blocks;
+  dim3 grid(p.S, B * p.H, lat_blocks);
+#define FLARE_ENC(DD, NW) \
+  hipLaunchKernelGGL((encode_bf16_kernel<DD, NW>), grid, dim3(64 * NW), 0, st, p)
   if (D == 32) {
-    if (waves == 2) FLARE_ENC(32, 2, 2);
-    else if (waves == 4) FLARE_ENC(32, 4, 2);
-    else if (waves == 8) FLARE_ENC(32, 8, 2);
-    else FLARE_ENC(32, 16, 2);
+    if (waves == 2) FLARE_ENC(32, 2);
+    else if (waves == 4) FLARE_ENC(32, 4);
+    else FLARE_ENC(32, 8);
   } else {
-    if (waves == 2) FLARE_ENC(16, 2, 2);
-    else if (waves == 4) FLARE_ENC(16, 4, 2);
-    else if (waves == 8) FLARE_ENC(16, 8, 2);
-    else FLARE_ENC(16, 16, 2);
+    if (waves == 2) FLARE_ENC(16, 2);
+    else if (waves == 4) FLARE_ENC(16, 4);
+    else FLARE_ENC(16, 8);
   }
 #undef FLARE_ENC
   return hipGetLastError();

@@ -42,7 +42,8 @@ struct DecodeParams {
   int y_f32;
   int64_t y_sb, y_sh, y_sl;
   int H, M;
-  int64_t N, tokens_per_block;
+  int64_t N;
+  int64_t tokens_per_block;  // bf16 path: workgroups per head; fp32 path: tokens per workgroup
   float c;
   int exact;
 };
@@ -62,7 +63,7 @@ struct GemmParams {
 // Split planning shared by the workspace-size query and the launcher.
 struct EncodePlan {
   int S;                    // number of token splits
-  int64_t tokens_per_split; // multiple of 64
+  int64_t tokens_per_split; // fp32 path: contiguous tokens per split (multiple of 128)
   int waves;                // waves per workgroup (bf16 path)
   int lat_blocks;           // 16-latent blocks per wave (bf16 path)
 };
@@ -71,6 +72,8 @@ EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32);
 hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, int lat_blocks, hipStream_t s);
 hipError_t launch_encode_f32(const EncodeParams& p, int D, int B, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int B, hipStream_t s);
+// Workgroups per (batch, head) of the bf16 decoder.
+int64_t plan_decode_bf16(int B, int H, int M, int64_t N, int D);
 hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams& p, int D, int B, hipStream_t s);
 hipError_t launch_transpose_weights(const void* w, void* wt, int Cin, int Cout, hipStream_t s);

@@ -12,6 +12,9 @@ sample on the host cores ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
        python bench.py --copy-calibration   (plain device copy, for PMC scaling)
+       python bench.py --write-traffic FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
+           (host only: turns rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of
+            the bench kernels and of the copy into profiles/traffic_<kernel>.json)
 """
 import argparse
 import hashlib
@@ -38,27 +41,90 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle sample")
     ap.add_argument("--y-layout", choices=("token", "head"), default="token")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     return ap.parse_args()
 
 
-def kernel_source_sha(files):
+# Sources whose change invalidates a stored counter reading of a kernel
+# (the kernel itself, shared device code, and the host code that picks its
+# grid).
+KERNEL_SOURCES = {
+    "encode_bf16_kernel": ["encode.hip", "common.hpp", "launch.hpp", "api.cpp"],
+    "merge_kernel": ["encode.hip", "common.hpp", "launch.hpp", "api.cpp"],
+    "decode_bf16_kernel": ["decode.hip", "common.hpp", "launch.hpp", "api.cpp"],
+}
+COPY_BYTES = 1 << 30  # bytes read (and written) per launch of the calibration copy
+
+
+def kernel_source_sha(kernel):
     h = hashlib.sha256()
-    for f in files:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "rank_latent_routing_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel, sha):
-    """HBM bytes per launch from the committed PMC summary, if it was taken
-    on the current kernel source; else None."""
-    p = os.path.join(PROFILES, f"traffic_{kernel}.json")
-    if not os.path.exists(p):
-        return None
-    d = json.load(open(p))
-    if d.get("source_sha") != sha:
-        return None
-    return d.get("bytes_per_launch")
+def stored_traffic(kernels):
+    """HBM bytes per launch (summed over the given kernels) from the committed
+    counter summaries, if every one was taken on the current kernel source;
+    else None."""
+    total = 0.0
+    for kernel in kernels:
+        p = os.path.join(PROFILES, f"traffic_{kernel}.encdec_n1m.json")
+        if not os.path.exists(p):
+            return None
+        d = json.load(open(p))
+        if d.get("source_sha") != kernel_source_sha(kernel):
+            return None
+        total += d["bytes_per_launch"]
+    return total
+
+
+def counter_means(path, counter):
+    """Mean over dispatches of one counter, per kernel (full demangled name),
+    from a rocprofv3 counter_collection csv (rows of one dispatch are summed)."""
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for row in csv.DictReader(open(path)):
+        if row["Counter_Name"] == counter:
+            per[row["Kernel_Name"]][row["Dispatch_Id"]] += float(row["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def library_kernel(means, kernel):
+    """The value of our kernel `kernel` (any template instance) in `means`."""
+    hits = [v for k, v in means.items() if f"flare::{kernel}" in k]
+    return hits[0] if len(hits) == 1 else None
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per launch of the bench kernels from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for a
+    plain 1 GiB device copy."""
+    fetch, write = counter_means(fetch_csv, "FETCH_SIZE"), counter_means(write_csv, "WRITE_SIZE")
+    cf, cw = counter_means(copy_fetch_csv, "FETCH_SIZE"), counter_means(copy_write_csv, "WRITE_SIZE")
+    copy_kernel = max(cf, key=cf.get)
+    f_read = COPY_BYTES / (cf[copy_kernel] * 1024.0)
+    f_write = COPY_BYTES / (cw[copy_kernel] * 1024.0)
+    os.makedirs(PROFILES, exist_ok=True)
+    for kernel in KERNEL_SOURCES:
+        kf, kw = library_kernel(fetch, kernel), library_kernel(write, kernel)
+        if kf is None or kw is None:
+            continue
+        d = {"kernel": kernel,
+             "workload": "FLARE encode+decode, B=1, H=8, D=32, N=1048576, M=256, bf16 (bench.py default)",
+             "source_sha": kernel_source_sha(kernel),
+             "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+             "copy_kernel": copy_kernel, "copy_fetch_kib": cf[copy_kernel], "copy_write_kib": cw[copy_kernel],
+             "copy_factor_read": f_read, "copy_factor_write": f_write,
+             "bytes_read_per_launch": kf * 1024.0 * f_read,
+             "bytes_written_per_launch": kw * 1024.0 * f_write,
+             "bytes_per_launch": kf * 1024.0 * f_read + kw * 1024.0 * f_write}
+        with open(os.path.join(PROFILES, f"traffic_{kernel}.encdec_n1m.json"), "w") as fh:
+            json.dump(d, fh, indent=1)
+        print(f"{kernel}: {d['bytes_per_launch'] / 1e9:.3f} GB per launch "
+              f"(read {d['bytes_read_per_launch'] / 1e9:.3f}, written {d['bytes_written_per_launch'] / 1e9:.3f})")
 
 
 def copy_calibration():
@@ -80,6 +146,8 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         return copy_calibration()
+    if args.write_traffic:
+        return write_traffic(*args.write_traffic)
 
     import numpy as np
     import torch
@@ -132,14 +200,14 @@ def main():
     # Dominant kernel: the longer of the two calls.  The decode call is one
     # kernel; the encode call is the split kernel plus a small merge.
     if dec_ms >= enc_ms:
-        kname, kms, kwork, ksha = "decode_bf16_kernel", dec_ms, dec, kernel_source_sha(["decode.hip", "common.hpp"])
+        kname, kms, kwork = "decode_bf16_kernel", dec_ms, dec
     else:
-        kname, kms, kwork, ksha = "encode_bf16_kernel+merge_kernel", enc_ms, enc, kernel_source_sha(["encode.hip", "common.hpp"])
+        kname, kms, kwork = "encode_bf16_kernel+merge_kernel", enc_ms, enc
     achieved = kwork.flops / (kms / 1e3) / 1e12
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": stored_traffic(kname.split("+")[0], ksha),
+                "traffic": stored_traffic(kname.split("+")),
                 "algorithmic_per_launch": {"flops": kwork.flops, "bytes": kwork.bytes,
                                            "unit": "per (token, head): 4*M*D flops, 4*D bytes",
                                            "units_per_launch": B * H * N},

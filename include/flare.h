@@ -64,8 +64,11 @@ typedef enum flare_dtype { FLARE_F32 = 0, FLARE_BF16 = 1 } flare_dtype;
  * the batch, e.g. learned queries or seeds).  Token-major activations
  * [B, N, H*D] are stride_b = N*H*D, stride_h = D, stride_l = H*D; head-major
  * [B, H, N, D] are stride_b = H*N*D, stride_h = N*D, stride_l = D.
- * Requirements: data 16-byte aligned; stride_h and stride_l multiples of 8
- * elements (bf16) or 4 elements (fp32); stride_b a multiple of the same or 0.
+ * Requirements for token-side tensors (K, V, eK, eV, Y): data 16-byte
+ * aligned; stride_h and stride_l multiples of 8 elements (bf16) or 4
+ * elements (fp32); stride_b a multiple of the same or 0; stride_l below 2^22
+ * elements (a 128-token tile is addressed with 32-bit byte offsets).
+ * Latent-side tensors (Q, seeds, Z) need only element alignment.
  */
 typedef struct flare_tensor {
   void* data;
@@ -134,8 +137,10 @@ flare_status flare_decode(const flare_tensor* K, const flare_tensor* Q,
  * no bias).  X [R, C_in] row-major bf16; each W_p [C_in, C_out] row-major
  * bf16; each Y_p bf16 written either row-major [R, C_out]
  * (out_head_major = 0) or head-major [B, H, N, D] with R = B*N and
- * C_out = H*D (out_head_major = 1, D = head_dim).  C_in, C_out multiples of
- * 32 and <= 1024; 1 <= n_proj <= 5.  Workspace holds the transposed weights:
+ * C_out = H*D (out_head_major = 1, D = head_dim).  C_in in {32, 64, 128,
+ * 256}; C_out a multiple of 16, at most 4096; 1 <= n_proj <= 5; X and every
+ * Y_p 16-byte aligned (FLARE_E_UNSUPPORTED / FLARE_E_INVALID otherwise).
+ * Workspace holds the weights rearranged into matrix-core operand order:
  * flare_project_workspace_size(C_in, C_out, n_proj) bytes.
  */
 size_t flare_project_workspace_size(int C_in, int C_out, int n_proj);
@@ -153,7 +158,10 @@ flare_status flare_project(const void* X, const void* const* W, void* const* Y,
  *           seeds and Q(X) = SDPA(seeds, eK, eV) replaces the learned queries
  *           in both the encode and the decode.
  * Heads are concatenated into out [B, N, C]; if W_O != NULL, out = Y W_O.
- * All weights [C, C] with y = x W.  Requires workspace_bytes >=
+ * All weights [C, C] with y = x W.  dtype must be FLARE_BF16; C = H*D with
+ * D in {16, 32} and C in {32, 64, 128, 256} (FLARE_E_UNSUPPORTED otherwise);
+ * X and out 16-byte aligned; Q_or_seeds [H, M, D] bf16, contiguous.
+ * Requires a 256-byte aligned workspace of workspace_bytes >=
  * flare_mix_workspace_size(B, N, C, H, M, W_eK != NULL, W_O != NULL).
  */
 size_t flare_mix_workspace_size(int B, int64_t N, int C, int H, int M,

@@ -138,7 +138,7 @@ flare_status flare_decode(const flare_tensor* K, const flare_tensor* Q,
  * bf16; each Y_p bf16 written either row-major [R, C_out]
  * (out_head_major = 0) or head-major [B, H, N, D] with R = B*N and
  * C_out = H*D (out_head_major = 1, D = head_dim).  C_in in {32, 64, 128,
- * 256}; C_out a multiple of 16, at most 4096; 1 <= n_proj <= 5; X and every
+ * 256}; C_out a multiple of 32, at most 4096; 1 <= n_proj <= 5; X and every
  * Y_p 16-byte aligned (FLARE_E_UNSUPPORTED / FLARE_E_INVALID otherwise).
  * Workspace holds the weights rearranged into matrix-core operand order:
  * flare_project_workspace_size(C_in, C_out, n_proj) bytes.

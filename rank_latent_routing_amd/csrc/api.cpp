@@ -138,9 +138,9 @@ flare_status decode_impl(const View& k, const View& q, const View& z, void* y, i
 }
 
 bool proj_shape_ok(int64_t R, int Cin, int Cout, int n_proj) {
-  return R >= 1 && (Cin == 32 || Cin == 64 || Cin == 128 || Cin == 256) && Cout >= 16 &&
-         Cout % 16 == 0 && Cout <= 4096 && n_proj >= 1 && n_proj <= 5 &&
-         (R + 255) / 256 <= 0x7fffffff;
+  return R >= 1 && (Cin == 32 || Cin == 64 || Cin == 128 || Cin == 256) && Cout >= 32 &&
+         Cout % 32 == 0 && Cout <= 4096 && n_proj >= 1 && n_proj <= 5 &&
+         (R + 511) / 512 <= 0x7fffffff;
 }
 
 size_t proj_ws(int Cin, int Cout, int n_proj) {
@@ -261,7 +261,7 @@ flare_status flare_project(const void* X, const void* const* W, void* const* Y, 
   }
   if (!X || !W || !Y || reinterpret_cast<uintptr_t>(X) % 16) return FLARE_E_INVALID;
   for (int i = 0; i < n_proj; ++i)
-    if (!W[i] || !Y[i] || reinterpret_cast<uintptr_t>(W[i]) % 2 || reinterpret_cast<uintptr_t>(Y[i]) % 8)
+    if (!W[i] || !Y[i] || reinterpret_cast<uintptr_t>(W[i]) % 2 || reinterpret_cast<uintptr_t>(Y[i]) % 16)
       return FLARE_E_INVALID;
   if (out_head_major) {
     if (B < 1 || R % B || (head_dim != 16 && head_dim != 32) || C_out % head_dim) return FLARE_E_INVALID;

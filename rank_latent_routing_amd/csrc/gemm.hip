@@ -2,22 +2,31 @@
 // ("FLARE++: Low-Rank Attention with Dynamic Attention Routing", section 3:
 // K = X W_K and V = X W_V in "Full self-attention" / "FLARE: fixed-query
 // latent routing", the extra eK, eV of equation 7, and the output
-// projection).  At C <= 1024 the reduction is short, so the kernel is built
-// around reading X from HBM once:
+// projection).  At C <= 256 the reduction is short and the outputs outweigh
+// the input, so the kernel is built around HBM traffic:
 //   - a wave loads its 64 rows of X once into registers, already as the B
 //     operand of Y^T = W^T X^T (lane (g, r): row r, inputs 8g..8g+7 of each
-//     32-wide step), and keeps them for every output column;
-//   - the weights are pre-swizzled (once per call, a few hundred KB) into
-//     operand order, so a 16-column block is a contiguous 1 KB per k-step that
-//     the workgroup copies into LDS (double buffered) and all four waves read;
-//   - the output tile comes out transposed, so each lane holds 4 consecutive
-//     output columns of one row and stores them as one 8-byte write.
+//     32-wide step), and keeps them for every output column of every
+//     projection, so X is read from HBM once;
+//   - the weights are rearranged once per call into operand order, in
+//     32-column blocks of 2 KB per k-step; the workgroup streams the blocks
+//     into LDS with buffer loads straight to LDS (four stages, three blocks in
+//     flight, one barrier per block) and all eight waves read them;
+//   - inside a block the two 16-column tiles are interleaved (tile t covers
+//     columns 8(m/4) + 4t + m%4 of its rows m), so each lane ends with eight
+//     consecutive output columns of one row and writes them as one 16-byte
+//     store.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace flare {
 
-// wsw[cb][ks][lane][j] = W[32 ks + 8 (lane/16) + j][16 cb + lane%16]
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// For 32-column block pb, k-step ks and tile t: the A operand of 16 output
+// columns as 64 lanes x 8 bf16,
+//   wsw[((pb KS + ks) 2 + t) 512 + 8 lane + j]
+//     = W[32 ks + 8 (lane / 16) + j][32 pb + 8 (m / 4) + 4 t + m % 4],  m = lane % 16.
 __global__ __launch_bounds__(256) void swizzle_weights_kernel(const bf16* __restrict__ w,
                                                               bf16* __restrict__ wsw, int Cin,
                                                               int Cout) {
@@ -26,31 +35,41 @@ __global__ __launch_bounds__(256) void swizzle_weights_kernel(const bf16* __rest
   if (idx >= total) return;
   const int j = (int)(idx & 7);
   const int lane = (int)((idx >> 3) & 63);
-  const int64_t rest = idx >> 9;
+  const int t = (int)((idx >> 9) & 1);
+  const int64_t rest = idx >> 10;
   const int KS = Cin / 32;
   const int ks = (int)(rest % KS);
-  const int cb = (int)(rest / KS);
+  const int pb = (int)(rest / KS);
+  const int m = lane & 15;
   const int c = 32 * ks + 8 * (lane >> 4) + j;
-  const int col = 16 * cb + (lane & 15);
+  const int col = 32 * pb + 8 * (m >> 2) + 4 * t + (m & 3);
   wsw[idx] = w[(int64_t)c * Cout + col];
 }
 
-constexpr int kGemmRowsPerWave = 64;
-constexpr int kGemmWaves = 4;
+constexpr int kGemmRowsPerWave = 64;  // four 16-row tiles
+constexpr int kGemmWaves = 8;
+constexpr int kGemmRowsPerBlock = kGemmRowsPerWave * kGemmWaves;
 
 template <int CIN>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p, int cb_per_group) {
+__global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int NW = kGemmWaves;
   constexpr int KS = CIN / 32;
-  constexpr int BLK = KS * 64 * 8;  // bf16 elements of one swizzled 16-column block
-  __shared__ __attribute__((aligned(16))) bf16 w_lds[2][BLK];
+  constexpr int BLK = KS * 2 * 512;  // bf16 elements of one 32-column block
+  constexpr int OPS = BLK / 512;     // 1 KB loads per block
+  constexpr int OPW = (OPS + NW - 1) / NW;
+  __shared__ __attribute__((aligned(16))) bf16 s0[BLK];
+  __shared__ __attribute__((aligned(16))) bf16 s1[BLK];
+  __shared__ __attribute__((aligned(16))) bf16 s2[BLK];
+  __shared__ __attribute__((aligned(16))) bf16 s3[BLK];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r = lane & 15;
-  const int64_t row0 = (int64_t)blockIdx.x * (kGemmRowsPerWave * kGemmWaves) + wave * kGemmRowsPerWave;
-  const int cb_per_proj = p.Cout / 16;
-  const int cb_total = p.n_proj * cb_per_proj;
-  const int cb_begin = blockIdx.y * cb_per_group;
-  const int cb_end = min(cb_total, cb_begin + cb_per_group);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
+  const int64_t row0 = (int64_t)blockIdx.x * kGemmRowsPerBlock + wave * kGemmRowsPerWave;
   const bf16* xin = reinterpret_cast<const bf16*>(p.x);
+  const int pairs = p.Cout / 32;
+  const int nblk = p.n_proj * pairs;
+  // Waves issue either OPW loads per block or none.
+  const int my_ops = wave * OPW < OPS ? OPW : 0;
 
   // X rows as B operands, held for all output columns.
   bf16x8 xb[4][KS];
@@ -68,72 +87,119 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p, int cb_per
     }
   }
 
-  constexpr int CHUNKS = BLK / 8;  // 16-byte chunks per block
-  constexpr int PER = (CHUNKS + 255) / 256;
-  u32x4 stage[PER];
-  auto src_block = [&](int cb) -> const bf16* {
-    const int pr = cb / cb_per_proj, cbl = cb - pr * cb_per_proj;
-    return reinterpret_cast<const bf16*>(p.wt[pr]) + (int64_t)cbl * BLK;
-  };
-  auto load_block = [&](int cb) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(src_block(cb));
+  // Block b (projection b / pairs, column block b % pairs) into stage S.
+  auto issue = [&](auto stage_tag, int b) {
+    constexpr int S = decltype(stage_tag)::value;
+    bf16* st = S == 0 ? s0 : S == 1 ? s1 : S == 2 ? s2 : s3;
+    const int pr = b / pairs, pb = b - pr * pairs;
+    const bf16* src = reinterpret_cast<const bf16*>(p.wt[pr]) + (int64_t)pb * BLK;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(src), (short)0, BLK * (int)sizeof(bf16), kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int u = tid + 256 * i;
-      if (u < CHUNKS) stage[i] = src[u];
-    }
-  };
-  auto store_block = [&](int buf) {
-    u32x4* dst = reinterpret_cast<u32x4*>(w_lds[buf]);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int u = tid + 256 * i;
-      if (u < CHUNKS) dst[u] = stage[i];
+    for (int q = 0; q < OPW; ++q) {
+      const int op = wave * OPW + q;
+      if (op < OPS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(st + op * 512), 16, lane * 16, op * 1024, 0, 0);
     }
   };
 
-  if (cb_begin < cb_end) {
-    load_block(cb_begin);
-    store_block(0);
+  // Element offset of (row row0 + 16 rb + r, column 0) in the output: row-major
+  // [R, Cout], or head-major [B, H, N, D] with R = B N (head 0 of the row's
+  // token; a column c adds (c / D) N D + c % D).
+  int64_t row_off[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int64_t row = min(row0 + 16 * rb + r, p.R - 1);
+    if (p.head_major) {
+      const int64_t bi = row / p.N, n = row - bi * p.N;
+      row_off[rb] = (bi * (p.Cout / p.D) * p.N + n) * p.D;
+    } else {
+      row_off[rb] = row * p.Cout;
+    }
   }
-  __syncthreads();
-  for (int cb = cb_begin; cb < cb_end; ++cb) {
-    const int buf = (cb - cb_begin) & 1;
-    if (cb + 1 < cb_end) load_block(cb + 1);
-    f32x4 acc[4];
+
+  // Store of one output row tile: lane (g, r) holds columns 8g .. 8g+7 of
+  // block pb (tile 0 gives 8g..8g+3, tile 1 gives 8g+4..8g+7) for row
+  // row0 + 16 rb + r.
+  auto store_row_tile = [&](const f32x4 (&acc)[2], int rb, int pr, int64_t col_off) {
+    bf16x8 v;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&w_lds[buf][(ks * 64 + lane) * 8]);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[rb] = mfma_16x16x32(a, xb[rb][ks], acc[rb]);
+    for (int i = 0; i < 4; ++i) {
+      v[i] = (bf16)acc[0][i];
+      v[4 + i] = (bf16)acc[1][i];
     }
-    // lane (g, r) of tile rb holds output columns 16cbl + 4g .. +3 of row
-    // row0 + 16rb + r
-    const int pr = cb / cb_per_proj, cbl = cb - pr * cb_per_proj;
-    const int col = 16 * cbl + 4 * g;
-    bf16* yout = reinterpret_cast<bf16*>(p.y[pr]);
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(p.y[pr]) + row_off[rb] + col_off) = v;
+  };
+
+  const bool full_rows = row0 + kGemmRowsPerWave <= p.R;  // uniform in the wave
+  auto compute_block = [&](auto stage_tag, int b) {
+    constexpr int S = decltype(stage_tag)::value;
+    const bf16* st = S == 0 ? s0 : S == 1 ? s1 : S == 2 ? s2 : s3;
+    f32x4 acc[4][2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int64_t row = row0 + 16 * rb + r;
-      if (row >= p.R) continue;
-      int64_t off;
-      if (p.head_major) {
-        const int64_t bi = row / p.N, n = row - bi * p.N;
-        const int hd = col / p.D, d = col - hd * p.D;
-        const int H = p.Cout / p.D;
-        off = ((bi * H + hd) * p.N + n) * p.D + d;
-      } else {
-        off = row * p.Cout + col;
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) acc[rb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + ((ks * 2 + t) * 64 + lane) * 8);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) acc[rb][t] = mfma_16x16x32(a, xb[rb][ks], acc[rb][t]);
       }
-      bf16x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = (bf16)acc[rb][i];
-      *reinterpret_cast<bf16x4*>(yout + off) = v;
+    const int pr = b / pairs, pb = b - pr * pairs;
+    const int col = 32 * pb + 8 * g;
+    int64_t col_off = col;
+    if (p.head_major) {
+      const int hd = col / p.D;
+      col_off = (int64_t)hd * p.N * p.D + (col - hd * p.D);
     }
-    if (cb + 1 < cb_end) store_block(buf ^ 1);
-    __syncthreads();
+    if (full_rows) {
+      // exactly four stores per block: the step's wait counts them
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) store_row_tile(acc[rb], rb, pr, col_off);
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        if (row0 + 16 * rb + r < p.R) store_row_tile(acc[rb], rb, pr, col_off);
+    }
+  };
+
+  // Block b lives in stage b % 4.  Step b: start the load of block b + 3,
+  // compute and store block b, then wait until this wave's load of block
+  // b + 1 has landed (vmcnt counts loads and stores in issue order: the
+  // loads of blocks b + 2 and b + 3 and the four stores of block b may stay
+  // in flight) and meet at the barrier.
+  auto step = [&](auto stage_tag, int b) {
+    constexpr int S = decltype(stage_tag)::value;
+    if (b + 3 < nblk) issue(std::integral_constant<int, (S + 3) % 4>(), b + 3);
+    compute_block(stage_tag, b);
+    const int later = ((b + 3 < nblk) + (b + 2 < nblk)) * (my_ops != 0);  // loads issued after block b + 1
+    if (!full_rows)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    else if (later == 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * OPW + 4));
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(OPW + 4));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4));
+    barrier_keep_loads();
+  };
+
+  issue(std::integral_constant<int, 0>(), 0);
+  if (nblk > 1) issue(std::integral_constant<int, 1>(), 1);
+  if (nblk > 2) issue(std::integral_constant<int, 2>(), 2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // X rows and the first blocks
+  barrier_keep_loads();
+  for (int b = 0; b < nblk; b += 4) {
+    step(std::integral_constant<int, 0>(), b);
+    if (b + 1 >= nblk) break;
+    step(std::integral_constant<int, 1>(), b + 1);
+    if (b + 2 >= nblk) break;
+    step(std::integral_constant<int, 2>(), b + 2);
+    if (b + 3 >= nblk) break;
+    step(std::integral_constant<int, 3>(), b + 3);
   }
 }
 
@@ -145,21 +211,14 @@ hipError_t launch_transpose_weights(const void* w, void* wt, int Cin, int Cout, 
 }
 
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t st) {
-  const int64_t rows_per_block = kGemmRowsPerWave * kGemmWaves;
-  const int64_t row_blocks = (p.R + rows_per_block - 1) / rows_per_block;
-  const int cb_total = p.n_proj * (p.Cout / 16);
-  // Enough workgroups to cover 256 compute units several times: split the
-  // output columns across workgroups when there are few row blocks.
-  int groups = 1;
-  while (row_blocks * groups < 1024 && groups * 2 <= cb_total) groups *= 2;
-  const int per = (cb_total + groups - 1) / groups;
-  groups = (cb_total + per - 1) / per;
-  dim3 grid((unsigned)row_blocks, groups);
+  const int64_t blocks = (p.R + kGemmRowsPerBlock - 1) / kGemmRowsPerBlock;
+  dim3 grid((unsigned)blocks);
+  dim3 block(64 * kGemmWaves);
   switch (p.Cin) {
-    case 32: hipLaunchKernelGGL((gemm_bf16_kernel<32>), grid, dim3(256), 0, st, p, per); break;
-    case 64: hipLaunchKernelGGL((gemm_bf16_kernel<64>), grid, dim3(256), 0, st, p, per); break;
-    case 128: hipLaunchKernelGGL((gemm_bf16_kernel<128>), grid, dim3(256), 0, st, p, per); break;
-    case 256: hipLaunchKernelGGL((gemm_bf16_kernel<256>), grid, dim3(256), 0, st, p, per); break;
+    case 32: hipLaunchKernelGGL((gemm_bf16_kernel<32>), grid, block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((gemm_bf16_kernel<64>), grid, block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL((gemm_bf16_kernel<128>), grid, block, 0, st, p); break;
+    case 256: hipLaunchKernelGGL((gemm_bf16_kernel<256>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

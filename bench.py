@@ -268,6 +268,28 @@ def main():
             "ms": round(mms, 4), "tokens_per_s": N / (mms / 1e3),
             "tflops": round(mwk.flops / (mms / 1e3) / 1e12, 1)}
 
+        # FLARE (fixed learned queries, no synthesis, no eK/eV) at the same
+        # sizes, for the FLARE++ / FLARE cost ratio the pages discuss.
+        def mix_fixed():
+            rl.flare_mix(m["x"], m["w_k"], m["w_v"], m["qs"], H, w_o=m["w_o"], out=out, workspace=mws,
+                         stream=stream)
+        for _ in range(max(2, args.warmup // 2)):
+            mix_fixed()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(msteps):
+            mix_fixed()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fms = e0.elapsed_time(e1) / msteps
+        fwk = costs.mixer(1, N, mw.C, H, M, dynamic=False, has_wo=True)
+        extra["flare_mixer"] = {
+            "config": "FLARE mixer with all projections, B=1, N=1048576, C=256, H=8, D=32, M=256, bf16",
+            "ms": round(fms, 4), "tokens_per_s": N / (fms / 1e3),
+            "tflops": round(fwk.flops / (fms / 1e3) / 1e12, 1)}
+        extra["flarepp_over_flare"] = {"time": round(mms / fms, 3),
+                                       "operations": round(mwk.flops / fwk.flops, 3)}
+
     cpu = None
     if not args.no_cpu:
         import oracle

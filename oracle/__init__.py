@@ -44,6 +44,9 @@ def _load():
     lib.oracle_sdpa.argtypes = [_d, _i64, _d, _i64, _d, _i64, _d, _i64, _d,
                                 _i64, _i64, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_double]
+    lib.oracle_sdpa_backward.argtypes = [_d, _i64, _d, _i64, _d, _i64, _d, _i64, _d, _i64,
+                                         _d, _i64, _d, _i64, _i64, _i64, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_double]
     lib.oracle_matmul.argtypes = [_d, _i64, _d, _i64, _d, _i64, _i64,
                                   ctypes.c_int, ctypes.c_int]
     lib.oracle_merge.argtypes = [_d, _i64, _d, ctypes.c_int, _i64, ctypes.c_int,
@@ -63,7 +66,7 @@ def _load():
     lib.oracle_flare_mix.argtypes = [_d, _d, _d, _d, _d, _d, _d, _d, _d, _d,
                                      ctypes.c_int, _i64, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_double]
-    for f in ("oracle_sdpa", "oracle_matmul", "oracle_merge",
+    for f in ("oracle_sdpa", "oracle_sdpa_backward", "oracle_matmul", "oracle_merge",
               "oracle_sharded_encode", "oracle_mixing_matrix",
               "oracle_flare_encdec", "oracle_flare_mix"):
         getattr(lib, f).restype = ctypes.c_int
@@ -115,6 +118,77 @@ def sdpa(q, k, v, scale=None, return_lse=False):
     _check(_load().oracle_sdpa(_p(q), D, _p(kp), D, _p(vp), Dv, _p(o), Dv,
                                _p(lse), Lq, Lk, D, Dv, float(scale)), "sdpa")
     return (o, lse) if return_lse else o
+
+
+def sdpa_backward(q, k, v, do, scale=None):
+    """Gradients (dq, dk, dv) of sum(do * sdpa(q, k, v)) for q [Lq, D],
+    k [Lk, D], v [Lk, Dv], do [Lq, Dv] (the standard SDPA gradient, which is
+    what the encoder and decoder calls need in training)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    Lq, D = q.shape
+    Lk, Dv = v.shape
+    assert k.shape == (Lk, D) and do.shape == (Lq, Dv)
+    if scale is None:
+        scale = default_scale(D)
+    dq, dk, dv = np.empty((Lq, D)), np.empty((Lk, D)), np.empty((Lk, Dv))
+    _check(_load().oracle_sdpa_backward(_p(q), D, _p(k), D, _p(v), Dv, _p(do), Dv,
+                                        _p(dq), D, _p(dk), D, _p(dv), Dv, Lq, Lk, D, Dv,
+                                        float(scale)), "sdpa_backward")
+    return dq, dk, dv
+
+
+def encode_backward(q, k, v, dz, scale=None):
+    """Gradients of sum(dz * encode(q, k, v)) for q [B|1, H, M, D] or [H, M, D],
+    k, v [B, H, N, D], dz [B, H, M, D].  Returns (dq [B, H, M, D] per batch
+    element, dk, dv [B, H, N, D]); a batch-shared q gets the sum over b."""
+    q = _f64(q)
+    if q.ndim == 3:
+        q = q[None]
+    k, v, dz = _f64(k), _f64(v), _f64(dz)
+    B, H, N, D = k.shape
+    dq = np.empty(dz.shape)
+    dk = np.empty(k.shape)
+    dv = np.empty(v.shape)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = sdpa_backward(q[b if q.shape[0] > 1 else 0, h], k[b, h],
+                                                         v[b, h], dz[b, h], scale)
+    return dq, dk, dv
+
+
+def decode_backward(k, q, z, dy, scale=None):
+    """Gradients of sum(dy * decode(k, q, z)) for k [B, H, N, D], q, z
+    [B|1, H, M, D] or [H, M, D], dy [B, H, N, D].  Returns (dk [B, H, N, D],
+    dq, dz [B, H, M, D] per batch element)."""
+    k, dy = _f64(k), _f64(dy)
+    q, z = _f64(q), _f64(z)
+    if q.ndim == 3:
+        q = q[None]
+    if z.ndim == 3:
+        z = z[None]
+    B, H, N, D = k.shape
+    M = q.shape[2]
+    dk = np.empty(k.shape)
+    dq = np.empty((B, H, M, D))
+    dz = np.empty((B, H, M, z.shape[3]))
+    for b in range(B):
+        for h in range(H):
+            dk[b, h], dq[b, h], dz[b, h] = sdpa_backward(k[b, h], q[b if q.shape[0] > 1 else 0, h],
+                                                         z[b if z.shape[0] > 1 else 0, h], dy[b, h], scale)
+    return dk, dq, dz
+
+
+def flare_encdec_backward(q, k, v, dy, scale=None):
+    """Gradients of sum(dy * Y) for the FLARE pair Z = SDPA(Q, K, V),
+    Y = SDPA(K, Q, Z) with head-major k, v, dy [B, H, N, D] and q
+    [B|1, H, M, D] or [H, M, D].  The chain rule through the two calls:
+    the decoder's gradient gives dK, dQ and dZ; dZ drives the encoder's
+    gradient, whose dQ and dK add to the decoder's.  Returns (dq per batch
+    element [B, H, M, D], dk, dv)."""
+    z, _ = encode(q, k, v, scale)
+    dk1, dq1, dz = decode_backward(k, q, z, dy, scale)
+    dq2, dk2, dv = encode_backward(q, k, v, dz, scale)
+    return dq1 + dq2, dk1 + dk2, dv
 
 
 def matmul(x, w):

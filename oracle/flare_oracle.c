@@ -114,6 +114,111 @@ int oracle_sdpa(const double* q, int64_t q_rs, const double* k, int64_t k_rs,
 }
 
 /*
+ * Gradient of one SDPA call.  Training with the mixer runs it backwards
+ * ([P1] "FLARE: fixed-query latent routing": encoder and decoder are
+ * standard SDPA calls, so their gradients are the standard SDPA gradients).
+ * With s_ij = scale q_i . k_j, P = softmax_j(s), o_i = sum_j P_ij v_j and an
+ * upstream gradient do (of o), differentiating the definition gives
+ *   delta_i = do_i . o_i
+ *   dS_ij   = P_ij (do_i . v_j - delta_i)          (gradient of s_ij)
+ *   dq_i    = scale sum_j dS_ij k_j
+ *   dk_j    = scale sum_i dS_ij q_i
+ *   dv_j    = sum_i P_ij do_i
+ * Three passes: row statistics (P recomputed with the two-pass softmax,
+ * o, delta), then dq by rows, then dk and dv by keys.  Nothing is
+ * materialised beyond two doubles per row.
+ */
+int oracle_sdpa_backward(const double* q, int64_t q_rs, const double* k, int64_t k_rs,
+                         const double* v, int64_t v_rs, const double* dout, int64_t do_rs,
+                         double* dq, int64_t dq_rs, double* dk, int64_t dk_rs, double* dv,
+                         int64_t dv_rs, int64_t Lq, int64_t Lk, int D, int Dv, double scale) {
+  if (Lq <= 0 || Lk <= 0 || D <= 0 || Dv <= 0) return ORACLE_EINVAL;
+  double* lse = (double*)malloc(sizeof(double) * (size_t)Lq);
+  double* delta = (double*)malloc(sizeof(double) * (size_t)Lq);
+  if (!lse || !delta) {
+    free(lse);
+    free(delta);
+    return ORACLE_ENOMEM;
+  }
+  int failed = 0;
+  /* pass 1: per row, the log-normaliser and delta = do . o */
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Lk);
+    double* o = (double*)malloc(sizeof(double) * (size_t)Dv);
+    if (!s || !o) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < Lq; ++i) {
+      if (!s || !o) continue;
+      const double* qi = q + i * q_rs;
+      for (int64_t j = 0; j < Lk; ++j) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qi[d] * k[j * k_rs + d];
+        s[j] = scale * dot;
+      }
+      double mx = s[0];
+      for (int64_t j = 1; j < Lk; ++j) mx = s[j] > mx ? s[j] : mx;
+      double l = 0.0;
+      for (int e = 0; e < Dv; ++e) o[e] = 0.0;
+      for (int64_t j = 0; j < Lk; ++j) {
+        const double p = exp(s[j] - mx);
+        l += p;
+        for (int e = 0; e < Dv; ++e) o[e] += p * v[j * v_rs + e];
+      }
+      double dl = 0.0;
+      for (int e = 0; e < Dv; ++e) dl += dout[i * do_rs + e] * (o[e] / l);
+      lse[i] = mx + log(l);
+      delta[i] = dl;
+    }
+    free(s);
+    free(o);
+  }
+  if (failed) {
+    free(lse);
+    free(delta);
+    return ORACLE_ENOMEM;
+  }
+  /* pass 2: dq by rows */
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < Lq; ++i) {
+    const double* qi = q + i * q_rs;
+    double* dqi = dq + i * dq_rs;
+    for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+    for (int64_t j = 0; j < Lk; ++j) {
+      double dot = 0.0, dp = 0.0;
+      for (int d = 0; d < D; ++d) dot += qi[d] * k[j * k_rs + d];
+      for (int e = 0; e < Dv; ++e) dp += dout[i * do_rs + e] * v[j * v_rs + e];
+      const double ds = exp(scale * dot - lse[i]) * (dp - delta[i]);
+      for (int d = 0; d < D; ++d) dqi[d] += scale * ds * k[j * k_rs + d];
+    }
+  }
+  /* pass 3: dk and dv by keys */
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < Lk; ++j) {
+    const double* kj = k + j * k_rs;
+    double* dkj = dk + j * dk_rs;
+    double* dvj = dv + j * dv_rs;
+    for (int d = 0; d < D; ++d) dkj[d] = 0.0;
+    for (int e = 0; e < Dv; ++e) dvj[e] = 0.0;
+    for (int64_t i = 0; i < Lq; ++i) {
+      double dot = 0.0, dp = 0.0;
+      for (int d = 0; d < D; ++d) dot += q[i * q_rs + d] * kj[d];
+      for (int e = 0; e < Dv; ++e) dp += dout[i * do_rs + e] * v[j * v_rs + e];
+      const double p = exp(scale * dot - lse[i]);
+      const double ds = p * (dp - delta[i]);
+      for (int d = 0; d < D; ++d) dkj[d] += scale * ds * q[i * q_rs + d];
+      for (int e = 0; e < Dv; ++e) dvj[e] += p * dout[i * do_rs + e];
+    }
+  }
+  free(lse);
+  free(delta);
+  return ORACLE_OK;
+}
+
+/*
  * Pointwise projection y = x W ([P1] "Full self-attention" and "FLARE:
  * fixed-query latent routing": K = X W_K, V = X W_V with W in R^{C x C};
  * "FLARE++: dynamic token routing": the two extra projections of

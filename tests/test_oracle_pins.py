@@ -344,3 +344,85 @@ def test_op_count_ratio_matches_pages():
     assert costs.primitives(True) == (5, 3)
     assert abs(costs.mixer_op_ratio(256, 256) - 1.6) < 1e-12
     assert abs(costs.mixer_op_ratio(128, 64) - (5 * 128 + 3 * 64) / (3 * 128 + 2 * 64)) < 1e-12
+
+
+# ---------------------------------------------------------------- gradients
+# The encoder and decoder are standard SDPA calls ([P1] "FLARE: fixed-query
+# latent routing"), so training runs the standard SDPA gradient through each.
+
+def _torch_sdpa_grads(q, k, v, do, scale):
+    qt, kt, vt = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v)]
+    o = torch.nn.functional.scaled_dot_product_attention(qt[None], kt[None], vt[None], scale=scale)[0]
+    (o * torch.tensor(do, dtype=torch.float64)).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("Lq,Lk,D,Dv,scale", [(5, 7, 4, 3, None), (32, 300, 16, 16, 0.7),
+                                              (300, 17, 32, 32, None), (1, 1, 8, 8, 2.0)])
+def test_sdpa_backward_matches_library_autograd(Lq, Lk, D, Dv, scale):
+    rng = np.random.default_rng(Lq * 31 + Lk)
+    q, k = rng.standard_normal((Lq, D)) * 2, rng.standard_normal((Lk, D))
+    v, do = rng.standard_normal((Lk, Dv)), rng.standard_normal((Lq, Dv))
+    s = scale if scale is not None else 1 / np.sqrt(D)
+    got = oracle.sdpa_backward(q, k, v, do, scale)
+    ref = _torch_sdpa_grads(q, k, v, do, s)
+    for g, r in zip(got, ref):
+        assert np.max(np.abs(g - r)) <= 1e-12 * max(1.0, np.max(np.abs(r)))
+
+
+def test_sdpa_backward_invariants():
+    # shifting every key by one vector leaves each softmax row unchanged, so
+    # the key gradients sum to zero; each row's weights sum to 1, so the value
+    # gradients sum to the summed upstream gradient
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal((40, 16)) * 3, rng.standard_normal((90, 16))
+    v, do = rng.standard_normal((90, 8)), rng.standard_normal((40, 8))
+    _, dk, dv = oracle.sdpa_backward(q, k, v, do)
+    assert np.max(np.abs(dk.sum(0))) <= 1e-12 * np.max(np.abs(dk)) * 90
+    assert np.allclose(dv.sum(0), do.sum(0), rtol=0, atol=1e-12 * 90)
+
+
+def _flare_y(q, k, v, scale):
+    z, _ = oracle.encode(q, k, v, scale)
+    return oracle.decode(k, q, z, scale)
+
+
+def test_flare_backward_matches_finite_differences():
+    # central differences of sum(dy * Y) through both calls, on a tiny head
+    rng = np.random.default_rng(11)
+    B, H, N, M, D = 1, 1, 6, 3, 4
+    q = rng.standard_normal((H, M, D))
+    k, v = rng.standard_normal((B, H, N, D)), rng.standard_normal((B, H, N, D))
+    dy = rng.standard_normal((B, H, N, D))
+    scale = 0.8
+    dq, dk, dv = oracle.flare_encdec_backward(q, k, v, dy, scale)
+    f = lambda q_, k_, v_: float(np.sum(dy * _flare_y(q_, k_, v_, scale)))
+    eps = 1e-6
+    for arr, grad, idx in ((q, dq[0], (0, 1, 2)), (k, dk, (0, 0, 4, 1)), (v, dv, (0, 0, 2, 3)),
+                           (q, dq[0], (0, 2, 0)), (k, dk, (0, 0, 0, 3))):
+        plus, minus = arr.copy(), arr.copy()
+        plus[idx] += eps
+        minus[idx] -= eps
+        args_p = [plus if arr is a else a for a in (q, k, v)]
+        args_m = [minus if arr is a else a for a in (q, k, v)]
+        fd = (f(*args_p) - f(*args_m)) / (2 * eps)
+        assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd))
+
+
+def test_flare_backward_matches_library_autograd():
+    # torch fp64 autograd of Y = SDPA(K, Q, SDPA(Q, K, V)) with a batch-shared Q
+    rng = np.random.default_rng(5)
+    B, H, N, M, D = 2, 3, 50, 7, 16
+    q = rng.standard_normal((H, M, D)) * 2
+    k, v = rng.standard_normal((B, H, N, D)), rng.standard_normal((B, H, N, D))
+    dy = rng.standard_normal((B, H, N, D))
+    dq, dk, dv = oracle.flare_encdec_backward(q, k, v, dy)
+    qt = torch.tensor(q, requires_grad=True)
+    kt, vt = torch.tensor(k, requires_grad=True), torch.tensor(v, requires_grad=True)
+    qb = qt[None].expand(B, H, M, D)
+    sdpa = torch.nn.functional.scaled_dot_product_attention
+    y = sdpa(kt, qb, sdpa(qb, kt, vt))
+    (y * torch.tensor(dy)).sum().backward()
+    assert np.max(np.abs(dq.sum(0) - qt.grad.numpy())) <= 1e-11
+    assert np.max(np.abs(dk - kt.grad.numpy())) <= 1e-11
+    assert np.max(np.abs(dv - vt.grad.numpy())) <= 1e-11

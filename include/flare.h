@@ -124,12 +124,15 @@ flare_status flare_route_queries(const flare_tensor* seeds,
  *   K [B, H, N, D]  bf16 or fp32;  Q, Z [B, H, M, D] bf16 or fp32
  *   Y [B, H, N, D]  output, same dtype as K (token-major strides give the
  *                   concatenated-heads [B, N, H*D] layout directly)
+ *   lse [B, H, N]   optional fp32 output (contiguous), each token's natural-log
+ *                   normaliser log sum_m exp(scale k_n . q_m); NULL = skip.
+ *                   flare_decode_backward needs it.
  * Needs no workspace.
  */
 flare_status flare_decode(const flare_tensor* K, const flare_tensor* Q,
-                          const flare_tensor* Z, const flare_tensor* Y, int B,
-                          int H, int M, int64_t N, int D, float scale,
-                          unsigned flags, void* stream);
+                          const flare_tensor* Z, const flare_tensor* Y,
+                          float* lse, int B, int H, int M, int64_t N, int D,
+                          float scale, unsigned flags, void* stream);
 
 /*
  * Pointwise projections of one token matrix, Y_p = X W_p for p < n_proj
@@ -172,6 +175,50 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V,
                        int dtype, int B, int64_t N, int C, int H, int M,
                        float scale, unsigned flags, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the two calls.  Each call is standard SDPA ("FLARE:
+ * fixed-query latent routing"), so with s = scale q . k, P the softmax
+ * weights, o the output and do its gradient:
+ *   delta = do . o per query row,  dS = P (do . v - delta),
+ *   dq = scale sum dS k,  dk = scale sum dS q,  dv = sum P do.
+ * P is recomputed from the normaliser the forward call returned (lse).
+ * Token-side inputs (K, V, Y, dY) must be bf16; token-side gradients (dK,
+ * dV) are fp32 [B, H, N, D] views; latent-side gradients (dQ, dZ) are
+ * contiguous fp32 [B, H, M, D] arrays, one block per batch element (for a
+ * query block shared by the batch the caller sums them over b).
+ * FLARE_E_UNSUPPORTED for other dtypes.
+ */
+
+/* Decoder: gradients of Y = SDPA(K, Q, Z) given dY.  lse is flare_decode's
+ * [B, H, N] output for the same inputs.  Writes dK (overwrites), dQ, dZ. */
+size_t flare_decode_backward_workspace_size(int B, int H, int M, int64_t N,
+                                            int D);
+flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q,
+                                   const flare_tensor* Z, const flare_tensor* Y,
+                                   const float* lse, const flare_tensor* dY,
+                                   const flare_tensor* dK, float* dQ, float* dZ,
+                                   int B, int H, int M, int64_t N, int D,
+                                   float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Encoder (and FLARE++ query synthesis): gradients of Z = SDPA(Q, K, V)
+ * given dZ.  lse is flare_encode's [B, H, M] output.  Writes dQ, dK, dV;
+ * with FLARE_ACCUMULATE_DQ / FLARE_ACCUMULATE_DK in `accumulate` it adds to
+ * dQ / dK instead (the chain rule through the decoder and the encoder,
+ * which share Q and K). */
+#define FLARE_ACCUMULATE_DQ 1u
+#define FLARE_ACCUMULATE_DK 2u
+size_t flare_encode_backward_workspace_size(int B, int H, int M, int64_t N,
+                                            int D);
+flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
+                                   const flare_tensor* V, const flare_tensor* Z,
+                                   const float* lse, const float* dZ, float* dQ,
+                                   const flare_tensor* dK, const flare_tensor* dV,
+                                   unsigned accumulate, int B, int H, int M,
+                                   int64_t N, int D, float scale,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* Static text for a status code. */
 const char* flare_status_string(int status);

@@ -27,10 +27,15 @@ FLARE_F32 = 0
 FLARE_BF16 = 1
 FLARE_FLAG_EXACT_SOFTMAX = 1
 
+FLARE_ACCUMULATE_DQ = 1
+FLARE_ACCUMULATE_DK = 2
+
 EXPORTS = ("flare_encode_workspace_size", "flare_encode", "flare_route_queries",
            "flare_decode", "flare_project_workspace_size", "flare_project",
-           "flare_mix_workspace_size", "flare_mix", "flare_status_string",
-           "flare_version")
+           "flare_mix_workspace_size", "flare_mix",
+           "flare_decode_backward_workspace_size", "flare_decode_backward",
+           "flare_encode_backward_workspace_size", "flare_encode_backward",
+           "flare_status_string", "flare_version")
 
 
 class FlareError(RuntimeError):
@@ -65,7 +70,15 @@ def lib():
     L.flare_encode_workspace_size.restype = sz
     L.flare_encode.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
     L.flare_route_queries.argtypes = [T, T, T, T, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
-    L.flare_decode.argtypes = [T, T, T, T, i32, i32, i32, i64, i32, f32, u32, vp]
+    L.flare_decode.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp]
+    L.flare_decode_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32]
+    L.flare_decode_backward_workspace_size.restype = sz
+    L.flare_decode_backward.argtypes = [T, T, T, T, vp, T, T, vp, vp, i32, i32, i32, i64, i32, f32,
+                                        vp, sz, vp]
+    L.flare_encode_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32]
+    L.flare_encode_backward_workspace_size.restype = sz
+    L.flare_encode_backward.argtypes = [T, T, T, T, vp, vp, vp, T, T, u32, i32, i32, i32, i64, i32,
+                                        f32, vp, sz, vp]
     L.flare_project_workspace_size.argtypes = [i32, i32, i32]
     L.flare_project_workspace_size.restype = sz
     L.flare_project.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i32,
@@ -74,7 +87,8 @@ def lib():
     L.flare_mix_workspace_size.restype = sz
     L.flare_mix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32,
                             f32, u32, vp, sz, vp]
-    for f in ("flare_encode", "flare_route_queries", "flare_decode", "flare_project", "flare_mix"):
+    for f in ("flare_encode", "flare_route_queries", "flare_decode", "flare_project", "flare_mix",
+              "flare_decode_backward", "flare_encode_backward"):
         getattr(L, f).restype = ctypes.c_int
     L.flare_status_string.argtypes = [i32]
     L.flare_status_string.restype = ctypes.c_char_p
@@ -181,16 +195,64 @@ def flare_route_queries(seeds, ek, ev, qx=None, scale=0.0, flags=0, workspace=No
     return qx
 
 
-def flare_decode(k, q, z, y=None, scale=0.0, flags=0, stream=None):
-    """Y = SDPA(K, Q, Z); k [B, H, N, D]; q, z [B, H, M, D] or shared."""
+def flare_decode(k, q, z, y=None, scale=0.0, flags=0, stream=None, want_lse=False):
+    """Y = SDPA(K, Q, Z); k [B, H, N, D]; q, z [B, H, M, D] or shared.  Returns
+    y (and the per-token normaliser lse [B, H, N] fp32 when want_lse)."""
     B, H, N, D = _dims(k)
     M = q.shape[-2]
     if y is None:
         y = torch.empty((B, H, N, D), dtype=k.dtype, device=k.device)
-    s = lib().flare_decode(describe(k), describe(q), describe(z), describe(y), B, H, M, N, D,
-                           float(scale), int(flags), _stream(stream))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=k.device) if want_lse else None
+    s = lib().flare_decode(describe(k), describe(q), describe(z), describe(y),
+                           ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
+                           B, H, M, N, D, float(scale), int(flags), _stream(stream))
     _check(s, "flare_decode")
-    return y
+    return (y, lse) if want_lse else y
+
+
+def _f32_ptr(t):
+    assert t.dtype == torch.float32 and t.is_contiguous()
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def flare_decode_backward(k, q, z, y, lse, dy, dk=None, dq=None, dz=None, scale=0.0,
+                          workspace=None, stream=None):
+    """Gradients (dk [B, H, N, D] fp32, dq, dz [B, H, M, D] fp32) of
+    sum(dy * Y) for Y = flare_decode(k, q, z) with its lse."""
+    B, H, N, D = _dims(k)
+    M = q.shape[-2]
+    dev = k.device
+    dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    dq = dq if dq is not None else torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    dz = dz if dz is not None else torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    ws = _workspace(lib().flare_decode_backward_workspace_size(B, H, M, N, D), dev, workspace)
+    s = lib().flare_decode_backward(describe(k), describe(q), describe(z), describe(y), _f32_ptr(lse),
+                                    describe(dy), describe(dk), _f32_ptr(dq), _f32_ptr(dz),
+                                    B, H, M, N, D, float(scale), ctypes.c_void_p(ws.data_ptr()),
+                                    ws.numel() * ws.element_size(), _stream(stream))
+    _check(s, "flare_decode_backward")
+    return dk, dq, dz
+
+
+def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, accumulate=0,
+                          scale=0.0, workspace=None, stream=None):
+    """Gradients (dq [B, H, M, D] fp32, dk, dv [B, H, N, D] fp32) of sum(dz * Z)
+    for Z = flare_encode(q, k, v) with its lse; FLARE_ACCUMULATE_DQ / _DK in
+    ``accumulate`` add into the given dq / dk."""
+    B, H, N, D = _dims(k)
+    M = q.shape[-2]
+    dev = k.device
+    dq = dq if dq is not None else torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    ws = _workspace(lib().flare_encode_backward_workspace_size(B, H, M, N, D), dev, workspace)
+    s = lib().flare_encode_backward(describe(q), describe(k), describe(v), describe(z), _f32_ptr(lse),
+                                    _f32_ptr(dz), _f32_ptr(dq), describe(dk), describe(dv),
+                                    int(accumulate), B, H, M, N, D, float(scale),
+                                    ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                    _stream(stream))
+    _check(s, "flare_encode_backward")
+    return dq, dk, dv
 
 
 def project_workspace_size(C_in, C_out, n_proj) -> int:

@@ -113,9 +113,10 @@ flare_status encode_impl(const View& q, const View& k, const View& v, void* z, i
 }
 
 flare_status decode_impl(const View& k, const View& q, const View& z, void* y, int y_f32,
-                         int64_t y_sb, int64_t y_sh, int64_t y_sl, int B, int H, int M, int64_t N,
-                         int D, float c, unsigned flags, hipStream_t st) {
+                         int64_t y_sb, int64_t y_sh, int64_t y_sl, float* lse, int B, int H, int M,
+                         int64_t N, int D, float c, unsigned flags, hipStream_t st) {
   DecodeParams dp;
+  dp.lse = lse;
   dp.k = k;
   dp.q = q;
   dp.z = z;
@@ -135,6 +136,30 @@ flare_status decode_impl(const View& k, const View& q, const View& z, void* y, i
   }
   dp.tokens_per_block = plan_decode_bf16(B, H, M, N, D);  // workgroups per head
   return hip_status(launch_decode_bf16(dp, D, B, st));
+}
+
+float natural_scale(float scale, int D) { return scale == 0.0f ? 1.0f / std::sqrt((float)D) : scale; }
+
+bool f32_ptr_ok(const void* p) { return p && reinterpret_cast<uintptr_t>(p) % 4 == 0; }
+
+flare_status bwd_common_checks(int B, int H, int M, int64_t N, int D, float scale) {
+  if (!sizes_ok(B, H, M, N, D)) {
+    if (B >= 1 && H >= 1 && M >= 1 && N >= 1 && (M > kMaxM || !(D == 16 || D == 32)))
+      return FLARE_E_UNSUPPORTED;
+    return FLARE_E_INVALID;
+  }
+  if (!scale_ok(scale)) return FLARE_E_INVALID;
+  return FLARE_OK;
+}
+
+// Workgroups per head of the token-parallel backward pass (4 waves x 32
+// tokens per step): about 2048 in all.
+int64_t tok_bwd_blocks(int B, int H, int64_t N) {
+  const int64_t bh = (int64_t)B * H;
+  const int64_t steps = (N + 127) / 128;
+  int64_t per = (2048 + bh - 1) / bh;
+  if (per > steps) per = steps;
+  return per < 1 ? 1 : per;
 }
 
 bool proj_shape_ok(int64_t R, int Cin, int Cout, int n_proj) {
@@ -232,8 +257,8 @@ flare_status flare_route_queries(const flare_tensor* seeds, const flare_tensor* 
 }
 
 flare_status flare_decode(const flare_tensor* K, const flare_tensor* Q, const flare_tensor* Z,
-                          const flare_tensor* Y, int B, int H, int M, int64_t N, int D, float scale,
-                          unsigned flags, void* stream) {
+                          const flare_tensor* Y, float* lse, int B, int H, int M, int64_t N, int D,
+                          float scale, unsigned flags, void* stream) {
   if (!sizes_ok(B, H, M, N, D)) {
     if (B >= 1 && H >= 1 && M >= 1 && N >= 1 && (M > kMaxM || !(D == 16 || D == 32)))
       return FLARE_E_UNSUPPORTED;
@@ -242,8 +267,9 @@ flare_status flare_decode(const flare_tensor* K, const flare_tensor* Q, const fl
   if (!token_tensor_ok(K) || !latent_tensor_ok(Q) || !latent_tensor_ok(Z) || !token_tensor_ok(Y))
     return FLARE_E_INVALID;
   if (!scale_ok(scale) || (flags & ~FLARE_FLAG_EXACT_SOFTMAX)) return FLARE_E_INVALID;
+  if (lse && reinterpret_cast<uintptr_t>(lse) % 4) return FLARE_E_INVALID;
   return decode_impl(view_of(K), view_of(Q), view_of(Z), Y->data, Y->dtype == FLARE_F32, Y->stride_b,
-                     Y->stride_h, Y->stride_l, B, H, M, N, D, log2_scale(scale, D), flags,
+                     Y->stride_h, Y->stride_l, lse, B, H, M, N, D, log2_scale(scale, D), flags,
                      reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -389,7 +415,7 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V, const vo
   z.sl = lat_sl;
   // (d) Y = SDPA(K, Q, Z), heads concatenated into [B, N, C]
   void* ydst = has_wo ? (void*)(ws + L.y) : out;
-  s = decode_impl(head_major(kp), q, z, ydst, 0, N * C, D, C, B, H, M, N, D, c, flags, st);
+  s = decode_impl(head_major(kp), q, z, ydst, 0, N * C, D, C, nullptr, B, H, M, N, D, c, flags, st);
   if (s != FLARE_OK) return s;
   // (e) out = Y W_O
   if (has_wo) {
@@ -398,6 +424,167 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V, const vo
     s = project_impl(ws + L.y, wo, yo, 1, (int64_t)B * N, C, C, 0, B, D, ws + L.wosw, st);
   }
   return s;
+}
+
+// ---------------------------------------------------------------- backward
+
+size_t flare_decode_backward_workspace_size(int B, int H, int M, int64_t N, int D) {
+  if (!sizes_ok(B, H, M, N, D)) return 0;
+  const int S = plan_bwd_splits(B, H, M, N);
+  const size_t part = align_up((size_t)B * H * S * M * D * 4);
+  return align_up((size_t)B * H * N * 4) + 2 * part;
+}
+
+size_t flare_encode_backward_workspace_size(int B, int H, int M, int64_t N, int D) {
+  if (!sizes_ok(B, H, M, N, D)) return 0;
+  const int S = plan_bwd_splits(B, H, M, N);
+  return align_up((size_t)B * H * S * M * D * 4);
+}
+
+flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q, const flare_tensor* Z,
+                                   const flare_tensor* Y, const float* lse, const flare_tensor* dY,
+                                   const flare_tensor* dK, float* dQ, float* dZ, int B, int H, int M,
+                                   int64_t N, int D, float scale, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  flare_status v = bwd_common_checks(B, H, M, N, D, scale);
+  if (v != FLARE_OK) return v;
+  if (!token_tensor_ok(K) || !token_tensor_ok(Y) || !token_tensor_ok(dY) || !token_tensor_ok(dK) ||
+      !latent_tensor_ok(Q) || !latent_tensor_ok(Z))
+    return FLARE_E_INVALID;
+  if (K->dtype != FLARE_BF16 || Y->dtype != FLARE_BF16 || dY->dtype != FLARE_BF16 || dK->dtype != FLARE_F32)
+    return FLARE_E_UNSUPPORTED;
+  if (!f32_ptr_ok(lse) || !f32_ptr_ok(dQ) || !f32_ptr_ok(dZ)) return FLARE_E_INVALID;
+  const size_t need = flare_decode_backward_workspace_size(B, H, M, N, D);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return FLARE_E_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int S = plan_bwd_splits(B, H, M, N);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* delta = reinterpret_cast<float*>(ws);
+  float* dq_part = reinterpret_cast<float*>(ws + align_up((size_t)B * H * N * 4));
+  float* dz_part = dq_part + align_up((size_t)B * H * S * M * D * 4) / 4;
+
+  TokBwdParams tp;
+  std::memset(&tp, 0, sizeof(tp));
+  tp.k = view_of(K);
+  tp.x = view_of(dY);
+  tp.y = view_of(Y);
+  tp.q = view_of(Q);
+  tp.w = view_of(Z);
+  tp.z = tp.w;
+  tp.lse = lse;
+  tp.dk = reinterpret_cast<float*>(dK->data);
+  tp.dk_sb = dK->stride_b;
+  tp.dk_sh = dK->stride_h;
+  tp.dk_sl = dK->stride_l;
+  tp.delta = delta;
+  tp.H = H;
+  tp.M = M;
+  tp.N = N;
+  tp.c = log2_scale(scale, D);
+  tp.scale = natural_scale(scale, D);
+  tp.accumulate = 0;
+  tp.blocks_per_head = tok_bwd_blocks(B, H, N);
+  hipError_t e = launch_tok_bwd(tp, D, B, false, st);
+  if (e != hipSuccess) return FLARE_E_HIP;
+
+  LatBwdParams lp;
+  std::memset(&lp, 0, sizeof(lp));
+  lp.k = tp.k;
+  lp.x = tp.x;
+  lp.q = tp.q;
+  lp.w = tp.w;
+  lp.z = tp.w;
+  lp.lse = lse;
+  lp.delta = delta;
+  lp.dq_part = dq_part;
+  lp.dz_part = dz_part;
+  lp.H = H;
+  lp.M = M;
+  lp.S = S;
+  lp.N = N;
+  lp.c = tp.c;
+  if ((e = launch_lat_bwd(lp, D, B, false, st)) != hipSuccess) return FLARE_E_HIP;
+  if ((e = launch_sum_splits(dq_part, dQ, (int64_t)B * H, S, (int64_t)M * D, tp.scale, 0, st)) != hipSuccess)
+    return FLARE_E_HIP;
+  if ((e = launch_sum_splits(dz_part, dZ, (int64_t)B * H, S, (int64_t)M * D, 1.0f, 0, st)) != hipSuccess)
+    return FLARE_E_HIP;
+  return FLARE_OK;
+}
+
+flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K, const flare_tensor* V,
+                                   const flare_tensor* Z, const float* lse, const float* dZ, float* dQ,
+                                   const flare_tensor* dK, const flare_tensor* dV, unsigned accumulate,
+                                   int B, int H, int M, int64_t N, int D, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  flare_status v = bwd_common_checks(B, H, M, N, D, scale);
+  if (v != FLARE_OK) return v;
+  if (!token_tensor_ok(K) || !token_tensor_ok(V) || !token_tensor_ok(dK) || !token_tensor_ok(dV) ||
+      !latent_tensor_ok(Q) || !latent_tensor_ok(Z))
+    return FLARE_E_INVALID;
+  if (K->dtype != FLARE_BF16 || V->dtype != FLARE_BF16 || dK->dtype != FLARE_F32 || dV->dtype != FLARE_F32)
+    return FLARE_E_UNSUPPORTED;
+  if (!f32_ptr_ok(lse) || !f32_ptr_ok(dZ) || !f32_ptr_ok(dQ)) return FLARE_E_INVALID;
+  if (accumulate & ~(FLARE_ACCUMULATE_DQ | FLARE_ACCUMULATE_DK)) return FLARE_E_INVALID;
+  const size_t need = flare_encode_backward_workspace_size(B, H, M, N, D);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return FLARE_E_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int S = plan_bwd_splits(B, H, M, N);
+  float* dq_part = reinterpret_cast<float*>(workspace);
+
+  View dzv;
+  dzv.data = dZ;
+  dzv.is_f32 = 1;
+  dzv.sb = (int64_t)H * M * D;
+  dzv.sh = (int64_t)M * D;
+  dzv.sl = D;
+
+  LatBwdParams lp;
+  std::memset(&lp, 0, sizeof(lp));
+  lp.k = view_of(K);
+  lp.x = view_of(V);
+  lp.q = view_of(Q);
+  lp.w = dzv;
+  lp.z = view_of(Z);
+  lp.lse = lse;
+  lp.dq_part = dq_part;
+  lp.H = H;
+  lp.M = M;
+  lp.S = S;
+  lp.N = N;
+  lp.c = log2_scale(scale, D);
+  hipError_t e = launch_lat_bwd(lp, D, B, true, st);
+  if (e != hipSuccess) return FLARE_E_HIP;
+  if ((e = launch_sum_splits(dq_part, dQ, (int64_t)B * H, S, (int64_t)M * D, natural_scale(scale, D),
+                             (accumulate & FLARE_ACCUMULATE_DQ) ? 1 : 0, st)) != hipSuccess)
+    return FLARE_E_HIP;
+
+  TokBwdParams tp;
+  std::memset(&tp, 0, sizeof(tp));
+  tp.k = lp.k;
+  tp.x = lp.x;
+  tp.q = lp.q;
+  tp.w = dzv;
+  tp.z = lp.z;
+  tp.lse = lse;
+  tp.dk = reinterpret_cast<float*>(dK->data);
+  tp.dk_sb = dK->stride_b;
+  tp.dk_sh = dK->stride_h;
+  tp.dk_sl = dK->stride_l;
+  tp.dv = reinterpret_cast<float*>(dV->data);
+  tp.dv_sb = dV->stride_b;
+  tp.dv_sh = dV->stride_h;
+  tp.dv_sl = dV->stride_l;
+  tp.H = H;
+  tp.M = M;
+  tp.N = N;
+  tp.c = lp.c;
+  tp.scale = natural_scale(scale, D);
+  tp.accumulate = (accumulate & FLARE_ACCUMULATE_DK) ? 1 : 0;
+  tp.blocks_per_head = tok_bwd_blocks(B, H, N);
+  if ((e = launch_tok_bwd(tp, D, B, true, st)) != hipSuccess) return FLARE_E_HIP;
+  return FLARE_OK;
 }
 
 }  // extern "C"

@@ -265,6 +265,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
       pass(std::integral_constant<bool, true>());
     }
 
+    // Row normalisers (natural log) for the backward pass.
+    if (p.lse && h == 0) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int64_t n = base + 32 * tb + c;
+        if (n < n_end) p.lse[(int64_t)bh * p.N + n] = ((exact ? mx[tb] : 0.f) + __log2f(lsum[tb])) * kLn2;
+      }
+    }
     // Output: lane (h, c) holds token base + 32tb + c, features 16h .. 16h+15.
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -337,6 +345,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
     for (int d = 0; d < D; ++d) acc[d] = fmaf(pw, z_s[m * D + d], acc[d]);
   }
   const float inv = 1.0f / l;
+  if (p.lse) p.lse[(int64_t)blockIdx.y * p.N + n] = (mx + log2f(l)) * kLn2;
   const int64_t off = b * p.y_sb + h * p.y_sh + n * p.y_sl;
   if (p.y_f32) {
     float* yp = reinterpret_cast<float*>(p.y) + off;

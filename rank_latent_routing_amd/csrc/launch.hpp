@@ -46,6 +46,44 @@ struct DecodeParams {
   int64_t tokens_per_block;  // bf16 path: workgroups per head; fp32 path: tokens per workgroup
   float c;
   int exact;
+  float* lse;         // [B, H, N] natural-log row normalisers, may be null
+};
+
+// Backward, token-parallel pass (decoder layout): per token, dK (and dV).
+//   decode role: P = softmax over latents of the decoder, W = Z, X = dY;
+//                writes dK and delta_n = dY_n . Y_n.
+//   encode role: P = softmax over tokens of the encoder (per-latent
+//                normaliser), W = dZ, X = V; writes dK and dV.
+struct TokBwdParams {
+  View k, x, y;          // token-side bf16 [B, H, N, D]; y: decode role only
+  View q, w, z;          // latent-side [B, H, M, D]; z: encode role only
+  const float* lse;      // natural-log normalisers: [B, H, N] (decode) or [B, H, M] (encode)
+  float* dk;             // fp32 [B, H, N, D] view
+  int64_t dk_sb, dk_sh, dk_sl;
+  float* dv;             // encode role only
+  int64_t dv_sb, dv_sh, dv_sl;
+  float* delta;          // decode role: [B, H, N] written
+  int H, M;
+  int64_t N;
+  float c, scale;        // c = scale * log2(e)
+  int accumulate;        // add into dk instead of overwriting
+  int blocks_per_head;
+};
+
+// Backward, latent-parallel pass over token splits (encoder layout): per
+// latent, fp32 partial sums of dQ (and dZ) for each split.
+//   decode role: W = Z, X = dY, per-token normaliser and delta; dQ and dZ.
+//   encode role: W = dZ, X = V, per-latent normaliser; dQ.
+struct LatBwdParams {
+  View k, x;             // token-side bf16 [B, H, N, D]
+  View q, w, z;          // latent-side [B, H, M, D]; z: encode role only
+  const float* lse;      // [B, H, N] (decode) or [B, H, M] (encode), natural log
+  const float* delta;    // decode role: [B, H, N]
+  float* dq_part;        // [B*H, S, M, D]
+  float* dz_part;        // decode role only
+  int H, M, S;
+  int64_t N;
+  float c;
 };
 
 struct GemmParams {
@@ -76,6 +114,11 @@ hipError_t launch_merge(const MergeParams& p, int B, hipStream_t s);
 int64_t plan_decode_bf16(int B, int H, int M, int64_t N, int D);
 hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams& p, int D, int B, hipStream_t s);
+int plan_bwd_splits(int B, int H, int M, int64_t N);
+hipError_t launch_tok_bwd(const TokBwdParams& p, int D, int B, bool encode_role, hipStream_t s);
+hipError_t launch_lat_bwd(const LatBwdParams& p, int D, int B, bool encode_role, hipStream_t s);
+hipError_t launch_sum_splits(const float* part, float* out, int64_t BH, int S, int64_t MD, float factor,
+                             int accumulate, hipStream_t s);
 hipError_t launch_transpose_weights(const void* w, void* wt, int Cin, int Cout, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
 

@@ -289,3 +289,107 @@ def test_block_workload_full_size_sampled():
         Y[:, sl] = oracle.sdpa(K[rows, sl], Qh, Zh)
     ref = oracle.matmul(Y, f64(m["w_o"]))
     check_bf16(got[b][rows], ref, "FLARE++ block out (sampled)")
+
+
+# ---------------------------------------------------------------- backward
+# Gradients of the two SDPA calls (standard SDPA backward, recomputed from the
+# forward normalisers) against the oracle's fp64 gradients on the same
+# bf16-rounded inputs.
+
+BWD_CASES = [
+    # B, H, N, D, M, q_mult, layout, per-batch q
+    (1, 2, 1000, 32, 64, 1.0, "head", False),
+    (2, 3, 777, 32, 200, 4.0, "token", False),
+    (1, 2, 333, 16, 48, 2.0, "head", True),
+    (1, 1, 5000, 32, 256, 8.0, "head", False),
+    (2, 2, 64, 32, 17, 1.0, "token", True),
+    (1, 1, 1, 32, 32, 1.0, "head", False),
+    (1, 2, 3000, 16, 512, 2.0, "head", False),
+]
+
+
+def check_grad(got, ref, what, scale_ref):
+    """rel-L2 within the bf16 bar; a gradient that is exactly zero in real
+    arithmetic (one token: the softmax weight is 1 and dS = dP - delta
+    cancels) is held to 1e-2 of a well-scaled gradient of the same call."""
+    nr = float(np.linalg.norm(ref.ravel()))
+    if nr <= 1e-12 * float(np.linalg.norm(scale_ref.ravel())):
+        e = float(np.linalg.norm(got.ravel())) / float(np.linalg.norm(scale_ref.ravel()))
+        say(f"  {what}: zero in exact arithmetic, |got| / |scale| {e:.3e}")
+        assert e <= BF16_TOL, what
+    else:
+        check_bf16(got, ref, what)
+
+
+def _bwd_inputs(case):
+    B, H, N, D, M, qm, layout, pbq = case
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=N + 3 * M, q_mult=qm, per_batch_q=pbq)
+    g = inputs.normal_tensor((B, N, H, D), "bf16", seed=N + M + 7)
+    return x, g
+
+
+def _dev_view(t, layout):
+    """[B, N, H, D] CPU tensor -> device [B, H, N, D] view in the given layout."""
+    if layout == "head":
+        return hm(t).contiguous().to(DEV)
+    return hm(t.to(DEV))
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}H{}N{}D{}M{}-q{}-{}-pb{}".format(*c))
+def test_decode_backward(case):
+    B, H, N, D, M, qm, layout, pbq = case
+    say(f"case {case}")
+    x, dy_t = _bwd_inputs(case)
+    q = x["q"].to(DEV)
+    k = _dev_view(x["k"], layout)
+    zr = inputs.normal_tensor((B, H, M, D), "bf16", seed=M + 11)  # any latent values
+    z = zr.to(DEV)
+    dy = _dev_view(dy_t, layout)
+    y, lse = rl.flare_decode(k, q, z, want_lse=True)
+    dk, dq, dz = rl.flare_decode_backward(k, q, z, y, lse, dy)
+    torch.cuda.synchronize()
+    dkr, dqr, dzr = oracle.decode_backward(f64(hm(x["k"])), f64(x["q"]), f64(zr), f64(hm(dy_t)))
+    check_grad(f64(dk), dkr, "dK (decoder)", dzr)
+    check_grad(f64(dq), dqr, "dQ (decoder)", dzr)
+    check_bf16(f64(dz), dzr, "dZ (decoder)")
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}H{}N{}D{}M{}-q{}-{}-pb{}".format(*c))
+def test_encode_backward(case):
+    B, H, N, D, M, qm, layout, pbq = case
+    say(f"case {case}")
+    x, _ = _bwd_inputs(case)
+    q = x["q"].to(DEV)
+    k, v = _dev_view(x["k"], layout), _dev_view(x["v"], layout)
+    z, lse = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    dz = inputs.normal_tensor((B, H, M, D), "f32", seed=M + 5).to(DEV)
+    dq, dk, dv = rl.flare_encode_backward(q, k, v, z, lse, dz)
+    torch.cuda.synchronize()
+    dqr, dkr, dvr = oracle.encode_backward(f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"])), f64(dz))
+    check_grad(f64(dq), dqr, "dQ (encoder)", dvr)
+    check_grad(f64(dk), dkr, "dK (encoder)", dvr)
+    check_bf16(f64(dv), dvr, "dV (encoder)")
+
+
+@pytest.mark.parametrize("case", BWD_CASES[:5], ids=lambda c: "B{}H{}N{}D{}M{}-q{}-{}-pb{}".format(*c))
+def test_flare_backward_chain(case):
+    # the chain rule through both calls: decoder gradient first (its dZ drives
+    # the encoder's), the encoder's dQ and dK accumulated onto the decoder's
+    B, H, N, D, M, qm, layout, pbq = case
+    say(f"case {case}")
+    x, dy_t = _bwd_inputs(case)
+    q = x["q"].to(DEV)
+    k, v = _dev_view(x["k"], layout), _dev_view(x["v"], layout)
+    dy = _dev_view(dy_t, layout)
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True)
+    dk, dq, dz = rl.flare_decode_backward(k, q, z, y, lse_d, dy)
+    dq, dk, dv = rl.flare_encode_backward(q, k, v, z, lse_e, dz, dq=dq, dk=dk,
+                                          accumulate=rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK)
+    torch.cuda.synchronize()
+    dqr, dkr, dvr = oracle.flare_encdec_backward(f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"])),
+                                                 f64(hm(dy_t)))
+    check_bf16(f64(dq), dqr, "dQ")
+    check_bf16(f64(dk), dkr, "dK")
+    check_bf16(f64(dv), dvr, "dV")

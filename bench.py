@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-mix", action="store_true", help="skip the FLARE++ mixer measurement")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle sample")
     ap.add_argument("--y-layout", choices=("token", "head"), default="token")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -238,6 +239,49 @@ def main():
     if extra["parity_rel_l2"]["Z_head0"] > 1e-2 or extra["parity_rel_l2"]["Y_head0_64_tokens"] > 1e-2:
         print("bench.py: parity check failed", extra["parity_rel_l2"], file=sys.stderr)
         sys.exit(3)
+
+    if not args.no_bwd:
+        # Backward of the same encode + decode pair: decoder gradient (dK, dQ,
+        # dZ), then the encoder's (dQ, dK accumulated, dV), from the forward
+        # normalisers; fp32 gradients, upstream gradient ~ N(0, 1).
+        zf, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32, stream=stream)
+        yb, lse_d = rl.flare_decode(k, q, zf, want_lse=True, stream=stream)
+        dy = torch.randn((B, H, N, D), generator=torch.Generator(device=dev).manual_seed(0), device=dev,
+                         dtype=torch.float32).to(torch.bfloat16)
+        dk_b = torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+        dv_b = torch.empty_like(dk_b)
+        dq_b = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+        dz_b = torch.empty_like(dq_b)
+        wsd = torch.empty(rl.lib().flare_decode_backward_workspace_size(B, H, M, N, D), dtype=torch.uint8,
+                          device=dev)
+        wse = torch.empty(rl.lib().flare_encode_backward_workspace_size(B, H, M, N, D), dtype=torch.uint8,
+                          device=dev)
+        acc = rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK
+
+        def backward():
+            rl.flare_decode_backward(k, q, zf, yb, lse_d, dy, dk=dk_b, dq=dq_b, dz=dz_b, workspace=wsd,
+                                     stream=stream)
+            rl.flare_encode_backward(q, k, v, zf, lse_e, dz_b, dq=dq_b, dk=dk_b, dv=dv_b, accumulate=acc,
+                                     workspace=wse, stream=stream)
+        for _ in range(max(2, args.warmup // 2)):
+            backward()
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bsteps = max(3, args.steps // 2)
+        b0.record(stream)
+        for _ in range(bsteps):
+            backward()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bms = b0.elapsed_time(b1) / bsteps
+        bwk = costs.encdec_backward(B, H, N, M, D)
+        extra["encdec_backward"] = {
+            "config": "gradients of FLARE encode+decode (dQ, dK, dV) at the bench sizes, bf16 inputs, "
+                      "fp32 gradients",
+            "ms": round(bms, 4), "tokens_per_s": tokens / (bms / 1e3),
+            "tflops": round(bwk.flops / (bms / 1e3) / 1e12, 1),
+            "over_forward": round(bms / ms_step, 3)}
+        del zf, yb, dy, dk_b, dv_b, dq_b, dz_b, wsd, wse
 
     if not args.no_mix:
         # FLARE++ forward mixer at the same sizes: C = 256, all projections.

@@ -80,3 +80,15 @@ def mixer_op_ratio(C: int, M: int) -> float:
     p1, c1 = primitives(False)
     p2, c2 = primitives(True)
     return (p2 * C * C + c2 * M * C) / (p1 * C * C + c1 * M * C)
+
+
+def encdec_backward(B, H, N, M, D, elem=BF16) -> Work:
+    """Gradients of one FLARE encode + decode pair: each SDPA call's backward
+    is five products of 2 N M D flops (scores recomputed, dP, dq, dk, dv) and
+    N M exponentials; bytes are the token-side reads (K, V, Y, dY) and writes
+    (dK, dV in fp32) per (token, head)."""
+    per = B * H * N
+    flops = 2 * 5 * 2.0 * M * D * per
+    exps = 2.0 * M * per
+    bytes_ = per * D * (4 * elem + 2 * 4)
+    return Work(flops, exps, bytes_)

@@ -261,7 +261,7 @@ def main():
         def backward():
             rl.flare_decode_backward(k, q, zf, yb, lse_d, dy, dk=dk_b, dq=dq_b, dz=dz_b, workspace=wsd,
                                      stream=stream)
-            rl.flare_encode_backward(q, k, v, zf, lse_e, dz_b, dq=dq_b, dk=dk_b, dv=dv_b, accumulate=acc,
+            rl.flare_encode_backward(q, k, v, zf, lse_e, dz_b, dq=dq_b, dk=dk_b, dv=dv_b, flags=acc,
                                      workspace=wse, stream=stream)
         for _ in range(max(2, args.warmup // 2)):
             backward()

@@ -107,13 +107,16 @@ flare_status flare_encode(const flare_tensor* Q, const flare_tensor* K,
  * ("FLARE++: dynamic token routing", equation 8): the same encoder with the
  * learned seeds as queries.  seeds [H, M, D] (stride_b normally 0);
  * eK, eV [B, H, N, D]; Qx [B, H, M, D] output (fp32 keeps the synthesized
- * queries unrounded for the encode/decode that follow).
+ * queries unrounded for the encode/decode that follow); lse [B, H, M]
+ * optional fp32 output as in flare_encode (flare_encode_backward needs it),
+ * NULL = skip.
  */
 flare_status flare_route_queries(const flare_tensor* seeds,
                                  const flare_tensor* eK,
                                  const flare_tensor* eV,
-                                 const flare_tensor* Qx, int B, int H, int M,
-                                 int64_t N, int D, float scale, unsigned flags,
+                                 const flare_tensor* Qx, float* lse, int B,
+                                 int H, int M, int64_t N, int D, float scale,
+                                 unsigned flags,
                                  void* workspace, size_t workspace_bytes,
                                  void* stream);
 
@@ -178,44 +181,55 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V,
 
 /*
  * Backward of the two calls.  Each call is standard SDPA ("FLARE:
- * fixed-query latent routing"), so with s = scale q . k, P the softmax
- * weights, o the output and do its gradient:
+ * fixed-query latent routing"; the query synthesis of "FLARE++: dynamic
+ * token routing", equation 8, is the encoder again), so with
+ * s = scale q . k, P the softmax weights, o the output and do its gradient:
  *   delta = do . o per query row,  dS = P (do . v - delta),
  *   dq = scale sum dS k,  dk = scale sum dS q,  dv = sum P do.
  * P is recomputed from the normaliser the forward call returned (lse).
  * Token-side inputs (K, V, Y, dY) must be bf16; token-side gradients (dK,
- * dV) are fp32 [B, H, N, D] views; latent-side gradients (dQ, dZ) are
- * contiguous fp32 [B, H, M, D] arrays, one block per batch element (for a
- * query block shared by the batch the caller sums them over b).
- * FLARE_E_UNSUPPORTED for other dtypes.
+ * dV) are fp32 [B, H, N, D] views; dZ and dQ are contiguous fp32 arrays,
+ * dZ [B, H, M, D], dQ [B, H, M, D] or, with FLARE_SUM_DQ_OVER_BATCH, [H, M, D]
+ * holding the sum over the batch (the gradient of a query block shared by
+ * the batch: FLARE's learned queries, FLARE++'s seeds).
+ * FLARE_E_UNSUPPORTED for other dtypes; FLARE_E_INVALID for unknown flags.
+ * Flags:
+ *   FLARE_ACCUMULATE_DQ      add into dQ instead of overwriting it
+ *   FLARE_ACCUMULATE_DK      add into dK instead of overwriting it
+ *   FLARE_SUM_DQ_OVER_BATCH  dQ is [H, M, D] and receives the sum over b
+ * The first two carry the chain rule through a decoder and an encoder that
+ * share Q and K.  Calls on one stream are ordered; accumulation assumes no
+ * other call writes the same dQ / dK concurrently.
  */
+#define FLARE_ACCUMULATE_DQ 1u
+#define FLARE_ACCUMULATE_DK 2u
+#define FLARE_SUM_DQ_OVER_BATCH 4u
 
 /* Decoder: gradients of Y = SDPA(K, Q, Z) given dY.  lse is flare_decode's
- * [B, H, N] output for the same inputs.  Writes dK (overwrites), dQ, dZ. */
+ * [B, H, N] output for the same inputs.  Writes dK, dQ (per the flags) and
+ * dZ (always overwritten). */
 size_t flare_decode_backward_workspace_size(int B, int H, int M, int64_t N,
                                             int D);
 flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q,
                                    const flare_tensor* Z, const flare_tensor* Y,
                                    const float* lse, const flare_tensor* dY,
                                    const flare_tensor* dK, float* dQ, float* dZ,
-                                   int B, int H, int M, int64_t N, int D,
-                                   float scale, void* workspace,
-                                   size_t workspace_bytes, void* stream);
+                                   unsigned flags, int B, int H, int M,
+                                   int64_t N, int D, float scale,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
-/* Encoder (and FLARE++ query synthesis): gradients of Z = SDPA(Q, K, V)
- * given dZ.  lse is flare_encode's [B, H, M] output.  Writes dQ, dK, dV;
- * with FLARE_ACCUMULATE_DQ / FLARE_ACCUMULATE_DK in `accumulate` it adds to
- * dQ / dK instead (the chain rule through the decoder and the encoder,
- * which share Q and K). */
-#define FLARE_ACCUMULATE_DQ 1u
-#define FLARE_ACCUMULATE_DK 2u
+/* Encoder and FLARE++ query synthesis: gradients of Z = SDPA(Q, K, V) given
+ * dZ.  lse is the [B, H, M] output of the forward call (flare_encode or
+ * flare_route_queries).  Writes dQ and dK per the flags and dV (always
+ * overwritten). */
 size_t flare_encode_backward_workspace_size(int B, int H, int M, int64_t N,
                                             int D);
 flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
                                    const flare_tensor* V, const flare_tensor* Z,
                                    const float* lse, const float* dZ, float* dQ,
                                    const flare_tensor* dK, const flare_tensor* dV,
-                                   unsigned accumulate, int B, int H, int M,
+                                   unsigned flags, int B, int H, int M,
                                    int64_t N, int D, float scale,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);

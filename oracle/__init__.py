@@ -191,6 +191,21 @@ def flare_encdec_backward(q, k, v, dy, scale=None):
     return dq1 + dq2, dk1 + dk2, dv
 
 
+def flarepp_backward(seeds, ek, ev, k, v, dy, scale=None):
+    """Gradients of sum(dy * Y) for FLARE++'s three calls ([P1] "FLARE++:
+    dynamic token routing", equation 8, then "FLARE: fixed-query latent
+    routing"): Q(X) = SDPA(seeds, eK, eV), Z = SDPA(Q(X), K, V),
+    Y = SDPA(K, Q(X), Z), with seeds [H, M, D] shared by the batch and
+    head-major ek, ev, k, v, dy [B, H, N, D].  The chain rule: the decoder
+    and the encoder give dQ(X), dK, dV as in flare_encdec_backward; dQ(X)
+    drives the synthesis gradient, whose seed part is summed over the batch.
+    Returns (dseeds [H, M, D], dek, dev, dk, dv)."""
+    qx, _ = encode(seeds, ek, ev, scale)
+    dqx, dk, dv = flare_encdec_backward(qx, k, v, dy, scale)
+    dseeds_b, dek, dev = encode_backward(seeds, ek, ev, dqx, scale)
+    return dseeds_b.sum(0), dek, dev, dk, dv
+
+
 def matmul(x, w):
     """y = x W for x [R, Cin], W [Cin, Cout] (pointwise projection)."""
     x, w = _f64(x), _f64(w)

@@ -29,6 +29,7 @@ FLARE_FLAG_EXACT_SOFTMAX = 1
 
 FLARE_ACCUMULATE_DQ = 1
 FLARE_ACCUMULATE_DK = 2
+FLARE_SUM_DQ_OVER_BATCH = 4
 
 EXPORTS = ("flare_encode_workspace_size", "flare_encode", "flare_route_queries",
            "flare_decode", "flare_project_workspace_size", "flare_project",
@@ -69,12 +70,12 @@ def lib():
     L.flare_encode_workspace_size.argtypes = [i32, i32, i32, i64, i32]
     L.flare_encode_workspace_size.restype = sz
     L.flare_encode.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
-    L.flare_route_queries.argtypes = [T, T, T, T, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
+    L.flare_route_queries.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
     L.flare_decode.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp]
     L.flare_decode_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32]
     L.flare_decode_backward_workspace_size.restype = sz
-    L.flare_decode_backward.argtypes = [T, T, T, T, vp, T, T, vp, vp, i32, i32, i32, i64, i32, f32,
-                                        vp, sz, vp]
+    L.flare_decode_backward.argtypes = [T, T, T, T, vp, T, T, vp, vp, u32, i32, i32, i32, i64, i32,
+                                        f32, vp, sz, vp]
     L.flare_encode_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32]
     L.flare_encode_backward_workspace_size.restype = sz
     L.flare_encode_backward.argtypes = [T, T, T, T, vp, vp, vp, T, T, u32, i32, i32, i32, i64, i32,
@@ -180,19 +181,22 @@ def flare_encode(q, k, v, z=None, want_lse=False, scale=0.0, flags=0, workspace=
 
 
 def flare_route_queries(seeds, ek, ev, qx=None, scale=0.0, flags=0, workspace=None,
-                        stream=None):
-    """Q(X) = SDPA(seeds, eK, eV); seeds [H, M, D]; returns qx [B, H, M, D] fp32."""
+                        stream=None, want_lse=False):
+    """Q(X) = SDPA(seeds, eK, eV); seeds [H, M, D]; returns qx [B, H, M, D] fp32
+    (and the per-query normaliser lse [B, H, M] fp32 when want_lse)."""
     B, H, N, D = _dims(ek)
     M = seeds.shape[-2]
     if qx is None:
         qx = torch.empty((B, H, M, D), dtype=torch.float32, device=ek.device)
+    lse = torch.empty((B, H, M), dtype=torch.float32, device=ek.device) if want_lse else None
     ws = _workspace(encode_workspace_size(B, H, M, N, D), ek.device, workspace)
     s = lib().flare_route_queries(describe(seeds), describe(ek), describe(ev), describe(qx),
+                                  ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
                                   B, H, M, N, D, float(scale), int(flags),
                                   ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                   _stream(stream))
     _check(s, "flare_route_queries")
-    return qx
+    return (qx, lse) if want_lse else qx
 
 
 def flare_decode(k, q, z, y=None, scale=0.0, flags=0, stream=None, want_lse=False):
@@ -215,40 +219,49 @@ def _f32_ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def flare_decode_backward(k, q, z, y, lse, dy, dk=None, dq=None, dz=None, scale=0.0,
+def _dq_shape(B, H, M, D, flags):
+    return (H, M, D) if flags & FLARE_SUM_DQ_OVER_BATCH else (B, H, M, D)
+
+
+def flare_decode_backward(k, q, z, y, lse, dy, dk=None, dq=None, dz=None, flags=0, scale=0.0,
                           workspace=None, stream=None):
     """Gradients (dk [B, H, N, D] fp32, dq, dz [B, H, M, D] fp32) of
-    sum(dy * Y) for Y = flare_decode(k, q, z) with its lse."""
+    sum(dy * Y) for Y = flare_decode(k, q, z) with its lse.  ``flags``:
+    FLARE_ACCUMULATE_DQ / _DK add into the given dq / dk;
+    FLARE_SUM_DQ_OVER_BATCH makes dq [H, M, D], summed over the batch."""
     B, H, N, D = _dims(k)
     M = q.shape[-2]
     dev = k.device
     dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
-    dq = dq if dq is not None else torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    dq = dq if dq is not None else torch.empty(_dq_shape(B, H, M, D, flags), dtype=torch.float32,
+                                               device=dev)
     dz = dz if dz is not None else torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
     ws = _workspace(lib().flare_decode_backward_workspace_size(B, H, M, N, D), dev, workspace)
     s = lib().flare_decode_backward(describe(k), describe(q), describe(z), describe(y), _f32_ptr(lse),
                                     describe(dy), describe(dk), _f32_ptr(dq), _f32_ptr(dz),
-                                    B, H, M, N, D, float(scale), ctypes.c_void_p(ws.data_ptr()),
+                                    int(flags), B, H, M, N, D, float(scale), ctypes.c_void_p(ws.data_ptr()),
                                     ws.numel() * ws.element_size(), _stream(stream))
     _check(s, "flare_decode_backward")
     return dk, dq, dz
 
 
-def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, accumulate=0,
+def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, flags=0,
                           scale=0.0, workspace=None, stream=None):
     """Gradients (dq [B, H, M, D] fp32, dk, dv [B, H, N, D] fp32) of sum(dz * Z)
-    for Z = flare_encode(q, k, v) with its lse; FLARE_ACCUMULATE_DQ / _DK in
-    ``accumulate`` add into the given dq / dk."""
+    for Z = flare_encode(q, k, v) (or flare_route_queries) with its lse.
+    ``flags``: FLARE_ACCUMULATE_DQ / _DK add into the given dq / dk;
+    FLARE_SUM_DQ_OVER_BATCH makes dq [H, M, D], summed over the batch."""
     B, H, N, D = _dims(k)
     M = q.shape[-2]
     dev = k.device
-    dq = dq if dq is not None else torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    dq = dq if dq is not None else torch.empty(_dq_shape(B, H, M, D, flags), dtype=torch.float32,
+                                               device=dev)
     dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
     dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
     ws = _workspace(lib().flare_encode_backward_workspace_size(B, H, M, N, D), dev, workspace)
     s = lib().flare_encode_backward(describe(q), describe(k), describe(v), describe(z), _f32_ptr(lse),
                                     _f32_ptr(dz), _f32_ptr(dq), describe(dk), describe(dv),
-                                    int(accumulate), B, H, M, N, D, float(scale),
+                                    int(flags), B, H, M, N, D, float(scale),
                                     ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                     _stream(stream))
     _check(s, "flare_encode_backward")

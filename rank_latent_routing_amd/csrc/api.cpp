@@ -142,6 +142,8 @@ float natural_scale(float scale, int D) { return scale == 0.0f ? 1.0f / std::sqr
 
 bool f32_ptr_ok(const void* p) { return p && reinterpret_cast<uintptr_t>(p) % 4 == 0; }
 
+constexpr unsigned kBwdFlags = FLARE_ACCUMULATE_DQ | FLARE_ACCUMULATE_DK | FLARE_SUM_DQ_OVER_BATCH;
+
 flare_status bwd_common_checks(int B, int H, int M, int64_t N, int D, float scale) {
   if (!sizes_ok(B, H, M, N, D)) {
     if (B >= 1 && H >= 1 && M >= 1 && N >= 1 && (M > kMaxM || !(D == 16 || D == 32)))
@@ -249,10 +251,10 @@ flare_status flare_encode(const flare_tensor* Q, const flare_tensor* K, const fl
 }
 
 flare_status flare_route_queries(const flare_tensor* seeds, const flare_tensor* eK,
-                                 const flare_tensor* eV, const flare_tensor* Qx, int B, int H,
-                                 int M, int64_t N, int D, float scale, unsigned flags,
+                                 const flare_tensor* eV, const flare_tensor* Qx, float* lse, int B,
+                                 int H, int M, int64_t N, int D, float scale, unsigned flags,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-  return encode_checked(seeds, eK, eV, Qx, nullptr, B, H, M, N, D, scale, flags, workspace,
+  return encode_checked(seeds, eK, eV, Qx, lse, B, H, M, N, D, scale, flags, workspace,
                         workspace_bytes, stream);
 }
 
@@ -443,9 +445,9 @@ size_t flare_encode_backward_workspace_size(int B, int H, int M, int64_t N, int 
 
 flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q, const flare_tensor* Z,
                                    const flare_tensor* Y, const float* lse, const flare_tensor* dY,
-                                   const flare_tensor* dK, float* dQ, float* dZ, int B, int H, int M,
-                                   int64_t N, int D, float scale, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
+                                   const flare_tensor* dK, float* dQ, float* dZ, unsigned flags, int B,
+                                   int H, int M, int64_t N, int D, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
   flare_status v = bwd_common_checks(B, H, M, N, D, scale);
   if (v != FLARE_OK) return v;
   if (!token_tensor_ok(K) || !token_tensor_ok(Y) || !token_tensor_ok(dY) || !token_tensor_ok(dK) ||
@@ -454,6 +456,7 @@ flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q,
   if (K->dtype != FLARE_BF16 || Y->dtype != FLARE_BF16 || dY->dtype != FLARE_BF16 || dK->dtype != FLARE_F32)
     return FLARE_E_UNSUPPORTED;
   if (!f32_ptr_ok(lse) || !f32_ptr_ok(dQ) || !f32_ptr_ok(dZ)) return FLARE_E_INVALID;
+  if (flags & ~kBwdFlags) return FLARE_E_INVALID;
   const size_t need = flare_decode_backward_workspace_size(B, H, M, N, D);
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
     return FLARE_E_WORKSPACE;
@@ -483,7 +486,7 @@ flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q,
   tp.N = N;
   tp.c = log2_scale(scale, D);
   tp.scale = natural_scale(scale, D);
-  tp.accumulate = 0;
+  tp.accumulate = (flags & FLARE_ACCUMULATE_DK) ? 1 : 0;
   tp.blocks_per_head = tok_bwd_blocks(B, H, N);
   hipError_t e = launch_tok_bwd(tp, D, B, false, st);
   if (e != hipSuccess) return FLARE_E_HIP;
@@ -505,16 +508,17 @@ flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q,
   lp.N = N;
   lp.c = tp.c;
   if ((e = launch_lat_bwd(lp, D, B, false, st)) != hipSuccess) return FLARE_E_HIP;
-  if ((e = launch_sum_splits(dq_part, dQ, (int64_t)B * H, S, (int64_t)M * D, tp.scale, 0, st)) != hipSuccess)
+  if ((e = launch_sum_splits(dq_part, dQ, B, H, S, (int64_t)M * D, (flags & FLARE_SUM_DQ_OVER_BATCH) != 0,
+                             tp.scale, (flags & FLARE_ACCUMULATE_DQ) ? 1 : 0, st)) != hipSuccess)
     return FLARE_E_HIP;
-  if ((e = launch_sum_splits(dz_part, dZ, (int64_t)B * H, S, (int64_t)M * D, 1.0f, 0, st)) != hipSuccess)
+  if ((e = launch_sum_splits(dz_part, dZ, B, H, S, (int64_t)M * D, false, 1.0f, 0, st)) != hipSuccess)
     return FLARE_E_HIP;
   return FLARE_OK;
 }
 
 flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K, const flare_tensor* V,
                                    const flare_tensor* Z, const float* lse, const float* dZ, float* dQ,
-                                   const flare_tensor* dK, const flare_tensor* dV, unsigned accumulate,
+                                   const flare_tensor* dK, const flare_tensor* dV, unsigned flags,
                                    int B, int H, int M, int64_t N, int D, float scale, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   flare_status v = bwd_common_checks(B, H, M, N, D, scale);
@@ -525,7 +529,7 @@ flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
   if (K->dtype != FLARE_BF16 || V->dtype != FLARE_BF16 || dK->dtype != FLARE_F32 || dV->dtype != FLARE_F32)
     return FLARE_E_UNSUPPORTED;
   if (!f32_ptr_ok(lse) || !f32_ptr_ok(dZ) || !f32_ptr_ok(dQ)) return FLARE_E_INVALID;
-  if (accumulate & ~(FLARE_ACCUMULATE_DQ | FLARE_ACCUMULATE_DK)) return FLARE_E_INVALID;
+  if (flags & ~kBwdFlags) return FLARE_E_INVALID;
   const size_t need = flare_encode_backward_workspace_size(B, H, M, N, D);
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
     return FLARE_E_WORKSPACE;
@@ -556,8 +560,9 @@ flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
   lp.c = log2_scale(scale, D);
   hipError_t e = launch_lat_bwd(lp, D, B, true, st);
   if (e != hipSuccess) return FLARE_E_HIP;
-  if ((e = launch_sum_splits(dq_part, dQ, (int64_t)B * H, S, (int64_t)M * D, natural_scale(scale, D),
-                             (accumulate & FLARE_ACCUMULATE_DQ) ? 1 : 0, st)) != hipSuccess)
+  if ((e = launch_sum_splits(dq_part, dQ, B, H, S, (int64_t)M * D, (flags & FLARE_SUM_DQ_OVER_BATCH) != 0,
+                             natural_scale(scale, D), (flags & FLARE_ACCUMULATE_DQ) ? 1 : 0, st)) !=
+      hipSuccess)
     return FLARE_E_HIP;
 
   TokBwdParams tp;
@@ -581,7 +586,7 @@ flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
   tp.N = N;
   tp.c = lp.c;
   tp.scale = natural_scale(scale, D);
-  tp.accumulate = (accumulate & FLARE_ACCUMULATE_DK) ? 1 : 0;
+  tp.accumulate = (flags & FLARE_ACCUMULATE_DK) ? 1 : 0;
   tp.blocks_per_head = tok_bwd_blocks(B, H, N);
   if ((e = launch_tok_bwd(tp, D, B, true, st)) != hipSuccess) return FLARE_E_HIP;
   return FLARE_OK;

@@ -377,16 +377,33 @@ __global__ __launch_bounds__(64 * NW) void lat_bwd_kernel(LatBwdParams p) {
   }
 }
 
-// out[bh, e] = (accumulate ? out[bh, e] : 0) + factor * sum_s part[bh, s, e]
+// out[r, e] = (accumulate ? out[r, e] : 0) + factor * sum_{b < nb} sum_s part[r, b, s, e],
+// with part[r, b, s, e] at (r S + s) MD + b bstride + e: one (batch, head)
+// row per r when nb = 1, or for a query block shared by the batch one head
+// per r with the batch summed (nb = B, bstride = H S MD).  A workgroup covers
+// 64 consecutive e of one r with four split groups (each thread takes every
+// fourth split, coalesced across the 64 lanes), combined through LDS.
 __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part, float* __restrict__ out,
-                                                         int64_t BH, int S, int64_t MD, float factor, int accumulate) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= BH * MD) return;
-  const int64_t bh = idx / MD, e = idx - bh * MD;
-  const float* ps = part + bh * S * MD + e;
+                                                         int S, int64_t MD, int nb, int64_t bstride, float factor,
+                                                         int accumulate) {
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int64_t r = blockIdx.y;
+  const int64_t e = (int64_t)blockIdx.x * 64 + lane;
   float acc = 0.f;
-  for (int s = 0; s < S; ++s) acc += ps[(int64_t)s * MD];
-  out[idx] = (accumulate ? out[idx] : 0.f) + factor * acc;
+  if (e < MD) {
+    for (int bi = 0; bi < nb; ++bi) {
+      const float* ps = part + r * S * MD + bi * bstride + e;
+      for (int s = grp; s < S; s += 4) acc += ps[(int64_t)s * MD];
+    }
+  }
+  red[grp][lane] = acc;
+  __syncthreads();
+  if (grp == 0 && e < MD) {
+    const float sum = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    const int64_t idx = r * MD + e;
+    out[idx] = (accumulate ? out[idx] : 0.f) + factor * sum;
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -446,11 +463,13 @@ hipError_t launch_lat_bwd(const LatBwdParams& p, int D, int B, bool encode_role,
   return hipGetLastError();
 }
 
-hipError_t launch_sum_splits(const float* part, float* out, int64_t BH, int S, int64_t MD, float factor,
-                             int accumulate, hipStream_t st) {
-  const int64_t total = BH * MD;
-  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part, out, BH, S,
-                     MD, factor, accumulate);
+hipError_t launch_sum_splits(const float* part, float* out, int B, int H, int S, int64_t MD, bool batch_sum,
+                             float factor, int accumulate, hipStream_t st) {
+  const int64_t rows = batch_sum ? H : (int64_t)B * H;
+  const int nb = batch_sum ? B : 1;
+  const int64_t bstride = (int64_t)H * S * MD;
+  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((MD + 63) / 64), (unsigned)rows), dim3(256), 0, st, part,
+                     out, S, MD, nb, bstride, factor, accumulate);
   return hipGetLastError();
 }
 

@@ -117,8 +117,8 @@ hipError_t launch_decode_f32(const DecodeParams& p, int D, int B, hipStream_t s)
 int plan_bwd_splits(int B, int H, int M, int64_t N);
 hipError_t launch_tok_bwd(const TokBwdParams& p, int D, int B, bool encode_role, hipStream_t s);
 hipError_t launch_lat_bwd(const LatBwdParams& p, int D, int B, bool encode_role, hipStream_t s);
-hipError_t launch_sum_splits(const float* part, float* out, int64_t BH, int S, int64_t MD, float factor,
-                             int accumulate, hipStream_t s);
+hipError_t launch_sum_splits(const float* part, float* out, int B, int H, int S, int64_t MD, bool batch_sum,
+                             float factor, int accumulate, hipStream_t st);
 hipError_t launch_transpose_weights(const void* w, void* wt, int Cin, int Cout, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
 

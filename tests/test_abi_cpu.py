@@ -93,7 +93,7 @@ def test_decode_and_route_reject_bad_arguments():
                           None) == fb.FLARE_E_INVALID
     assert L.flare_decode(r(ok), r(ok), r(ok), r(ok), ctypes.c_void_p(FAKE + 2), 1, 1, 8, 10, 32, 0.0,
                           0, None) == fb.FLARE_E_INVALID
-    assert L.flare_route_queries(r(ok), r(ok), r(ok), r(ok), 1, 1, 8, 10, 32, 0.0, 0, None, 0,
+    assert L.flare_route_queries(r(ok), r(ok), r(ok), r(ok), None, 1, 1, 8, 10, 32, 0.0, 0, None, 0,
                                  None) == fb.FLARE_E_WORKSPACE
 
 
@@ -146,19 +146,22 @@ def test_backward_calls_reject_bad_arguments():
     need = L.flare_decode_backward_workspace_size(1, 1, 8, 10, 32)
     assert need > 0 and L.flare_encode_backward_workspace_size(1, 1, 8, 10, 32) > 0
     # token-side inputs must be bf16, token-side gradients fp32
-    assert L.flare_decode_backward(r(f32), r(ok), r(ok), r(ok), p, r(ok), r(f32), p, p, 1, 1, 8, 10, 32,
+    assert L.flare_decode_backward(r(f32), r(ok), r(ok), r(ok), p, r(ok), r(f32), p, p, 0, 1, 1, 8, 10, 32,
                                    0.0, ws, need, None) == fb.FLARE_E_UNSUPPORTED
-    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), p, r(ok), r(ok), p, p, 1, 1, 8, 10, 32,
+    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), p, r(ok), r(ok), p, p, 0, 1, 1, 8, 10, 32,
                                    0.0, ws, need, None) == fb.FLARE_E_UNSUPPORTED
     # the normaliser is required; sizes; workspace
-    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), None, r(ok), r(f32), p, p, 1, 1, 8, 10, 32,
+    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), None, r(ok), r(f32), p, p, 0, 1, 1, 8, 10, 32,
                                    0.0, ws, need, None) == fb.FLARE_E_INVALID
-    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), p, r(ok), r(f32), p, p, 1, 1, 8, 10, 8,
+    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), p, r(ok), r(f32), p, p, 0, 1, 1, 8, 10, 8,
                                    0.0, ws, need, None) == fb.FLARE_E_UNSUPPORTED
-    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), p, r(ok), r(f32), p, p, 1, 1, 8, 10, 32,
+    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), p, r(ok), r(f32), p, p, 0, 1, 1, 8, 10, 32,
                                    0.0, ws, need - 1, None) == fb.FLARE_E_WORKSPACE
+    # unknown flag bits
+    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), p, r(ok), r(f32), p, p, 8, 1, 1, 8, 10, 32,
+                                   0.0, ws, need, None) == fb.FLARE_E_INVALID
     need = L.flare_encode_backward_workspace_size(1, 1, 8, 10, 32)
-    assert L.flare_encode_backward(r(ok), r(ok), r(ok), r(ok), p, p, p, r(f32), r(f32), 4, 1, 1, 8, 10, 32,
+    assert L.flare_encode_backward(r(ok), r(ok), r(ok), r(ok), p, p, p, r(f32), r(f32), 8, 1, 1, 8, 10, 32,
                                    0.0, ws, need, None) == fb.FLARE_E_INVALID
     assert L.flare_encode_backward(r(ok), r(ok), r(ok), r(ok), p, p, p, r(ok), r(f32), 0, 1, 1, 8, 10, 32,
                                    0.0, ws, need, None) == fb.FLARE_E_UNSUPPORTED

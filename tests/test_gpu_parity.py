@@ -386,10 +386,67 @@ def test_flare_backward_chain(case):
     y, lse_d = rl.flare_decode(k, q, z, want_lse=True)
     dk, dq, dz = rl.flare_decode_backward(k, q, z, y, lse_d, dy)
     dq, dk, dv = rl.flare_encode_backward(q, k, v, z, lse_e, dz, dq=dq, dk=dk,
-                                          accumulate=rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK)
+                                          flags=rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK)
     torch.cuda.synchronize()
     dqr, dkr, dvr = oracle.flare_encdec_backward(f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"])),
                                                  f64(hm(dy_t)))
     check_bf16(f64(dq), dqr, "dQ")
     check_bf16(f64(dk), dkr, "dK")
     check_bf16(f64(dv), dvr, "dV")
+
+
+@pytest.mark.parametrize("case", [(2, 3, 777, 32, 200, 4.0, "token", False),
+                                  (3, 2, 1500, 16, 40, 2.0, "head", False)],
+                         ids=lambda c: "B{}H{}N{}D{}M{}-q{}-{}".format(*c[:7]))
+def test_flare_backward_shared_queries(case):
+    # FLARE's learned queries are shared by the batch: both calls sum their dQ
+    # over b in the split reduction, the encoder's onto the decoder's
+    B, H, N, D, M, qm, layout, _ = case
+    say(f"case {case}")
+    x, dy_t = _bwd_inputs(case)
+    q = x["q"].to(DEV)
+    assert q.dim() == 3
+    k, v = _dev_view(x["k"], layout), _dev_view(x["v"], layout)
+    dy = _dev_view(dy_t, layout)
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True)
+    dk, dq, dz = rl.flare_decode_backward(k, q, z, y, lse_d, dy, flags=rl.FLARE_SUM_DQ_OVER_BATCH)
+    assert tuple(dq.shape) == (H, M, D)
+    dq, dk, dv = rl.flare_encode_backward(
+        q, k, v, z, lse_e, dz, dq=dq, dk=dk,
+        flags=rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK | rl.FLARE_SUM_DQ_OVER_BATCH)
+    torch.cuda.synchronize()
+    dqr, dkr, dvr = oracle.flare_encdec_backward(f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"])),
+                                                 f64(hm(dy_t)))
+    check_bf16(f64(dq), dqr.sum(0), "dQ (summed over the batch)")
+    check_bf16(f64(dk), dkr, "dK")
+    check_bf16(f64(dv), dvr, "dV")
+
+
+@pytest.mark.parametrize("B,H,N,D,M,qm", [(2, 2, 1000, 32, 64, 2.0), (3, 1, 700, 16, 40, 4.0),
+                                          (1, 2, 4096, 32, 128, 1.0)])
+def test_flarepp_backward_chain(B, H, N, D, M, qm):
+    # FLARE++ end to end: synthesis Q(X) = SDPA(seeds, eK, eV), encode and
+    # decode with Q(X), then the three backward calls in reverse order; the
+    # seeds' gradient is summed over the batch
+    say(f"case B{B} H{H} N{N} D{D} M{M} q{qm}")
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=N + M, q_mult=qm, synth=True)
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=N + 2 * M)
+    seeds = x["seeds"].to(DEV)
+    ek, ev = hm(x["ek"]).contiguous().to(DEV), hm(x["ev"]).contiguous().to(DEV)
+    k, v = hm(x["k"]).contiguous().to(DEV), hm(x["v"]).contiguous().to(DEV)
+    dy = hm(dy_t).contiguous().to(DEV)
+    qx, lse_s = rl.flare_route_queries(seeds, ek, ev, want_lse=True)
+    z, lse_e = rl.flare_encode(qx, k, v, want_lse=True, z_dtype=torch.float32)
+    y, lse_d = rl.flare_decode(k, qx, z, want_lse=True)
+    dk, dqx, dz = rl.flare_decode_backward(k, qx, z, y, lse_d, dy)
+    dqx, dk, dv = rl.flare_encode_backward(qx, k, v, z, lse_e, dz, dq=dqx, dk=dk,
+                                           flags=rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK)
+    dseeds, dek, dev = rl.flare_encode_backward(seeds, ek, ev, qx, lse_s, dqx,
+                                                flags=rl.FLARE_SUM_DQ_OVER_BATCH)
+    torch.cuda.synchronize()
+    ref = oracle.flarepp_backward(f64(x["seeds"]), f64(hm(x["ek"])), f64(hm(x["ev"])),
+                                  f64(hm(x["k"])), f64(hm(x["v"])), f64(hm(dy_t)))
+    for got, r, what in zip((dseeds, dek, dev, dk, dv), ref, ("dseeds", "deK", "deV", "dK", "dV")):
+        check_bf16(f64(got), r, what)

@@ -426,3 +426,60 @@ def test_flare_backward_matches_library_autograd():
     assert np.max(np.abs(dq.sum(0) - qt.grad.numpy())) <= 1e-11
     assert np.max(np.abs(dk - kt.grad.numpy())) <= 1e-11
     assert np.max(np.abs(dv - vt.grad.numpy())) <= 1e-11
+
+
+def _torch_flarepp_grads(seeds, ek, ev, k, v, dy, scale):
+    ts = [torch.tensor(a, requires_grad=True) for a in (seeds, ek, ev, k, v)]
+    st, ekt, evt, kt, vt = ts
+    B, H, M, D = ek.shape[0], seeds.shape[0], seeds.shape[1], seeds.shape[2]
+    sdpa = torch.nn.functional.scaled_dot_product_attention
+    qx = sdpa(st[None].expand(B, H, M, D), ekt, evt, scale=scale)
+    y = sdpa(kt, qx, sdpa(qx, kt, vt, scale=scale), scale=scale)
+    (y * torch.tensor(dy)).sum().backward()
+    return [t.grad.numpy() for t in ts]
+
+
+def test_flarepp_backward_matches_library_autograd():
+    # torch fp64 autograd of the three-call FLARE++ chain (synthesis, encode,
+    # decode) with batch-shared seeds and sharp seeds
+    rng = np.random.default_rng(9)
+    B, H, N, M, D = 3, 2, 40, 5, 8
+    seeds = rng.standard_normal((H, M, D)) * 3
+    ek, ev = rng.standard_normal((B, H, N, D)), rng.standard_normal((B, H, N, D))
+    k, v = rng.standard_normal((B, H, N, D)), rng.standard_normal((B, H, N, D))
+    dy = rng.standard_normal((B, H, N, D))
+    scale = 0.6
+    got = oracle.flarepp_backward(seeds, ek, ev, k, v, dy, scale)
+    ref = _torch_flarepp_grads(seeds, ek, ev, k, v, dy, scale)
+    assert got[0].shape == (H, M, D)
+    for g, r in zip(got, ref):
+        assert np.max(np.abs(g - r)) <= 1e-11 * max(1.0, np.max(np.abs(r)))
+
+
+def test_flarepp_backward_matches_finite_differences():
+    # central differences of sum(dy * Y) in the seeds and the synthesis
+    # projections, whose gradients reach them only through Q(X)
+    rng = np.random.default_rng(13)
+    B, H, N, M, D = 2, 1, 7, 3, 4
+    seeds = rng.standard_normal((H, M, D)) * 2
+    ek, ev = rng.standard_normal((B, H, N, D)), rng.standard_normal((B, H, N, D))
+    k, v = rng.standard_normal((B, H, N, D)), rng.standard_normal((B, H, N, D))
+    dy = rng.standard_normal((B, H, N, D))
+    scale = 0.9
+    grads = oracle.flarepp_backward(seeds, ek, ev, k, v, dy, scale)
+    args = [seeds, ek, ev, k, v]
+
+    def f(a):
+        qx, _ = oracle.encode(a[0], a[1], a[2], scale)
+        z, _ = oracle.encode(qx, a[3], a[4], scale)
+        return float(np.sum(dy * oracle.decode(a[3], qx, z, scale)))
+
+    eps = 1e-6
+    for which, idx in ((0, (0, 1, 2)), (0, (0, 2, 0)), (1, (1, 0, 3, 1)), (2, (0, 0, 5, 2)),
+                       (3, (1, 0, 0, 3)), (4, (0, 0, 6, 0))):
+        plus = [a.copy() for a in args]
+        minus = [a.copy() for a in args]
+        plus[which][idx] += eps
+        minus[which][idx] -= eps
+        fd = (f(plus) - f(minus)) / (2 * eps)
+        assert abs(fd - grads[which][idx]) <= 1e-7 * max(1.0, abs(fd))

@@ -154,11 +154,11 @@ flare_status bwd_common_checks(int B, int H, int M, int64_t N, int D, float scal
   return FLARE_OK;
 }
 
-// Workgroups per head of the token-parallel backward pass (4 waves x 32
+// Workgroups per head of the token-parallel backward pass (4 waves x 64
 // tokens per step): about 2048 in all.
 int64_t tok_bwd_blocks(int B, int H, int64_t N) {
   const int64_t bh = (int64_t)B * H;
-  const int64_t steps = (N + 127) / 128;
+  const int64_t steps = (N + 255) / 256;
   int64_t per = (2048 + bh - 1) / bh;
   if (per > steps) per = steps;
   return per < 1 ? 1 : per;

@@ -69,8 +69,30 @@ __device__ void stage_latent_block(const View& v, int b, int hd, int M, int MC, 
 // ------------------------------------------------------- token-parallel pass
 constexpr int kTokBwdWaves = 4;
 
+// v as three bf16 terms, written to e[at], e[at + 1], e[at + 2], whose sum
+// carries v to about fp32 precision.
+__device__ __forceinline__ void split3_bf16(float v, bf16x8& e, int at) {
+  const bf16 a = (bf16)v;
+  float r = v - (float)a;
+  const bf16 b = (bf16)r;
+  r -= (float)b;
+  e[at] = a;
+  e[at + 1] = b;
+  e[at + 2] = (bf16)r;
+}
+
+// Per-latent terms of the encode role enter the score products as one more
+// 16-wide matrix-core K step: with A holding (t1, t2, t3) of latent m in
+// columns 0..2 and B holding -1 there, S' = S - (t1 + t2 + t3) for every
+// token.  With t1 + t2 + t3 = L_m / c (the normaliser over the exponent
+// scale) the exponent c S' equals c S - L_m, and with the delta terms
+// dP' = dP - delta_m; the products are exact and the fp32 accumulation
+// rounds like the subtraction itself.  Each lane of an A operand holds one
+// latent, so this replaces a per-element LDS read of the row's normaliser
+// and delta by one 16-byte read per lane and chunk.
+
 template <int D, bool ENC>
-__global__ __launch_bounds__(64 * kTokBwdWaves) void tok_bwd_kernel(TokBwdParams p) {
+__global__ __launch_bounds__(64 * kTokBwdWaves, 2) void tok_bwd_kernel(TokBwdParams p) {
   constexpr int NW = kTokBwdWaves;
   constexpr int SD = D / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -82,116 +104,149 @@ __global__ __launch_bounds__(64 * kTokBwdWaves) void tok_bwd_kernel(TokBwdParams
   bf16x8* q_lds = reinterpret_cast<bf16x8*>(smem);
   bf16x8* w_lds = q_lds + MC * SD * 64;
   bf16x8* qt_lds = w_lds + MC * SD * 64;
-  bf16x8* wt_lds = qt_lds + MC * 2 * 64;                                    // encode role
-  float* l2_lds = reinterpret_cast<float*>(wt_lds + (ENC ? MC * 2 * 64 : 0));  // encode role
-  float* dl_lds = l2_lds + MC * 32;                                          // encode role
+  bf16x8* wt_lds = qt_lds + MC * 2 * 64;           // encode role
+  bf16x8* aug_lds = wt_lds + MC * 2 * 64;          // encode role: MC * 32 latents + a zero slot
 
   stage_latent_block<D>(p.q, b, hd, p.M, MC, q_lds, qt_lds, tid, 64 * NW);
   stage_latent_block<D>(p.w, b, hd, p.M, MC, w_lds, ENC ? wt_lds : nullptr, tid, 64 * NW);
   if constexpr (ENC) {
-    // per latent: base-2 normaliser (+inf pads the last chunk: weight 0) and
-    // delta_m = dZ_m . Z_m
-    for (int m = tid; m < MC * 32; m += 64 * NW) {
-      float l2 = INFINITY, dl = 0.f;
-      if (m < p.M) {
-        l2 = p.lse[(int64_t)bh * p.M + m] * kLog2e;
-        for (int d = 0; d < D; ++d) {
-          float a, z;
-          load_as_f32<1>(p.w.data, p.w.is_f32, b * p.w.sb + hd * p.w.sh + (int64_t)m * p.w.sl + d, &a);
-          load_as_f32<1>(p.z.data, p.z.is_f32, b * p.z.sb + hd * p.z.sh + (int64_t)m * p.z.sl + d, &z);
-          dl = fmaf(a, z, dl);
+    // per latent m: L_m / c (base-2 normaliser over the exponent scale) and
+    // delta_m = dZ_m . Z_m, three bf16 terms each: (t1, t2, t3, 0, d1, d2, d3,
+    // 0).  Padded latents get a huge finite offset (weight exactly 0); the
+    // slot after the last latent stays zero for the lanes of the second K half.
+    for (int m = tid; m <= MC * 32; m += 64 * NW) {
+      bf16x8 e = {};
+      if (m < MC * 32) {
+        float v = 1e30f, dl = 0.f;
+        if (m < p.M) {
+          v = p.lse[(int64_t)bh * p.M + m] * kLog2e / p.c;
+          for (int d = 0; d < D; ++d) {
+            float a, z;
+            load_as_f32<1>(p.w.data, p.w.is_f32, b * p.w.sb + hd * p.w.sh + (int64_t)m * p.w.sl + d, &a);
+            load_as_f32<1>(p.z.data, p.z.is_f32, b * p.z.sb + hd * p.z.sh + (int64_t)m * p.z.sl + d, &z);
+            dl = fmaf(a, z, dl);
+          }
         }
+        split3_bf16(v, e, 0);
+        split3_bf16(dl, e, 4);
       }
-      l2_lds[m] = l2;
-      dl_lds[m] = dl;
+      aug_lds[m] = e;
     }
   }
   __syncthreads();
 
+  // B operand of the extra K step: -1 in K rows 0..2 (lane half 0), else 0
+  bf16x8 bneg = {};
+  if (h == 0) bneg[0] = bneg[1] = bneg[2] = (bf16)-1.0f;
+
   const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + hd * p.k.sh;
   const bf16* xbase = reinterpret_cast<const bf16*>(p.x.data) + b * p.x.sb + hd * p.x.sh;
   const float cs = p.c;
-  const int64_t stride = (int64_t)gridDim.x * NW * 32;
-  for (int64_t base = ((int64_t)blockIdx.x * NW + wave) * 32; base < p.N; base += stride) {
-    const int64_t n = base + c;
-    const bool valid = n < p.N;
+  // A wave takes 64 tokens at a time, two blocks of 32 (lane (h, c): token
+  // base + 32 tb + c): every LDS read of a latent chunk serves two score
+  // tiles, and the products of the second block run under the first block's
+  // exponentials.
+  const int64_t stride = (int64_t)gridDim.x * NW * 64;
+  for (int64_t base = ((int64_t)blockIdx.x * NW + wave) * 64; base < p.N; base += stride) {
     // B operands: token n, features 16sd + 8h .. +7 of K and of X
-    bf16x8 kb[SD], xb[SD];
+    bf16x8 kb[2][SD], xb[2][SD];
+    float l2n[2] = {0.f, 0.f}, dln[2] = {0.f, 0.f};
 #pragma unroll
-    for (int sd = 0; sd < SD; ++sd) {
-      if (valid) {
-        kb[sd] = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 16 * sd + 8 * h);
-        xb[sd] = *reinterpret_cast<const bf16x8*>(xbase + n * p.x.sl + 16 * sd + 8 * h);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kb[sd][j] = xb[sd][j] = (bf16)0.0f;
-      }
-    }
-    float l2n = 0.f, dln = 0.f;
-    if constexpr (!ENC) {
-      // delta_n = dY_n . Y_n over the token's D features (half per lane half)
-      const bf16* ybase = reinterpret_cast<const bf16*>(p.y.data) + b * p.y.sb + hd * p.y.sh;
-      float part = 0.f;
-      if (valid) {
-#pragma unroll
-        for (int sd = 0; sd < SD; ++sd) {
-          const bf16x8 yv = *reinterpret_cast<const bf16x8*>(ybase + n * p.y.sl + 16 * sd + 8 * h);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) part = fmaf((float)xb[sd][j], (float)yv[j], part);
-        }
-        l2n = p.lse[(int64_t)bh * p.N + n] * kLog2e;
-      }
-      dln = part + shfl_xor_f(part, 32);
-      if (h == 0 && valid) p.delta[(int64_t)bh * p.N + n] = dln;
-    }
-
-    f32x16 dk = zero16(), dv = zero16();
-    for (int ch = 0; ch < MC; ++ch) {
-      f32x16 sc = zero16(), dp = zero16();
+    for (int tb = 0; tb < 2; ++tb) {
+      const int64_t n = base + 32 * tb + c;
+      const bool valid = n < p.N;
 #pragma unroll
       for (int sd = 0; sd < SD; ++sd) {
-        sc = mfma_32x32x16(q_lds[(ch * SD + sd) * 64 + lane], kb[sd], sc);
-        dp = mfma_32x32x16(w_lds[(ch * SD + sd) * 64 + lane], xb[sd], dp);
-      }
-      // element i: latent 32ch + 8(i/4) + 4h + i%4 of token n
-      f32x16 pw, ds;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float l2v[4], dlv[4];
-        if constexpr (ENC) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(l2_lds + 32 * ch + 8 * q4 + 4 * h);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl_lds + 32 * ch + 8 * q4 + 4 * h);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            l2v[j] = a[j];
-            dlv[j] = d4[j];
-          }
+        if (valid) {
+          kb[tb][sd] = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 16 * sd + 8 * h);
+          xb[tb][sd] = *reinterpret_cast<const bf16x8*>(xbase + n * p.x.sl + 16 * sd + 8 * h);
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            l2v[j] = l2n;
-            dlv[j] = dln;
+          for (int j = 0; j < 8; ++j) kb[tb][sd][j] = xb[tb][sd][j] = (bf16)0.0f;
+        }
+      }
+      if constexpr (!ENC) {
+        // delta_n = dY_n . Y_n over the token's D features (half per lane half)
+        const bf16* ybase = reinterpret_cast<const bf16*>(p.y.data) + b * p.y.sb + hd * p.y.sh;
+        float part = 0.f;
+        if (valid) {
+#pragma unroll
+          for (int sd = 0; sd < SD; ++sd) {
+            const bf16x8 yv = *reinterpret_cast<const bf16x8*>(ybase + n * p.y.sl + 16 * sd + 8 * h);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) part = fmaf((float)xb[tb][sd][j], (float)yv[j], part);
+          }
+          l2n[tb] = p.lse[(int64_t)bh * p.N + n] * kLog2e;
+        }
+        dln[tb] = part + shfl_xor_f(part, 32);
+        if (h == 0 && valid) p.delta[(int64_t)bh * p.N + n] = dln[tb];
+      }
+    }
+
+    f32x16 dk[2], dv[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) dk[tb] = dv[tb] = zero16();
+    for (int ch = 0; ch < MC; ++ch) {
+      // S^T and dP^T of both token blocks; element i of a tile is latent
+      // 32ch + 8(i/4) + 4h + i%4
+      f32x16 sc[2], dp[2];
+      {
+        bf16x8 qa[SD], wa[SD];
+#pragma unroll
+        for (int sd = 0; sd < SD; ++sd) {
+          qa[sd] = q_lds[(ch * SD + sd) * 64 + lane];
+          wa[sd] = w_lds[(ch * SD + sd) * 64 + lane];
+        }
+        bf16x8 as = {}, ad = {};
+        if constexpr (ENC) {
+          const u32x4 e = __builtin_bit_cast(u32x4, aug_lds[h == 0 ? 32 * ch + c : MC * 32]);
+          as = __builtin_bit_cast(bf16x8, u32x4{e[0], e[1], 0u, 0u});
+          ad = __builtin_bit_cast(bf16x8, u32x4{e[2], e[3], 0u, 0u});
+        }
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          sc[tb] = zero16();
+          dp[tb] = zero16();
+#pragma unroll
+          for (int sd = 0; sd < SD; ++sd) {
+            sc[tb] = mfma_32x32x16(qa[sd], kb[tb][sd], sc[tb]);
+            dp[tb] = mfma_32x32x16(wa[sd], xb[tb][sd], dp[tb]);
+          }
+          if constexpr (ENC) {
+            sc[tb] = mfma_32x32x16(as, bneg, sc[tb]);
+            dp[tb] = mfma_32x32x16(ad, bneg, dp[tb]);
+          }
+        }
+      }
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        f32x16 pw, ds;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if constexpr (ENC) {
+            pw[i] = exp2_fast(sc[tb][i] * cs);
+            ds[i] = pw[i] * dp[tb][i];
+          } else {
+            pw[i] = exp2_fast(sc[tb][i] * cs - l2n[tb]);
+            ds[i] = pw[i] * (dp[tb][i] - dln[tb]);
           }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * q4 + j;
-          pw[i] = exp2_fast(sc[i] * cs - l2v[j]);
-          ds[i] = pw[i] * (dp[i] - dlv[j]);
+        for (int ug = 0; ug < 2; ++ug) {
+          dk[tb] = mfma_32x32x16(qt_lds[(ch * 2 + ug) * 64 + lane], pack8_16(ds, ug), dk[tb]);
+          if constexpr (ENC) dv[tb] = mfma_32x32x16(wt_lds[(ch * 2 + ug) * 64 + lane], pack8_16(pw, ug), dv[tb]);
         }
       }
-#pragma unroll
-      for (int ug = 0; ug < 2; ++ug) {
-        dk = mfma_32x32x16(qt_lds[(ch * 2 + ug) * 64 + lane], pack8_16(ds, ug), dk);
-        if constexpr (ENC) dv = mfma_32x32x16(wt_lds[(ch * 2 + ug) * 64 + lane], pack8_16(pw, ug), dv);
-      }
     }
-    // lane (h, c): token n, features 16h .. 16h + 15
-    if (valid && 16 * h < D) {
+    // lane (h, c): token base + 32 tb + c, features 16h .. 16h + 15
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int64_t n = base + 32 * tb + c;
+      if (n >= p.N || 16 * h >= D) continue;
       float* kp = p.dk + b * p.dk_sb + hd * p.dk_sh + n * p.dk_sl + 16 * h;
 #pragma unroll
       for (int j = 0; j < 16; j += 4) {
-        f32x4 v = {dk[j] * p.scale, dk[j + 1] * p.scale, dk[j + 2] * p.scale, dk[j + 3] * p.scale};
+        f32x4 v = {dk[tb][j] * p.scale, dk[tb][j + 1] * p.scale, dk[tb][j + 2] * p.scale, dk[tb][j + 3] * p.scale};
         if (p.accumulate) v += *reinterpret_cast<const f32x4*>(kp + j);
         *reinterpret_cast<f32x4*>(kp + j) = v;
       }
@@ -199,7 +254,7 @@ __global__ __launch_bounds__(64 * kTokBwdWaves) void tok_bwd_kernel(TokBwdParams
         float* vp = p.dv + b * p.dv_sb + hd * p.dv_sh + n * p.dv_sl + 16 * h;
 #pragma unroll
         for (int j = 0; j < 16; j += 4)
-          *reinterpret_cast<f32x4*>(vp + j) = f32x4{dv[j], dv[j + 1], dv[j + 2], dv[j + 3]};
+          *reinterpret_cast<f32x4*>(vp + j) = f32x4{dv[tb][j], dv[tb][j + 1], dv[tb][j + 2], dv[tb][j + 3]};
       }
     }
   }
@@ -211,14 +266,25 @@ constexpr int kLatBwdTile = 64;  // tokens per LDS tile
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
+// 16-byte chunk slot of (token, chunk dc) in a staged token tile: the chunk
+// index is XOR-swizzled with bits 2..3 (D = 32) or bit 2 (D = 16) of the
+// token, so that the A-operand reads (a 16-lane group reads one chunk of 16
+// consecutive tokens) spread over all bank groups.  The transposing reads
+// take whole rows per 32-lane pass and stay conflict-free under any
+// permutation of a row's chunks.
+template <int D>
+__device__ __forceinline__ int lat_chunk_pos(int token, int dc) {
+  if constexpr (D == 32) return token * 4 + (dc ^ ((token >> 2) & 3));
+  else return token * 2 + (dc ^ ((token >> 2) & 1));
+}
+
 template <int D, bool ENC, int NW>
-__global__ __launch_bounds__(64 * NW) void lat_bwd_kernel(LatBwdParams p) {
+__global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
   constexpr int SD = D / 16;
   constexpr int T = kLatBwdTile;
   __shared__ __attribute__((aligned(16))) bf16 kt[T * D];
   __shared__ __attribute__((aligned(16))) bf16 xt[T * D];
-  __shared__ __attribute__((aligned(16))) float l2t[T];
-  __shared__ __attribute__((aligned(16))) float dlt[T];
+  __shared__ __attribute__((aligned(16))) bf16x8 augt[T + 1];  // decode role: per token, and a zero slot
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31, i16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -262,69 +328,50 @@ __global__ __launch_bounds__(64 * NW) void lat_bwd_kernel(LatBwdParams p) {
   const float cs = p.c;
   const bf16 zero = (bf16)0.0f;
   f32x16 dq = zero16(), dz = zero16();
-  const int64_t tiles = (p.N + T - 1) / T;
-  for (int64_t t = s; t < tiles; t += p.S) {
-    const int64_t t0 = t * T;
-    __syncthreads();
-    for (int u = tid; u < T * D / 8; u += 64 * NW) {
-      const int tok = u / (D / 8), dc = u % (D / 8);
-      const int64_t n = t0 + tok;
-      bf16x8 kv, xv;
-      if (n < p.N) {
-        kv = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 8 * dc);
-        xv = *reinterpret_cast<const bf16x8*>(xbase + n * p.x.sl + 8 * dc);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kv[j] = xv[j] = zero;
-      }
-      reinterpret_cast<bf16x8*>(kt)[u] = kv;
-      reinterpret_cast<bf16x8*>(xt)[u] = xv;
-    }
-    if constexpr (!ENC) {
-      for (int u = tid; u < T; u += 64 * NW) {
-        const int64_t n = t0 + u;
-        l2t[u] = n < p.N ? p.lse[(int64_t)bh * p.N + n] * kLog2e : INFINITY;
-        dlt[u] = n < p.N ? p.delta[(int64_t)bh * p.N + n] : 0.f;
-      }
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int qt = 0; qt < T / 32; ++qt) {
-      // S^T and dP^T: element i is token 32qt + 8(i/4) + 4h + i%4 of latent c
-      f32x16 sc = zero16(), dp = zero16();
+  // B operand of the extra K step: -1 in K rows 0..2 (lane half 0), else 0
+  bf16x8 bneg = {};
+  if (h == 0) bneg[0] = bneg[1] = bneg[2] = (bf16)-1.0f;
+
+  // The staged tile's products for this wave's 32 latents.  RAGGED (encode
+  // role, last tile only) gives tokens past the end weight 0 through an
+  // infinite normaliser; in the decode role their staged offset already
+  // does.
+  auto tile = [&](auto ragged_tag, int rem) {
+    constexpr bool RAGGED = decltype(ragged_tag)::value;
+    // S^T and dP^T of 32-token half qt: element i is token
+    // 32qt + 8(i/4) + 4h + i%4 of latent c.  In the decode role the token's
+    // normaliser and delta enter as an extra K step, as in the token pass.
+    auto products = [&](int qt, f32x16& sc, f32x16& dp) {
+      sc = zero16();
+      dp = zero16();
 #pragma unroll
       for (int sd = 0; sd < SD; ++sd) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + (32 * qt + c) * D + 16 * sd + 8 * h);
-        const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xt + (32 * qt + c) * D + 16 * sd + 8 * h);
+        const int slot = 8 * lat_chunk_pos<D>(32 * qt + c, 2 * sd + h);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + slot);
+        const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xt + slot);
         sc = mfma_32x32x16(ka, qop[sd], sc);
         dp = mfma_32x32x16(xa, wop[sd], dp);
       }
+      if constexpr (!ENC) {
+        const u32x4 e = __builtin_bit_cast(u32x4, augt[h == 0 ? 32 * qt + c : T]);
+        sc = mfma_32x32x16(__builtin_bit_cast(bf16x8, u32x4{e[0], e[1], 0u, 0u}), bneg, sc);
+        dp = mfma_32x32x16(__builtin_bit_cast(bf16x8, u32x4{e[2], e[3], 0u, 0u}), bneg, dp);
+      }
+    };
+    // Weights and score gradients of half qt, then dQ (and dZ) += their
+    // products with the staged tokens.
+    auto finish = [&](int qt, const f32x16& sc, const f32x16& dp) {
       f32x16 pw, ds;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int row = 32 * qt + 8 * q4 + 4 * h;
-        float l2v[4], dlv[4];
+      for (int i = 0; i < 16; ++i) {
         if constexpr (ENC) {
-          const int rem = (int)min((int64_t)T, p.N - t0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            l2v[j] = row + j < rem ? l2m : INFINITY;
-            dlv[j] = dlm;
-          }
+          const int row = 32 * qt + 8 * (i >> 2) + 4 * h + (i & 3);
+          const float l2 = (!RAGGED || row < rem) ? l2m : INFINITY;
+          pw[i] = exp2_fast(sc[i] * cs - l2);
+          ds[i] = pw[i] * (dp[i] - dlm);
         } else {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(l2t + row);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + row);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            l2v[j] = a[j];
-            dlv[j] = d4[j];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * q4 + j;
-          pw[i] = exp2_fast(sc[i] * cs - l2v[j]);
-          ds[i] = pw[i] * (dp[i] - dlv[j]);
+          pw[i] = exp2_fast(sc[i] * cs);
+          ds[i] = pw[i] * dp[i];
         }
       }
 #pragma unroll
@@ -337,13 +384,14 @@ __global__ __launch_bounds__(64 * NW) void lat_bwd_kernel(LatBwdParams p) {
         for (int half = 0; half < 2; ++half) {
           const int row = 32 * qt + 16 * ug + 8 * half + 4 * h + (i16 >> 2);
           const int col = (D == 32 ? 16 * (c >> 4) : 0) + 4 * (i16 & 3);
+          const int off = 8 * lat_chunk_pos<D>(row, col >> 3) + (col & 7);
           const bf16x4 k4 = __builtin_bit_cast(
-              bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)((lds_void_t*)(kt + row * D + col))));
+              bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)((lds_void_t*)(kt + off))));
 #pragma unroll
           for (int j = 0; j < 4; ++j) kb[4 * half + j] = k4[j];
           if constexpr (!ENC) {
             const bf16x4 x4 = __builtin_bit_cast(
-                bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)((lds_void_t*)(xt + row * D + col))));
+                bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)((lds_void_t*)(xt + off))));
 #pragma unroll
             for (int j = 0; j < 4; ++j) xb[4 * half + j] = x4[j];
           }
@@ -360,7 +408,81 @@ __global__ __launch_bounds__(64 * NW) void lat_bwd_kernel(LatBwdParams p) {
         dq = mfma_32x32x16(pack8_16(ds, ug), kb, dq);
         if constexpr (!ENC) dz = mfma_32x32x16(pack8_16(pw, ug), xb, dz);
       }
+    };
+    f32x16 sc0, dp0, sc1, dp1;
+    products(0, sc0, dp0);
+    if constexpr (ENC) {
+      finish(0, sc0, dp0);
+      products(1, sc1, dp1);
+    } else {
+      // the second half's products run under the first half's exponentials
+      products(1, sc1, dp1);
+      finish(0, sc0, dp0);
     }
+    finish(1, sc1, dp1);
+  };
+
+  // Token tiles t = s, s + S, ... of this split, staged through registers:
+  // the next tile's loads are in flight while the current one is computed.
+  constexpr int UNITS = T * D / 8;                           // 16-byte chunks per tensor
+  constexpr int UPT = (UNITS + 64 * NW - 1) / (64 * NW);     // per thread
+  const int64_t tiles = (p.N + T - 1) / T;
+  bf16x8 kv[UPT], xv[UPT];
+  float l2s = 1e30f, dls = 0.f;
+  auto fetch = [&](int64_t t) {
+    const int64_t t0 = t * T;
+#pragma unroll
+    for (int q = 0; q < UPT; ++q) {
+      const int u = tid + q * 64 * NW;
+      const int tok = u / (D / 8), dc = u % (D / 8);
+      const int64_t n = t0 + tok;
+      if (u < UNITS && n < p.N) {
+        kv[q] = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 8 * dc);
+        xv[q] = *reinterpret_cast<const bf16x8*>(xbase + n * p.x.sl + 8 * dc);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kv[q][j] = xv[q][j] = zero;
+      }
+    }
+    if constexpr (!ENC) {
+      const int64_t n = t0 + tid;
+      if (tid < T) {
+        l2s = n < p.N ? p.lse[(int64_t)bh * p.N + n] * kLog2e / p.c : 1e30f;
+        dls = n < p.N ? p.delta[(int64_t)bh * p.N + n] : 0.f;
+      }
+    }
+  };
+  if (s < tiles) fetch(s);
+  for (int64_t t = s; t < tiles; t += p.S) {
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int q = 0; q < UPT; ++q) {
+      const int u = tid + q * 64 * NW;
+      if (u < UNITS) {
+        const int pos = lat_chunk_pos<D>(u / (D / 8), u % (D / 8));
+        reinterpret_cast<bf16x8*>(kt)[pos] = kv[q];
+        reinterpret_cast<bf16x8*>(xt)[pos] = xv[q];
+      }
+    }
+    if constexpr (!ENC) {
+      // per token: L_n / c and delta_n as three bf16 terms each (tokens past
+      // the end get a huge finite offset: weight 0)
+      if (tid <= T) {
+        bf16x8 e = {};
+        if (tid < T) {
+          split3_bf16(l2s, e, 0);
+          split3_bf16(dls, e, 4);
+        }
+        augt[tid] = e;
+      }
+    }
+    __syncthreads();
+    if (t + p.S < tiles) fetch(t + p.S);
+    const int rem = (int)min((int64_t)T, p.N - t * T);
+    if (ENC && rem < T)
+      tile(std::integral_constant<bool, true>(), rem);
+    else
+      tile(std::integral_constant<bool, false>(), rem);
   }
 
   // Partials of this split: accumulator row i of lane (h, c) is latent
@@ -420,7 +542,7 @@ int plan_bwd_splits(int B, int H, int M, int64_t N) {
 static size_t tok_bwd_lds(int M, int D, bool enc) {
   const int MC = (M + 31) / 32;
   size_t bytes = (size_t)MC * (D / 16) * 64 * 16 * 2 + (size_t)MC * 2 * 64 * 16;
-  if (enc) bytes += (size_t)MC * 2 * 64 * 16 + (size_t)MC * 32 * 4 * 2;
+  if (enc) bytes += (size_t)MC * 2 * 64 * 16 + (size_t)(MC * 32 + 1) * 16;
   return bytes;
 }
 

@@ -292,47 +292,43 @@ def main():
         mws = torch.empty(rl.mix_workspace_size(1, N, mw.C, H, M, True, True), dtype=torch.uint8,
                           device=dev)
 
-        def mix():
-            rl.flare_mix(m["x"], m["w_k"], m["w_v"], m["qs"], H, w_ek=m["w_ek"], w_ev=m["w_ev"],
-                         w_o=m["w_o"], out=out, workspace=mws, stream=stream)
-        for _ in range(max(2, args.warmup // 2)):
-            mix()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         msteps = max(3, args.steps // 2)
-        e0.record(stream)
-        for _ in range(msteps):
-            mix()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        mms = e0.elapsed_time(e1) / msteps
-        mwk = costs.mixer(1, N, mw.C, H, M, dynamic=True, has_wo=True)
-        extra["flarepp_mixer"] = {
-            "config": "FLARE++ mixer with all projections, B=1, N=1048576, C=256, H=8, D=32, M=256, bf16",
-            "ms": round(mms, 4), "tokens_per_s": N / (mms / 1e3),
-            "tflops": round(mwk.flops / (mms / 1e3) / 1e12, 1)}
 
-        # FLARE (fixed learned queries, no synthesis, no eK/eV) at the same
-        # sizes, for the FLARE++ / FLARE cost ratio the pages discuss.
-        def mix_fixed():
-            rl.flare_mix(m["x"], m["w_k"], m["w_v"], m["qs"], H, w_o=m["w_o"], out=out, workspace=mws,
-                         stream=stream)
-        for _ in range(max(2, args.warmup // 2)):
-            mix_fixed()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(msteps):
-            mix_fixed()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        fms = e0.elapsed_time(e1) / msteps
+        def time_mix(**kw):
+            def run():
+                rl.flare_mix(m["x"], m["w_k"], m["w_v"], m["qs"], H, w_o=m["w_o"], out=out, workspace=mws,
+                             stream=stream, **kw)
+            for _ in range(max(2, args.warmup // 2)):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(msteps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / msteps
+
+        def mix_entry(what, ms, wk):
+            return {"config": f"{what} with all projections, B=1, N=1048576, C=256, H=8, D=32, M=256, bf16",
+                    "ms": round(ms, 4), "tokens_per_s": N / (ms / 1e3),
+                    "tflops": round(wk.flops / (ms / 1e3) / 1e12, 1)}
+        # FLARE++ (synthesis with its own eK/eV projections), FLARE++ with
+        # shared projections (the synthesis attends over K and V), and FLARE
+        # (fixed learned queries), for the cost ratios the pages discuss.
+        mms = time_mix(w_ek=m["w_ek"], w_ev=m["w_ev"])
+        sms = time_mix(w_ek=m["w_k"], w_ev=m["w_v"])
+        fms = time_mix()
+        mwk = costs.mixer(1, N, mw.C, H, M, dynamic=True, has_wo=True)
         fwk = costs.mixer(1, N, mw.C, H, M, dynamic=False, has_wo=True)
-        extra["flare_mixer"] = {
-            "config": "FLARE mixer with all projections, B=1, N=1048576, C=256, H=8, D=32, M=256, bf16",
-            "ms": round(fms, 4), "tokens_per_s": N / (fms / 1e3),
-            "tflops": round(fwk.flops / (fms / 1e3) / 1e12, 1)}
+        swk = costs.mixer(1, N, mw.C, H, M, dynamic=True, has_wo=True, shared=True)
+        extra["flarepp_mixer"] = mix_entry("FLARE++ mixer", mms, mwk)
+        extra["flarepp_shared_mixer"] = mix_entry("FLARE++ mixer, shared projections (eK = K, eV = V)", sms, swk)
+        extra["flare_mixer"] = mix_entry("FLARE mixer", fms, fwk)
         extra["flarepp_over_flare"] = {"time": round(mms / fms, 3),
-                                       "operations": round(mwk.flops / fwk.flops, 3)}
+                                       "operations": round(mwk.flops / fwk.flops, 3),
+                                       "shared_time": round(sms / fms, 3),
+                                       "shared_operations": round(swk.flops / fwk.flops, 3)}
 
     cpu = None
     if not args.no_cpu:

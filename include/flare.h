@@ -162,7 +162,10 @@ flare_status flare_project(const void* X, const void* const* W, void* const* Y,
  *           the learned queries; Z = SDPA(Q, K, V); Y = SDPA(K, Q, Z).
  *   FLARE++ (W_eK != NULL): also eK = X W_eK, eV = X W_eV; Q_or_seeds are the
  *           seeds and Q(X) = SDPA(seeds, eK, eV) replaces the learned queries
- *           in both the encode and the decode.
+ *           in both the encode and the decode.  Passing W_eK == W_K and
+ *           W_eV == W_V (the same pointers) selects the variant with shared
+ *           projections: the synthesis attends over K and V themselves and
+ *           only two input projections run.
  * Heads are concatenated into out [B, N, C]; if W_O != NULL, out = Y W_O.
  * All weights [C, C] with y = x W.  dtype must be FLARE_BF16; C = H*D with
  * D in {16, 32} and C in {32, 64, 128, 256} (FLARE_E_UNSUPPORTED otherwise);

@@ -53,11 +53,13 @@ def projection(B, N, C, n_proj, elem=BF16, read_x=True) -> Work:
     return Work(2.0 * B * N * C * C * n_proj, 0.0, float(byts))
 
 
-def mixer(B, N, C, H, M, dynamic: bool, has_wo: bool, elem=BF16) -> Work:
-    """Whole mixer: projections + SDPA calls (+ output projection)."""
+def mixer(B, N, C, H, M, dynamic: bool, has_wo: bool, elem=BF16, shared: bool = False) -> Work:
+    """Whole mixer: projections + SDPA calls (+ output projection).  With
+    ``shared`` (FLARE++ whose synthesis reuses K and V) the eK, eV
+    projections drop out."""
     D = C // H
     n_proj, calls = primitives(dynamic, has_wo)
-    n_in = n_proj - (1 if has_wo else 0)
+    n_in = n_proj - (1 if has_wo else 0) - (2 if dynamic and shared else 0)
     w = projection(B, N, C, n_in, elem)
     for _ in range(calls):
         w = w + sdpa_call(B, H, N, M, D, elem)

@@ -367,13 +367,16 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V, const vo
   const size_t act = align_up((size_t)B * N * C * 2);
   void* kp = ws + L.kv;
   void* vp = ws + L.kv + act;
-  void* ekp = ws + L.kv + 2 * act;
-  void* evp = ws + L.kv + 3 * act;
+  // FLARE++ with shared projections (the synthesis reuses K and V) when the
+  // caller passes the same weights for both pairs: two projections, not four.
+  const bool shared = dynamic && W_eK == W_K && W_eV == W_V;
+  void* ekp = shared ? kp : ws + L.kv + 2 * act;
+  void* evp = shared ? vp : ws + L.kv + 3 * act;
 
   // (a) projections, written head-major [B, H, N, D]
   const void* w_in[4] = {W_K, W_V, W_eK, W_eV};
   void* y_in[4] = {kp, vp, ekp, evp};
-  flare_status s = project_impl(X, w_in, y_in, dynamic ? 4 : 2, (int64_t)B * N, C, C, 1, B, D,
+  flare_status s = project_impl(X, w_in, y_in, dynamic && !shared ? 4 : 2, (int64_t)B * N, C, C, 1, B, D,
                                 ws + L.wsw, st);
   if (s != FLARE_OK) return s;
 

@@ -233,6 +233,21 @@ def test_mix_block_reduced(dynamic, has_wo, qm, flags):
     check_bf16(_gpu_mix(m, w.H, flags), _oracle_mix(m, w.H), f"mix dyn={dynamic} wo={has_wo}")
 
 
+@pytest.mark.parametrize("qm", [1.0, 8.0])
+def test_mix_shared_projections(qm):
+    # FLARE++ with shared projections (the synthesis attends over K and V):
+    # the same weight tensors passed for both pairs; the oracle runs the
+    # general mixer with eK = K, eV = V.
+    w = inputs.Workload("t", "mix", 2, 3000, 8, 32, 128, "bf16", dynamic=True, has_wo=True)
+    m = inputs.make_mix(w, seed=4, q_mult=qm)
+    g = {n: t.to(DEV) for n, t in m.items()}
+    out = rl.flare_mix(g["x"], g["w_k"], g["w_v"], g["qs"], w.H, w_ek=g["w_k"], w_ev=g["w_v"], w_o=g["w_o"])
+    torch.cuda.synchronize()
+    ref = oracle.flare_mix(f64(m["x"]), f64(m["w_k"]), f64(m["w_v"]), f64(m["qs"]), w.H,
+                           w_ek=f64(m["w_k"]), w_ev=f64(m["w_v"]), w_o=f64(m["w_o"]))[0]
+    check_bf16(f64(out), ref, f"FLARE++ shared projections (seed x{qm})")
+
+
 def test_deterministic_repeat():
     w = inputs.Workload("t", "encdec", 1, 4000, 4, 32, 256, "bf16")
     x = inputs.make_encdec(w, seed=9, q_mult=2.0)

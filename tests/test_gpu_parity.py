@@ -465,3 +465,31 @@ def test_flarepp_backward_chain(B, H, N, D, M, qm):
                                   f64(hm(x["k"])), f64(hm(x["v"])), f64(hm(dy_t)))
     for got, r, what in zip((dseeds, dek, dev, dk, dv), ref, ("dseeds", "deK", "deV", "dK", "dV")):
         check_bf16(f64(got), r, what)
+
+
+def test_backward_metric_workload_full_size_one_head():
+    # The backward of the FLARE pair at N = 1,048,576, H=8, D=32, M=256 (bf16),
+    # in the calls and launch configuration the benchmark times (decoder
+    # backward, then encoder backward accumulating dQ and dK).  The oracle's
+    # chain rule runs on head 3 over all tokens (about 15-30 s of fp64 work);
+    # the head's dQ, and its dK and dV for every token, are compared.
+    w = inputs.WORKLOADS["encdec_bf16_n1m"]
+    x = inputs.make_encdec(w, seed=0)
+    dy_t = inputs.normal_tensor((w.B, w.N, w.H, w.D), "bf16", seed=77)
+    q = x["q"].to(DEV)
+    k = hm(x["k"]).contiguous().to(DEV)
+    v = hm(x["v"]).contiguous().to(DEV)
+    dy = hm(dy_t).contiguous().to(DEV)
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True)
+    dk, dq, dz = rl.flare_decode_backward(k, q, z, y, lse_d, dy)
+    dq, dk, dv = rl.flare_encode_backward(q, k, v, z, lse_e, dz, dq=dq, dk=dk,
+                                          flags=rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK)
+    torch.cuda.synchronize()
+    h = 3
+    say("oracle: chain-rule gradients of head 3 over all tokens")
+    dqr, dkr, dvr = oracle.flare_encdec_backward(f64(x["q"][h:h + 1]), f64(hm(x["k"][:, :, h:h + 1])),
+                                                 f64(hm(x["v"][:, :, h:h + 1])), f64(hm(dy_t[:, :, h:h + 1])))
+    check_bf16(f64(dq[:, h:h + 1]), dqr, "dQ head 3")
+    check_bf16(f64(dk[:, h:h + 1]), dkr, "dK head 3")
+    check_bf16(f64(dv[:, h:h + 1]), dvr, "dV head 3")

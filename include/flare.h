@@ -237,6 +237,33 @@ flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* The FLARE pair, Z = SDPA(Q, K, V) then Y = SDPA(K, Q, Z) ("FLARE:
+ * fixed-query latent routing"): dQ, dK, dV of sum(dY * Y) through both calls
+ * in one call.  It equals flare_decode_backward followed by
+ * flare_encode_backward with FLARE_ACCUMULATE_DQ | FLARE_ACCUMULATE_DK, but
+ * the two token-side passes share their score products and dK is written
+ * once.
+ *   Q, Z, lse_enc   flare_encode's inputs and outputs (Z as flare_decode used
+ *                   it); lse_enc [B, H, M]
+ *   Y, lse_dec      flare_decode's output and its [B, H, N] normalisers
+ *   dY              upstream gradient of Y (bf16, like K, V, Y)
+ *   dQ              fp32 [B, H, M, D] (or [H, M, D] with
+ *                   FLARE_SUM_DQ_OVER_BATCH); dK, dV fp32 [B, H, N, D] views
+ * Flags as for the two calls (accumulation into dQ / dK, batch sum of dQ).
+ * M above 256 runs the two calls internally.  Workspace:
+ * flare_encdec_backward_workspace_size bytes, 256-byte aligned. */
+size_t flare_encdec_backward_workspace_size(int B, int H, int M, int64_t N,
+                                            int D);
+flare_status flare_encdec_backward(const flare_tensor* Q, const flare_tensor* K,
+                                   const flare_tensor* V, const flare_tensor* Z,
+                                   const float* lse_enc, const flare_tensor* Y,
+                                   const float* lse_dec, const flare_tensor* dY,
+                                   float* dQ, const flare_tensor* dK,
+                                   const flare_tensor* dV, unsigned flags,
+                                   int B, int H, int M, int64_t N, int D,
+                                   float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* flare_status_string(int status);
 

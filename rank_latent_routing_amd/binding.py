@@ -36,6 +36,7 @@ EXPORTS = ("flare_encode_workspace_size", "flare_encode", "flare_route_queries",
            "flare_mix_workspace_size", "flare_mix",
            "flare_decode_backward_workspace_size", "flare_decode_backward",
            "flare_encode_backward_workspace_size", "flare_encode_backward",
+           "flare_encdec_backward_workspace_size", "flare_encdec_backward",
            "flare_status_string", "flare_version")
 
 
@@ -80,6 +81,10 @@ def lib():
     L.flare_encode_backward_workspace_size.restype = sz
     L.flare_encode_backward.argtypes = [T, T, T, T, vp, vp, vp, T, T, u32, i32, i32, i32, i64, i32,
                                         f32, vp, sz, vp]
+    L.flare_encdec_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32]
+    L.flare_encdec_backward_workspace_size.restype = sz
+    L.flare_encdec_backward.argtypes = [T, T, T, T, vp, T, vp, T, vp, T, T, u32, i32, i32, i32, i64, i32,
+                                        f32, vp, sz, vp]
     L.flare_project_workspace_size.argtypes = [i32, i32, i32]
     L.flare_project_workspace_size.restype = sz
     L.flare_project.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i32,
@@ -89,7 +94,7 @@ def lib():
     L.flare_mix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32,
                             f32, u32, vp, sz, vp]
     for f in ("flare_encode", "flare_route_queries", "flare_decode", "flare_project", "flare_mix",
-              "flare_decode_backward", "flare_encode_backward"):
+              "flare_decode_backward", "flare_encode_backward", "flare_encdec_backward"):
         getattr(L, f).restype = ctypes.c_int
     L.flare_status_string.argtypes = [i32]
     L.flare_status_string.restype = ctypes.c_char_p
@@ -265,6 +270,28 @@ def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, flags=
                                     ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                     _stream(stream))
     _check(s, "flare_encode_backward")
+    return dq, dk, dv
+
+
+def flare_encdec_backward(q, k, v, z, lse_enc, y, lse_dec, dy, dq=None, dk=None, dv=None, flags=0,
+                          scale=0.0, workspace=None, stream=None):
+    """Gradients (dq fp32, dk, dv [B, H, N, D] fp32) of sum(dy * Y) through the
+    FLARE pair Z = flare_encode(q, k, v), Y = flare_decode(k, q, z), given
+    both calls' outputs and normalisers.  ``flags`` as for the two calls."""
+    B, H, N, D = _dims(k)
+    M = q.shape[-2]
+    dev = k.device
+    dq = dq if dq is not None else torch.empty(_dq_shape(B, H, M, D, flags), dtype=torch.float32,
+                                               device=dev)
+    dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    ws = _workspace(lib().flare_encdec_backward_workspace_size(B, H, M, N, D), dev, workspace)
+    s = lib().flare_encdec_backward(describe(q), describe(k), describe(v), describe(z), _f32_ptr(lse_enc),
+                                    describe(y), _f32_ptr(lse_dec), describe(dy), _f32_ptr(dq),
+                                    describe(dk), describe(dv), int(flags), B, H, M, N, D, float(scale),
+                                    ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                    _stream(stream))
+    _check(s, "flare_encdec_backward")
     return dq, dk, dv
 
 

@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 
 #include "../../include/flare.h"
@@ -160,6 +161,16 @@ int64_t tok_bwd_blocks(int B, int H, int64_t N) {
   const int64_t bh = (int64_t)B * H;
   const int64_t steps = (N + 255) / 256;
   int64_t per = (2048 + bh - 1) / bh;
+  if (per > steps) per = steps;
+  return per < 1 ? 1 : per;
+}
+
+// Workgroups per head of the pair pass (12 waves x 32 tokens per step): one
+// per CU in all, so each stages its head's latent operands once.
+int64_t tok_pair_blocks(int B, int H, int64_t N) {
+  const int64_t bh = (int64_t)B * H;
+  const int64_t steps = (N + 383) / 384;
+  int64_t per = (256 + bh - 1) / bh;
   if (per > steps) per = steps;
   return per < 1 ? 1 : per;
 }
@@ -592,6 +603,136 @@ flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
   tp.accumulate = (flags & FLARE_ACCUMULATE_DK) ? 1 : 0;
   tp.blocks_per_head = tok_bwd_blocks(B, H, N);
   if ((e = launch_tok_bwd(tp, D, B, true, st)) != hipSuccess) return FLARE_E_HIP;
+  return FLARE_OK;
+}
+
+size_t flare_encdec_backward_workspace_size(int B, int H, int M, int64_t N, int D) {
+  if (!sizes_ok(B, H, M, N, D)) return 0;
+  const size_t dz = align_up((size_t)B * H * M * D * 4);
+  const size_t rest = std::max(flare_decode_backward_workspace_size(B, H, M, N, D),
+                               flare_encode_backward_workspace_size(B, H, M, N, D));
+  return dz + rest;
+}
+
+flare_status flare_encdec_backward(const flare_tensor* Q, const flare_tensor* K, const flare_tensor* V,
+                                   const flare_tensor* Z, const float* lse_enc, const flare_tensor* Y,
+                                   const float* lse_dec, const flare_tensor* dY, float* dQ,
+                                   const flare_tensor* dK, const flare_tensor* dV, unsigned flags, int B,
+                                   int H, int M, int64_t N, int D, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  flare_status v = bwd_common_checks(B, H, M, N, D, scale);
+  if (v != FLARE_OK) return v;
+  if (!token_tensor_ok(K) || !token_tensor_ok(V) || !token_tensor_ok(Y) || !token_tensor_ok(dY) ||
+      !token_tensor_ok(dK) || !token_tensor_ok(dV) || !latent_tensor_ok(Q) || !latent_tensor_ok(Z))
+    return FLARE_E_INVALID;
+  if (K->dtype != FLARE_BF16 || V->dtype != FLARE_BF16 || Y->dtype != FLARE_BF16 || dY->dtype != FLARE_BF16 ||
+      dK->dtype != FLARE_F32 || dV->dtype != FLARE_F32)
+    return FLARE_E_UNSUPPORTED;
+  if (!f32_ptr_ok(lse_enc) || !f32_ptr_ok(lse_dec) || !f32_ptr_ok(dQ)) return FLARE_E_INVALID;
+  if (flags & ~kBwdFlags) return FLARE_E_INVALID;
+  const size_t need = flare_encdec_backward_workspace_size(B, H, M, N, D);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return FLARE_E_WORKSPACE;
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* dZ = reinterpret_cast<float*>(ws);
+  char* rest = ws + align_up((size_t)B * H * M * D * 4);
+  const size_t rest_bytes = workspace_bytes - align_up((size_t)B * H * M * D * 4);
+  const unsigned q_sum = flags & FLARE_SUM_DQ_OVER_BATCH;
+  if (M > kTokPairMaxM) {
+    // the pair pass's latent operands would not fit one CU's LDS: the two
+    // calls one after the other, the encoder's dQ and dK added on
+    flare_status st = flare_decode_backward(K, Q, Z, Y, lse_dec, dY, dK, dQ, dZ, flags, B, H, M, N, D, scale,
+                                            rest, rest_bytes, stream);
+    if (st != FLARE_OK) return st;
+    return flare_encode_backward(Q, K, V, Z, lse_enc, dZ, dQ, dK, dV,
+                                 FLARE_ACCUMULATE_DQ | FLARE_ACCUMULATE_DK | q_sum, B, H, M, N, D, scale, rest,
+                                 rest_bytes, stream);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int S = plan_bwd_splits(B, H, M, N);
+  float* delta = reinterpret_cast<float*>(rest);
+  float* dq_part = reinterpret_cast<float*>(rest + align_up((size_t)B * H * N * 4));
+  float* dz_part = dq_part + align_up((size_t)B * H * S * M * D * 4) / 4;
+  const float c = log2_scale(scale, D), sc = natural_scale(scale, D);
+  const int64_t MD = (int64_t)M * D;
+
+  // (1) latent pass of the decoder: dQ, dZ partials; delta = dY . Y
+  LatBwdParams lp;
+  std::memset(&lp, 0, sizeof(lp));
+  lp.k = view_of(K);
+  lp.x = view_of(dY);
+  lp.y = view_of(Y);
+  lp.q = view_of(Q);
+  lp.w = view_of(Z);
+  lp.z = lp.w;
+  lp.lse = lse_dec;
+  lp.delta_out = delta;
+  lp.dq_part = dq_part;
+  lp.dz_part = dz_part;
+  lp.H = H;
+  lp.M = M;
+  lp.S = S;
+  lp.N = N;
+  lp.c = c;
+  hipError_t e = launch_lat_bwd(lp, D, B, false, st);
+  if (e != hipSuccess) return FLARE_E_HIP;
+  if ((e = launch_sum_splits(dz_part, dZ, B, H, S, MD, false, 1.0f, 0, st)) != hipSuccess) return FLARE_E_HIP;
+  if ((e = launch_sum_splits(dq_part, dQ, B, H, S, MD, q_sum != 0, sc, (flags & FLARE_ACCUMULATE_DQ) ? 1 : 0,
+                             st)) != hipSuccess)
+    return FLARE_E_HIP;
+
+  // (2) latent pass of the encoder with dZ: its dQ added on
+  View dzv;
+  dzv.data = dZ;
+  dzv.is_f32 = 1;
+  dzv.sb = (int64_t)H * MD;
+  dzv.sh = MD;
+  dzv.sl = D;
+  LatBwdParams le;
+  std::memset(&le, 0, sizeof(le));
+  le.k = view_of(K);
+  le.x = view_of(V);
+  le.q = view_of(Q);
+  le.w = dzv;
+  le.z = view_of(Z);
+  le.lse = lse_enc;
+  le.dq_part = dq_part;
+  le.H = H;
+  le.M = M;
+  le.S = S;
+  le.N = N;
+  le.c = c;
+  if ((e = launch_lat_bwd(le, D, B, true, st)) != hipSuccess) return FLARE_E_HIP;
+  if ((e = launch_sum_splits(dq_part, dQ, B, H, S, MD, q_sum != 0, sc, 1, st)) != hipSuccess) return FLARE_E_HIP;
+
+  // (3) token pass of both roles: dK, dV
+  TokPairParams tp;
+  std::memset(&tp, 0, sizeof(tp));
+  tp.k = view_of(K);
+  tp.v = view_of(V);
+  tp.dy = view_of(dY);
+  tp.q = view_of(Q);
+  tp.z = view_of(Z);
+  tp.dz = dzv;
+  tp.lse_e = lse_enc;
+  tp.lse_d = lse_dec;
+  tp.delta_d = delta;
+  tp.dk = reinterpret_cast<float*>(dK->data);
+  tp.dk_sb = dK->stride_b;
+  tp.dk_sh = dK->stride_h;
+  tp.dk_sl = dK->stride_l;
+  tp.dv = reinterpret_cast<float*>(dV->data);
+  tp.dv_sb = dV->stride_b;
+  tp.dv_sh = dV->stride_h;
+  tp.dv_sl = dV->stride_l;
+  tp.H = H;
+  tp.M = M;
+  tp.N = N;
+  tp.c = c;
+  tp.scale = sc;
+  tp.accumulate = (flags & FLARE_ACCUMULATE_DK) ? 1 : 0;
+  tp.blocks_per_head = tok_pair_blocks(B, H, N);
+  if ((e = launch_tok_pair(tp, D, B, st)) != hipSuccess) return FLARE_E_HIP;
   return FLARE_OK;
 }
 

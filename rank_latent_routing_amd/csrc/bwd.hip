@@ -260,6 +260,125 @@ __global__ __launch_bounds__(64 * kTokBwdWaves, 2) void tok_bwd_kernel(TokBwdPar
   }
 }
 
+// ------------------------------------------- token-parallel pass, both roles
+// For the pair Z = SDPA(Q, K, V), Y = SDPA(K, Q, Z) the two calls score the
+// same products s = scale q . k: the encoder normalises them per latent, the
+// decoder per token.  One pass over the token x latent tiles therefore serves
+// both token-side gradients,
+//   dk_n = scale sum_m (P_d (dP_d - delta_n) + P_e (dP_e - delta_m)) q_m,
+//   dv_n = sum_m P_e dZ_m,
+// with P_d, dP_d = dY_n . Z_m from the decoder and P_e, dP_e = dZ_m . V_n from
+// the encoder.  dK is written once, with no second pass reading it back.
+constexpr int kTokPairWaves = 12;
+
+template <int D>
+__global__ __launch_bounds__(64 * kTokPairWaves, 3) void tok_pair_kernel(TokPairParams p) {
+  constexpr int NW = kTokPairWaves;
+  constexpr int SD = D / 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.y, b = bh / p.H, hd = bh - b * p.H;
+  const int MC = (p.M + 31) / 32;
+  bf16x8* q_lds = reinterpret_cast<bf16x8*>(smem);  // A of S^T = Q K^T
+  bf16x8* z_lds = q_lds + MC * SD * 64;             // A of dP_d^T = Z dY^T
+  bf16x8* dz_lds = z_lds + MC * SD * 64;            // A of dP_e^T = dZ V^T
+  bf16x8* qt_lds = dz_lds + MC * SD * 64;           // A of dK^T += Q^T dS^T
+  bf16x8* dzt_lds = qt_lds + MC * 2 * 64;           // A of dV^T += dZ^T P_e^T
+  bf16x8* aug_lds = dzt_lds + MC * 2 * 64;          // per latent L_m / c and delta_m; zero slot
+
+  stage_latent_block<D>(p.q, b, hd, p.M, MC, q_lds, qt_lds, tid, 64 * NW);
+  stage_latent_block<D>(p.z, b, hd, p.M, MC, z_lds, nullptr, tid, 64 * NW);
+  stage_latent_block<D>(p.dz, b, hd, p.M, MC, dz_lds, dzt_lds, tid, 64 * NW);
+  for (int m = tid; m <= MC * 32; m += 64 * NW) {
+    bf16x8 e = {};
+    if (m < MC * 32) {
+      float v = 1e30f, dl = 0.f;
+      if (m < p.M) {
+        v = p.lse_e[(int64_t)bh * p.M + m] * kLog2e / p.c;
+        for (int d = 0; d < D; ++d) {
+          float a, z;
+          load_as_f32<1>(p.dz.data, p.dz.is_f32, b * p.dz.sb + hd * p.dz.sh + (int64_t)m * p.dz.sl + d, &a);
+          load_as_f32<1>(p.z.data, p.z.is_f32, b * p.z.sb + hd * p.z.sh + (int64_t)m * p.z.sl + d, &z);
+          dl = fmaf(a, z, dl);
+        }
+      }
+      split3_bf16(v, e, 0);
+      split3_bf16(dl, e, 4);
+    }
+    aug_lds[m] = e;
+  }
+  __syncthreads();
+
+  bf16x8 bneg = {};
+  if (h == 0) bneg[0] = bneg[1] = bneg[2] = (bf16)-1.0f;
+  const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + hd * p.k.sh;
+  const bf16* vbase = reinterpret_cast<const bf16*>(p.v.data) + b * p.v.sb + hd * p.v.sh;
+  const bf16* gbase = reinterpret_cast<const bf16*>(p.dy.data) + b * p.dy.sb + hd * p.dy.sh;
+  const float cs = p.c;
+  const int64_t stride = (int64_t)gridDim.x * NW * 32;
+  for (int64_t base = ((int64_t)blockIdx.x * NW + wave) * 32; base < p.N; base += stride) {
+    // lane (h, c): token n; B operands hold features 16sd + 8h .. +7
+    const int64_t n = base + c;
+    const bool valid = n < p.N;
+    bf16x8 kb[SD], vb[SD], gb[SD];
+#pragma unroll
+    for (int sd = 0; sd < SD; ++sd) {
+      if (valid) {
+        kb[sd] = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 16 * sd + 8 * h);
+        vb[sd] = *reinterpret_cast<const bf16x8*>(vbase + n * p.v.sl + 16 * sd + 8 * h);
+        gb[sd] = *reinterpret_cast<const bf16x8*>(gbase + n * p.dy.sl + 16 * sd + 8 * h);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kb[sd][j] = vb[sd][j] = gb[sd][j] = (bf16)0.0f;
+      }
+    }
+    const float l2d = valid ? p.lse_d[(int64_t)bh * p.N + n] * kLog2e : 0.f;
+    const float dd = valid ? p.delta_d[(int64_t)bh * p.N + n] : 0.f;
+
+    f32x16 dk = zero16(), dv = zero16();
+    for (int ch = 0; ch < MC; ++ch) {
+      // element i of a tile: latent 32ch + 8(i/4) + 4h + i%4 of token n
+      f32x16 sc = zero16(), dpd = zero16(), dpe = zero16();
+#pragma unroll
+      for (int sd = 0; sd < SD; ++sd) {
+        sc = mfma_32x32x16(q_lds[(ch * SD + sd) * 64 + lane], kb[sd], sc);
+        dpd = mfma_32x32x16(z_lds[(ch * SD + sd) * 64 + lane], gb[sd], dpd);
+        dpe = mfma_32x32x16(dz_lds[(ch * SD + sd) * 64 + lane], vb[sd], dpe);
+      }
+      // the encoder's per-latent normaliser and delta as one more K step
+      const u32x4 e = __builtin_bit_cast(u32x4, aug_lds[h == 0 ? 32 * ch + c : MC * 32]);
+      const f32x16 se = mfma_32x32x16(__builtin_bit_cast(bf16x8, u32x4{e[0], e[1], 0u, 0u}), bneg, sc);
+      dpe = mfma_32x32x16(__builtin_bit_cast(bf16x8, u32x4{e[2], e[3], 0u, 0u}), bneg, dpe);
+      f32x16 pe, ds;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pd = exp2_fast(sc[i] * cs - l2d);
+        pe[i] = exp2_fast(se[i] * cs);
+        ds[i] = fmaf(pe[i], dpe[i], pd * (dpd[i] - dd));
+      }
+#pragma unroll
+      for (int ug = 0; ug < 2; ++ug) {
+        dk = mfma_32x32x16(qt_lds[(ch * 2 + ug) * 64 + lane], pack8_16(ds, ug), dk);
+        dv = mfma_32x32x16(dzt_lds[(ch * 2 + ug) * 64 + lane], pack8_16(pe, ug), dv);
+      }
+    }
+    // lane (h, c): token n, features 16h .. 16h + 15
+    if (valid && 16 * h < D) {
+      float* kp = p.dk + b * p.dk_sb + hd * p.dk_sh + n * p.dk_sl + 16 * h;
+      float* vp = p.dv + b * p.dv_sb + hd * p.dv_sh + n * p.dv_sl + 16 * h;
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) {
+        f32x4 kv = {dk[j] * p.scale, dk[j + 1] * p.scale, dk[j + 2] * p.scale, dk[j + 3] * p.scale};
+        if (p.accumulate) kv += *reinterpret_cast<const f32x4*>(kp + j);
+        *reinterpret_cast<f32x4*>(kp + j) = kv;
+        *reinterpret_cast<f32x4*>(vp + j) = f32x4{dv[j], dv[j + 1], dv[j + 2], dv[j + 3]};
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------ latent-parallel pass
 constexpr int kLatBwdTile = 64;  // tokens per LDS tile
 
@@ -427,8 +546,13 @@ __global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
   constexpr int UNITS = T * D / 8;                           // 16-byte chunks per tensor
   constexpr int UPT = (UNITS + 64 * NW - 1) / (64 * NW);     // per thread
   const int64_t tiles = (p.N + T - 1) / T;
-  bf16x8 kv[UPT], xv[UPT];
-  float l2s = 1e30f, dls = 0.f;
+  bf16x8 kv[UPT], xv[UPT], yv[UPT];
+  // decode role, held by the first thread of each token (chunk 0): the
+  // token's L / c and delta (read; or, when p.y is given, computed as dY . Y
+  // from the staged chunks once they have arrived)
+  float l2s[UPT], dls[UPT];
+  const bool self_delta = !ENC && p.y.data != nullptr;
+  const bf16* ybase = self_delta ? reinterpret_cast<const bf16*>(p.y.data) + b * p.y.sb + hd * p.y.sh : nullptr;
   auto fetch = [&](int64_t t) {
     const int64_t t0 = t * T;
 #pragma unroll
@@ -436,44 +560,68 @@ __global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
       const int u = tid + q * 64 * NW;
       const int tok = u / (D / 8), dc = u % (D / 8);
       const int64_t n = t0 + tok;
-      if (u < UNITS && n < p.N) {
+      const bool valid = u < UNITS && n < p.N;
+      if (valid) {
         kv[q] = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 8 * dc);
         xv[q] = *reinterpret_cast<const bf16x8*>(xbase + n * p.x.sl + 8 * dc);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) kv[q][j] = xv[q][j] = zero;
       }
-    }
-    if constexpr (!ENC) {
-      const int64_t n = t0 + tid;
-      if (tid < T) {
-        l2s = n < p.N ? p.lse[(int64_t)bh * p.N + n] * kLog2e / p.c : 1e30f;
-        dls = n < p.N ? p.delta[(int64_t)bh * p.N + n] : 0.f;
+      if constexpr (!ENC) {
+        if (self_delta) {
+          if (valid) {
+            yv[q] = *reinterpret_cast<const bf16x8*>(ybase + n * p.y.sl + 8 * dc);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) yv[q][j] = zero;
+          }
+        }
+        l2s[q] = 1e30f;
+        dls[q] = 0.f;
+        if (valid && dc == 0) {
+          l2s[q] = p.lse[(int64_t)bh * p.N + n] * kLog2e / p.c;
+          if (!self_delta) dls[q] = p.delta[(int64_t)bh * p.N + n];
+        }
       }
     }
   };
+  if constexpr (!ENC) {
+    if (tid == 0) augt[T] = bf16x8{};  // zero slot for the lanes of the second K half
+  }
   if (s < tiles) fetch(s);
   for (int64_t t = s; t < tiles; t += p.S) {
     __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
     for (int q = 0; q < UPT; ++q) {
       const int u = tid + q * 64 * NW;
+      const int tok = u / (D / 8), dc = u % (D / 8);
+      if constexpr (!ENC) {
+        if (self_delta) {
+          float part = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) part = fmaf((float)xv[q][j], (float)yv[q][j], part);
+          // the D / 8 chunks of a token sit in adjacent lanes of one wave
+          part += shfl_xor_f(part, 1);
+          if constexpr (D == 32) part += shfl_xor_f(part, 2);
+          dls[q] = part;
+          const int64_t n = t * T + tok;
+          if (u < UNITS && dc == 0 && n < p.N && p.delta_out && blockIdx.z == 0)
+            p.delta_out[(int64_t)bh * p.N + n] = part;
+        }
+      }
       if (u < UNITS) {
-        const int pos = lat_chunk_pos<D>(u / (D / 8), u % (D / 8));
+        const int pos = lat_chunk_pos<D>(tok, dc);
         reinterpret_cast<bf16x8*>(kt)[pos] = kv[q];
         reinterpret_cast<bf16x8*>(xt)[pos] = xv[q];
-      }
-    }
-    if constexpr (!ENC) {
-      // per token: L_n / c and delta_n as three bf16 terms each (tokens past
-      // the end get a huge finite offset: weight 0)
-      if (tid <= T) {
-        bf16x8 e = {};
-        if (tid < T) {
-          split3_bf16(l2s, e, 0);
-          split3_bf16(dls, e, 4);
+        if (!ENC && dc == 0) {
+          // per token: L_n / c and delta_n as three bf16 terms each (tokens
+          // past the end get a huge finite offset: weight 0)
+          bf16x8 e = {};
+          split3_bf16(l2s[q], e, 0);
+          split3_bf16(dls[q], e, 4);
+          augt[tok] = e;
         }
-        augt[tid] = e;
       }
     }
     __syncthreads();
@@ -565,6 +713,26 @@ hipError_t launch_tok_bwd(const TokBwdParams& p, int D, int B, bool encode_role,
     if (encode_role) { FLARE_TOK(16, true); } else { FLARE_TOK(16, false); }
   }
 #undef FLARE_TOK
+  return hipGetLastError();
+}
+
+static size_t tok_pair_lds(int M, int D) {
+  const int MC = (M + 31) / 32;
+  return (size_t)MC * (D / 16) * 64 * 16 * 3 + (size_t)MC * 2 * 64 * 16 * 2 + (size_t)(MC * 32 + 1) * 16;
+}
+
+hipError_t launch_tok_pair(const TokPairParams& p, int D, int B, hipStream_t st) {
+  if (p.M > kTokPairMaxM) return hipErrorInvalidValue;
+  dim3 grid((unsigned)p.blocks_per_head, B * p.H);
+  const size_t lds = tok_pair_lds(p.M, D);
+  hipError_t e;
+  if (D == 32) {
+    if ((e = allow_lds_bwd(tok_pair_kernel<32>, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((tok_pair_kernel<32>), grid, dim3(64 * kTokPairWaves), lds, st, p);
+  } else {
+    if ((e = allow_lds_bwd(tok_pair_kernel<16>, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL((tok_pair_kernel<16>), grid, dim3(64 * kTokPairWaves), lds, st, p);
+  }
   return hipGetLastError();
 }
 

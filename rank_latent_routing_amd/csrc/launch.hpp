@@ -70,6 +70,26 @@ struct TokBwdParams {
   int blocks_per_head;
 };
 
+// Backward of a FLARE encode/decode pair, token-parallel pass of both roles
+// at once: the scores Q K^T serve the encoder's and the decoder's weights,
+// and dK takes both roles' gradients in one accumulator.
+struct TokPairParams {
+  View k, v, dy;         // token-side bf16 [B, H, N, D]
+  View q, z, dz;         // latent-side [B, H, M, D]
+  const float* lse_e;    // encoder normalisers [B, H, M], natural log
+  const float* lse_d;    // decoder normalisers [B, H, N], natural log
+  const float* delta_d;  // dY . Y [B, H, N]
+  float* dk;             // fp32 [B, H, N, D] views
+  int64_t dk_sb, dk_sh, dk_sl;
+  float* dv;
+  int64_t dv_sb, dv_sh, dv_sl;
+  int H, M;
+  int64_t N;
+  float c, scale;
+  int accumulate;        // add into dk instead of overwriting
+  int blocks_per_head;
+};
+
 // Backward, latent-parallel pass over token splits (encoder layout): per
 // latent, fp32 partial sums of dQ (and dZ) for each split.
 //   decode role: W = Z, X = dY, per-token normaliser and delta; dQ and dZ.
@@ -78,7 +98,9 @@ struct LatBwdParams {
   View k, x;             // token-side bf16 [B, H, N, D]
   View q, w, z;          // latent-side [B, H, M, D]; z: encode role only
   const float* lse;      // [B, H, N] (decode) or [B, H, M] (encode), natural log
-  const float* delta;    // decode role: [B, H, N]
+  const float* delta;    // decode role: [B, H, N], read unless y is given
+  View y;                // decode role, optional: Y, to compute delta = dY . Y in place
+  float* delta_out;      // with y: delta written here ([B, H, N]) when non-null
   float* dq_part;        // [B*H, S, M, D]
   float* dz_part;        // decode role only
   int H, M, S;
@@ -117,6 +139,9 @@ hipError_t launch_decode_f32(const DecodeParams& p, int D, int B, hipStream_t s)
 int plan_bwd_splits(int B, int H, int M, int64_t N);
 hipError_t launch_tok_bwd(const TokBwdParams& p, int D, int B, bool encode_role, hipStream_t s);
 hipError_t launch_lat_bwd(const LatBwdParams& p, int D, int B, bool encode_role, hipStream_t s);
+// Largest M the pair pass stages (its latent operands must fit one CU's LDS).
+constexpr int kTokPairMaxM = 256;
+hipError_t launch_tok_pair(const TokPairParams& p, int D, int B, hipStream_t s);
 hipError_t launch_sum_splits(const float* part, float* out, int B, int H, int S, int64_t MD, bool batch_sum,
                              float factor, int accumulate, hipStream_t st);
 hipError_t launch_transpose_weights(const void* w, void* wt, int Cin, int Cout, hipStream_t s);

@@ -167,3 +167,15 @@ def test_backward_calls_reject_bad_arguments():
                                    0.0, ws, need, None) == fb.FLARE_E_UNSUPPORTED
     assert L.flare_encode_backward(r(ok), r(ok), r(ok), r(ok), p, p, p, r(f32), r(f32), 0, 1, 1, 8, 10, 32,
                                    float("nan"), ws, need, None) == fb.FLARE_E_INVALID
+    # the fused pair: same rules
+    need = L.flare_encdec_backward_workspace_size(1, 1, 8, 10, 32)
+    assert need >= L.flare_decode_backward_workspace_size(1, 1, 8, 10, 32)
+    pair = lambda **kw: L.flare_encdec_backward(
+        r(ok), r(kw.get("k", ok)), r(ok), r(ok), kw.get("lse", p), r(ok), p, r(ok), p, r(kw.get("dk", f32)),
+        r(f32), kw.get("flags", 0), 1, 1, 8, 10, kw.get("D", 32), 0.0, ws, kw.get("ws", need), None)
+    assert pair(k=f32) == fb.FLARE_E_UNSUPPORTED
+    assert pair(dk=ok) == fb.FLARE_E_UNSUPPORTED
+    assert pair(lse=None) == fb.FLARE_E_INVALID
+    assert pair(flags=8) == fb.FLARE_E_INVALID
+    assert pair(D=8) == fb.FLARE_E_UNSUPPORTED
+    assert pair(ws=need - 1) == fb.FLARE_E_WORKSPACE

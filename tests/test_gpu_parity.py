@@ -410,6 +410,52 @@ def test_flare_backward_chain(case):
     check_bf16(f64(dv), dvr, "dV")
 
 
+PAIR_CASES = BWD_CASES + [(2, 2, 900, 32, 300, 2.0, "head", False), (1, 2, 700, 16, 512, 4.0, "token", True)]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=lambda c: "B{}H{}N{}D{}M{}-q{}-{}-pb{}".format(*c))
+def test_flare_pair_backward(case):
+    # flare_encdec_backward: the whole FLARE pair's gradient in one call (a
+    # shared token pass for M <= 256, the two calls above that)
+    B, H, N, D, M, qm, layout, pbq = case
+    say(f"case {case}")
+    x, dy_t = _bwd_inputs(case)
+    q = x["q"].to(DEV)
+    k, v = _dev_view(x["k"], layout), _dev_view(x["v"], layout)
+    dy = _dev_view(dy_t, layout)
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True)
+    dq, dk, dv = rl.flare_encdec_backward(q, k, v, z, lse_e, y, lse_d, dy)
+    torch.cuda.synchronize()
+    dqr, dkr, dvr = oracle.flare_encdec_backward(f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"])),
+                                                 f64(hm(dy_t)))
+    check_grad(f64(dq), dqr, "dQ", dvr)
+    check_grad(f64(dk), dkr, "dK", dvr)
+    check_bf16(f64(dv), dvr, "dV")
+
+
+@pytest.mark.parametrize("M", [64, 320])
+def test_flare_pair_backward_flags(M):
+    # batch-summed dQ for shared queries, and accumulation into given dQ / dK
+    B, H, N, D = 3, 2, 1200, 32
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=M, q_mult=3.0)
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=M + 1)
+    q = x["q"].to(DEV)
+    k, v, dy = hm(x["k"]).contiguous().to(DEV), hm(x["v"]).contiguous().to(DEV), hm(dy_t).contiguous().to(DEV)
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True)
+    dq0 = inputs.normal_tensor((H, M, D), "f32", seed=5).to(DEV)
+    dk0 = inputs.normal_tensor((B, H, N, D), "f32", seed=6).to(DEV)
+    dq, dk = dq0.clone(), dk0.clone()
+    rl.flare_encdec_backward(q, k, v, z, lse_e, y, lse_d, dy, dq=dq, dk=dk,
+                             flags=rl.FLARE_SUM_DQ_OVER_BATCH | rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK)
+    torch.cuda.synchronize()
+    dqr, dkr, _ = oracle.flare_encdec_backward(f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"])), f64(hm(dy_t)))
+    check_bf16(f64(dq) - f64(dq0), dqr.sum(0), "dQ added, summed over the batch")
+    check_bf16(f64(dk) - f64(dk0), dkr, "dK added")
+
+
 @pytest.mark.parametrize("case", [(2, 3, 777, 32, 200, 4.0, "token", False),
                                   (3, 2, 1500, 16, 40, 2.0, "head", False)],
                          ids=lambda c: "B{}H{}N{}D{}M{}-q{}-{}".format(*c[:7]))

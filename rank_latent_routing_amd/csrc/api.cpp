@@ -155,12 +155,13 @@ flare_status bwd_common_checks(int B, int H, int M, int64_t N, int D, float scal
   return FLARE_OK;
 }
 
-// Workgroups per head of the token-parallel backward pass (4 waves x 64
-// tokens per step): about 2048 in all.
-int64_t tok_bwd_blocks(int B, int H, int64_t N) {
+// Workgroups per head of the token-parallel backward pass: about `total` in
+// all, each step of a workgroup covering `step` tokens (4 waves x 64 tokens in
+// the decode role; 8 x 64 in the encode role, one workgroup per CU).
+int64_t tok_bwd_blocks(int B, int H, int64_t N, int64_t step, int64_t total) {
   const int64_t bh = (int64_t)B * H;
-  const int64_t steps = (N + 255) / 256;
-  int64_t per = (2048 + bh - 1) / bh;
+  const int64_t steps = (N + step - 1) / step;
+  int64_t per = (total + bh - 1) / bh;
   if (per > steps) per = steps;
   return per < 1 ? 1 : per;
 }
@@ -501,7 +502,7 @@ flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q,
   tp.c = log2_scale(scale, D);
   tp.scale = natural_scale(scale, D);
   tp.accumulate = (flags & FLARE_ACCUMULATE_DK) ? 1 : 0;
-  tp.blocks_per_head = tok_bwd_blocks(B, H, N);
+  tp.blocks_per_head = tok_bwd_blocks(B, H, N, 256, 2048);
   hipError_t e = launch_tok_bwd(tp, D, B, false, st);
   if (e != hipSuccess) return FLARE_E_HIP;
 
@@ -601,7 +602,7 @@ flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
   tp.c = lp.c;
   tp.scale = natural_scale(scale, D);
   tp.accumulate = (flags & FLARE_ACCUMULATE_DK) ? 1 : 0;
-  tp.blocks_per_head = tok_bwd_blocks(B, H, N);
+  tp.blocks_per_head = tok_bwd_blocks(B, H, N, 512, 512);
   if ((e = launch_tok_bwd(tp, D, B, true, st)) != hipSuccess) return FLARE_E_HIP;
   return FLARE_OK;
 }

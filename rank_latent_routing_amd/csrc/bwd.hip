@@ -16,6 +16,8 @@
 // splits in the encoder's layout (lat_bwd_kernel), with fp32 partials per
 // split added by sum_splits_kernel.  The operand layouts are those of the
 // forward kernels: see encode.hip and decode.hip.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,10 +35,12 @@ __device__ __forceinline__ int bwd_chunk_latent(int ch, int u, int h, int j) {
 //                        latent 32ch + c, features 16sd + 8h .. +7);
 //   at_lds [MC][2][64]:  transposed A operand (rows are features sigma(r),
 //                        K slots latents), so each lane ends with 16
-//                        contiguous features of its token; skipped when null.
+//                        contiguous features of its token; skipped when null;
+//   alo_lds (optional):  the bf16 rounding residual of a_lds, for products
+//                        whose fp32 input must keep about 16 mantissa bits.
 template <int D>
 __device__ void stage_latent_block(const View& v, int b, int hd, int M, int MC, bf16x8* a_lds, bf16x8* at_lds,
-                                   int tid, int nt) {
+                                   int tid, int nt, bf16x8* alo_lds = nullptr) {
   constexpr int SD = D / 16;
   for (int u = tid; u < MC * SD * 64; u += nt) {
     const int ch = u / (SD * 64), sd = (u >> 6) % SD, ln = u & 63, hh = ln >> 5, cc = ln & 31;
@@ -45,10 +49,14 @@ __device__ void stage_latent_block(const View& v, int b, int hd, int M, int MC, 
 #pragma unroll
     for (int j = 0; j < 8; ++j) vv[j] = 0.f;
     if (m < M) load_as_f32<8>(v.data, v.is_f32, b * v.sb + hd * v.sh + (int64_t)m * v.sl + 16 * sd + 8 * hh, vv);
-    bf16x8 o;
+    bf16x8 o, lo;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = (bf16)vv[j];
+    for (int j = 0; j < 8; ++j) {
+      o[j] = (bf16)vv[j];
+      lo[j] = (bf16)(vv[j] - (float)o[j]);
+    }
     a_lds[(ch * SD + sd) * 64 + ln] = o;
+    if (alo_lds) alo_lds[(ch * SD + sd) * 64 + ln] = lo;
   }
   if (!at_lds) return;
   for (int u = tid; u < MC * 2 * 64; u += nt) {
@@ -66,8 +74,17 @@ __device__ void stage_latent_block(const View& v, int b, int hd, int M, int MC, 
   }
 }
 
+// The view's rows from m0 on (latent-side tensors).
+__device__ __forceinline__ View rows_from(View v, int m0) {
+  v.data = reinterpret_cast<const char*>(v.data) + (int64_t)m0 * v.sl * (v.is_f32 ? 4 : 2);
+  return v;
+}
+
 // ------------------------------------------------------- token-parallel pass
-constexpr int kTokBwdWaves = 4;
+// waves per workgroup: 4 in the decode role, 8 in the encode role (whose
+// larger latent staging leaves one workgroup per CU)
+template <bool ENC>
+constexpr int tok_bwd_waves() { return ENC ? 8 : 4; }
 
 // v as three bf16 terms, written to e[at], e[at + 1], e[at + 2], whose sum
 // carries v to about fp32 precision.
@@ -92,23 +109,30 @@ __device__ __forceinline__ void split3_bf16(float v, bf16x8& e, int at) {
 // and delta by one 16-byte read per lane and chunk.
 
 template <int D, bool ENC>
-__global__ __launch_bounds__(64 * kTokBwdWaves, 2) void tok_bwd_kernel(TokBwdParams p) {
-  constexpr int NW = kTokBwdWaves;
+__global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(TokBwdParams p) {
+  constexpr int NW = tok_bwd_waves<ENC>();
   constexpr int SD = D / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.y, b = bh / p.H, hd = bh - b * p.H;
-  const int MC = (p.M + 31) / 32;
+  // this launch's latents [m0, m0 + mb)
+  const int MC = (p.mb + 31) / 32;
+  const View qv = rows_from(p.q, p.m0), wv = rows_from(p.w, p.m0), zv = rows_from(p.z, p.m0);
   bf16x8* q_lds = reinterpret_cast<bf16x8*>(smem);
   bf16x8* w_lds = q_lds + MC * SD * 64;
   bf16x8* qt_lds = w_lds + MC * SD * 64;
   bf16x8* wt_lds = qt_lds + MC * 2 * 64;           // encode role
   bf16x8* aug_lds = wt_lds + MC * 2 * 64;          // encode role: MC * 32 latents + a zero slot
+  bf16x8* wlo_lds = aug_lds + (MC * 32 + 1);        // encode role: dZ - bf16(dZ)
 
-  stage_latent_block<D>(p.q, b, hd, p.M, MC, q_lds, qt_lds, tid, 64 * NW);
-  stage_latent_block<D>(p.w, b, hd, p.M, MC, w_lds, ENC ? wt_lds : nullptr, tid, 64 * NW);
+  stage_latent_block<D>(qv, b, hd, p.mb, MC, q_lds, qt_lds, tid, 64 * NW);
+  // In the encode role W = dZ is an fp32 gradient whose dP = dZ . V is then
+  // reduced against delta = dZ . Z: with concentrated weights the two nearly
+  // cancel, so dZ enters the product as bf16 high and low parts.
+  stage_latent_block<D>(wv, b, hd, p.mb, MC, w_lds, ENC ? wt_lds : nullptr, tid, 64 * NW,
+                        ENC ? wlo_lds : nullptr);
   if constexpr (ENC) {
     // per latent m: L_m / c (base-2 normaliser over the exponent scale) and
     // delta_m = dZ_m . Z_m, three bf16 terms each: (t1, t2, t3, 0, d1, d2, d3,
@@ -118,12 +142,12 @@ __global__ __launch_bounds__(64 * kTokBwdWaves, 2) void tok_bwd_kernel(TokBwdPar
       bf16x8 e = {};
       if (m < MC * 32) {
         float v = 1e30f, dl = 0.f;
-        if (m < p.M) {
-          v = p.lse[(int64_t)bh * p.M + m] * kLog2e / p.c;
+        if (m < p.mb) {
+          v = p.lse[(int64_t)bh * p.M + p.m0 + m] * kLog2e / p.c;
           for (int d = 0; d < D; ++d) {
             float a, z;
-            load_as_f32<1>(p.w.data, p.w.is_f32, b * p.w.sb + hd * p.w.sh + (int64_t)m * p.w.sl + d, &a);
-            load_as_f32<1>(p.z.data, p.z.is_f32, b * p.z.sb + hd * p.z.sh + (int64_t)m * p.z.sl + d, &z);
+            load_as_f32<1>(wv.data, wv.is_f32, b * wv.sb + hd * wv.sh + (int64_t)m * wv.sl + d, &a);
+            load_as_f32<1>(zv.data, zv.is_f32, b * zv.sb + hd * zv.sh + (int64_t)m * zv.sl + d, &z);
             dl = fmaf(a, z, dl);
           }
         }
@@ -191,11 +215,12 @@ __global__ __launch_bounds__(64 * kTokBwdWaves, 2) void tok_bwd_kernel(TokBwdPar
       // 32ch + 8(i/4) + 4h + i%4
       f32x16 sc[2], dp[2];
       {
-        bf16x8 qa[SD], wa[SD];
+        bf16x8 qa[SD], wa[SD], wl[SD];
 #pragma unroll
         for (int sd = 0; sd < SD; ++sd) {
           qa[sd] = q_lds[(ch * SD + sd) * 64 + lane];
           wa[sd] = w_lds[(ch * SD + sd) * 64 + lane];
+          if constexpr (ENC) wl[sd] = wlo_lds[(ch * SD + sd) * 64 + lane];
         }
         bf16x8 as = {}, ad = {};
         if constexpr (ENC) {
@@ -211,6 +236,7 @@ __global__ __launch_bounds__(64 * kTokBwdWaves, 2) void tok_bwd_kernel(TokBwdPar
           for (int sd = 0; sd < SD; ++sd) {
             sc[tb] = mfma_32x32x16(qa[sd], kb[tb][sd], sc[tb]);
             dp[tb] = mfma_32x32x16(wa[sd], xb[tb][sd], dp[tb]);
+            if constexpr (ENC) dp[tb] = mfma_32x32x16(wl[sd], xb[tb][sd], dp[tb]);
           }
           if constexpr (ENC) {
             sc[tb] = mfma_32x32x16(as, bneg, sc[tb]);
@@ -253,8 +279,11 @@ __global__ __launch_bounds__(64 * kTokBwdWaves, 2) void tok_bwd_kernel(TokBwdPar
       if constexpr (ENC) {
         float* vp = p.dv + b * p.dv_sb + hd * p.dv_sh + n * p.dv_sl + 16 * h;
 #pragma unroll
-        for (int j = 0; j < 16; j += 4)
-          *reinterpret_cast<f32x4*>(vp + j) = f32x4{dv[tb][j], dv[tb][j + 1], dv[tb][j + 2], dv[tb][j + 3]};
+        for (int j = 0; j < 16; j += 4) {
+          f32x4 vv = {dv[tb][j], dv[tb][j + 1], dv[tb][j + 2], dv[tb][j + 3]};
+          if (p.accumulate_v) vv += *reinterpret_cast<const f32x4*>(vp + j);
+          *reinterpret_cast<f32x4*>(vp + j) = vv;
+        }
       }
     }
   }
@@ -287,10 +316,13 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 3) void tok_pair_kernel(TokPair
   bf16x8* qt_lds = dz_lds + MC * SD * 64;           // A of dK^T += Q^T dS^T
   bf16x8* dzt_lds = qt_lds + MC * 2 * 64;           // A of dV^T += dZ^T P_e^T
   bf16x8* aug_lds = dzt_lds + MC * 2 * 64;          // per latent L_m / c and delta_m; zero slot
+  bf16x8* dzlo_lds = aug_lds + (MC * 32 + 1);       // dZ - bf16(dZ), the low part of dP_e's A
 
   stage_latent_block<D>(p.q, b, hd, p.M, MC, q_lds, qt_lds, tid, 64 * NW);
   stage_latent_block<D>(p.z, b, hd, p.M, MC, z_lds, nullptr, tid, 64 * NW);
-  stage_latent_block<D>(p.dz, b, hd, p.M, MC, dz_lds, dzt_lds, tid, 64 * NW);
+  // dZ enters dP_e = dZ . V as bf16 high and low parts (dP_e nearly cancels
+  // against delta_m when the encoder's weights are concentrated)
+  stage_latent_block<D>(p.dz, b, hd, p.M, MC, dz_lds, dzt_lds, tid, 64 * NW, dzlo_lds);
   for (int m = tid; m <= MC * 32; m += 64 * NW) {
     bf16x8 e = {};
     if (m < MC * 32) {
@@ -346,6 +378,7 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 3) void tok_pair_kernel(TokPair
         sc = mfma_32x32x16(q_lds[(ch * SD + sd) * 64 + lane], kb[sd], sc);
         dpd = mfma_32x32x16(z_lds[(ch * SD + sd) * 64 + lane], gb[sd], dpd);
         dpe = mfma_32x32x16(dz_lds[(ch * SD + sd) * 64 + lane], vb[sd], dpe);
+        dpe = mfma_32x32x16(dzlo_lds[(ch * SD + sd) * 64 + lane], vb[sd], dpe);
       }
       // the encoder's per-latent normaliser and delta as one more K step
       const u32x4 e = __builtin_bit_cast(u32x4, aug_lds[h == 0 ? 32 * ch + c : MC * 32]);
@@ -412,7 +445,7 @@ __global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
   const int m_lane = lat0 + wave * 32 + c;
 
   // B operands of the two products against this lane's latent: Q and W
-  bf16x8 qop[SD], wop[SD];
+  bf16x8 qop[SD], wop[SD], wlo[SD];
   float dpart = 0.f;
 #pragma unroll
   for (int sd = 0; sd < SD; ++sd) {
@@ -433,6 +466,9 @@ __global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
     for (int j = 0; j < 8; ++j) {
       qop[sd][j] = (bf16)qv[j];
       wop[sd][j] = (bf16)wv[j];
+      // encode role: W = dZ also as its bf16 rounding residual (dP = dZ . V
+      // nearly cancels against delta_m when the weights are concentrated)
+      wlo[sd][j] = (bf16)(wv[j] - (float)wop[sd][j]);
     }
   }
   // encode role: this lane's latent's base-2 normaliser and delta_m = dZ . Z
@@ -470,6 +506,7 @@ __global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
         const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xt + slot);
         sc = mfma_32x32x16(ka, qop[sd], sc);
         dp = mfma_32x32x16(xa, wop[sd], dp);
+        if constexpr (ENC) dp = mfma_32x32x16(xa, wlo[sd], dp);
       }
       if constexpr (!ENC) {
         const u32x4 e = __builtin_bit_cast(u32x4, augt[h == 0 ? 32 * qt + c : T]);
@@ -690,7 +727,7 @@ int plan_bwd_splits(int B, int H, int M, int64_t N) {
 static size_t tok_bwd_lds(int M, int D, bool enc) {
   const int MC = (M + 31) / 32;
   size_t bytes = (size_t)MC * (D / 16) * 64 * 16 * 2 + (size_t)MC * 2 * 64 * 16;
-  if (enc) bytes += (size_t)MC * 2 * 64 * 16 + (size_t)(MC * 32 + 1) * 16;
+  if (enc) bytes += (size_t)MC * 2 * 64 * 16 + (size_t)(MC * 32 + 1) * 16 + (size_t)MC * (D / 16) * 64 * 16;
   return bytes;
 }
 
@@ -702,23 +739,35 @@ static hipError_t allow_lds_bwd(K kernel, size_t bytes) {
 
 hipError_t launch_tok_bwd(const TokBwdParams& p, int D, int B, bool encode_role, hipStream_t st) {
   dim3 grid((unsigned)p.blocks_per_head, B * p.H);
-  const size_t lds = tok_bwd_lds(p.M, D, encode_role);
-  hipError_t e;
+  // The encode role stages five latent blocks: above 256 latents they would
+  // exceed one CU's LDS, so it runs per block of 256, later blocks adding
+  // into dK and dV.
+  const int step = encode_role ? 256 : p.M;
+  hipError_t e = hipSuccess;
+  for (int m0 = 0; m0 < p.M; m0 += step) {
+    TokBwdParams q = p;
+    q.m0 = m0;
+    q.mb = std::min(step, p.M - m0);
+    q.accumulate = m0 > 0 ? 1 : p.accumulate;
+    q.accumulate_v = m0 > 0 ? 1 : 0;
+    const size_t lds = tok_bwd_lds(q.mb, D, encode_role);
 #define FLARE_TOK(DD, EE)                                                                  \
   if ((e = allow_lds_bwd(tok_bwd_kernel<DD, EE>, lds)) != hipSuccess) return e;              \
-  hipLaunchKernelGGL((tok_bwd_kernel<DD, EE>), grid, dim3(64 * kTokBwdWaves), lds, st, p)
-  if (D == 32) {
-    if (encode_role) { FLARE_TOK(32, true); } else { FLARE_TOK(32, false); }
-  } else {
-    if (encode_role) { FLARE_TOK(16, true); } else { FLARE_TOK(16, false); }
-  }
+  hipLaunchKernelGGL((tok_bwd_kernel<DD, EE>), grid, dim3(64 * tok_bwd_waves<EE>()), lds, st, q)
+    if (D == 32) {
+      if (encode_role) { FLARE_TOK(32, true); } else { FLARE_TOK(32, false); }
+    } else {
+      if (encode_role) { FLARE_TOK(16, true); } else { FLARE_TOK(16, false); }
+    }
 #undef FLARE_TOK
-  return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return e;
 }
 
 static size_t tok_pair_lds(int M, int D) {
   const int MC = (M + 31) / 32;
-  return (size_t)MC * (D / 16) * 64 * 16 * 3 + (size_t)MC * 2 * 64 * 16 * 2 + (size_t)(MC * 32 + 1) * 16;
+  return (size_t)MC * (D / 16) * 64 * 16 * 4 + (size_t)MC * 2 * 64 * 16 * 2 + (size_t)(MC * 32 + 1) * 16;
 }
 
 hipError_t launch_tok_pair(const TokPairParams& p, int D, int B, hipStream_t st) {

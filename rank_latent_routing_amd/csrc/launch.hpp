@@ -68,6 +68,9 @@ struct TokBwdParams {
   float c, scale;        // c = scale * log2(e)
   int accumulate;        // add into dk instead of overwriting
   int blocks_per_head;
+  // set by the launcher: this launch covers latents [m0, m0 + mb) and adds
+  // into dv when accumulate_v (the encode role runs in latent blocks)
+  int m0, mb, accumulate_v;
 };
 
 // Backward of a FLARE encode/decode pair, token-parallel pass of both roles

@@ -539,3 +539,46 @@ def test_backward_metric_workload_full_size_one_head():
     check_bf16(f64(dq[:, h:h + 1]), dqr, "dQ head 3")
     check_bf16(f64(dk[:, h:h + 1]), dkr, "dK head 3")
     check_bf16(f64(dv[:, h:h + 1]), dvr, "dV head 3")
+
+
+def _sweep_cases(count=12, seed=2024):
+    """Seeded random shapes: ragged N, M on and off the 32-latent chunk, both
+    head dims and layouts, shared or per-batch queries, mild to sharp scores."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        B, H = int(rng.integers(1, 4)), int(rng.choice([1, 2, 3, 5]))
+        D = int(rng.choice([16, 32]))
+        M = int(rng.choice([1, 2, 31, 32, 33, 63, 100, 255, 256, 257, 384, 511, 512]))
+        N = int(rng.integers(1, 6000))
+        if B * H * N * M > 2e7:
+            continue
+        layout = str(rng.choice(["head", "token"]))
+        qm = float(rng.choice([0.5, 1.0, 3.0, 10.0]))
+        pbq = bool(rng.integers(0, 2))
+        out.append((B, H, N, D, M, layout, qm, pbq))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "B{}H{}N{}D{}M{}-{}-q{}-pb{}".format(*c))
+def test_sweep_forward_and_pair_backward(case):
+    # forward (encode, decode) and the pair's gradient on seeded random shapes
+    B, H, N, D, M, layout, qm, pbq = case
+    say(f"case {case}")
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=7 * N + M, q_mult=qm, per_batch_q=pbq)
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=N + 3)
+    q = x["q"].to(DEV)
+    k, v, dy = _dev_view(x["k"], layout), _dev_view(x["v"], layout), _dev_view(dy_t, layout)
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True)
+    dq, dk, dv = rl.flare_encdec_backward(q, k, v, z, lse_e, y, lse_d, dy)
+    torch.cuda.synchronize()
+    qo, ko, vo = f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"]))
+    zr, _ = oracle.encode(qo, ko, vo)
+    check_bf16(f64(z), zr, "Z")
+    check_bf16(f64(y), oracle.decode(ko, qo, zr), "Y")
+    dqr, dkr, dvr = oracle.flare_encdec_backward(qo, ko, vo, f64(hm(dy_t)))
+    check_grad(f64(dq), dqr, "dQ", dvr)
+    check_grad(f64(dk), dkr, "dK", dvr)
+    check_bf16(f64(dv), dvr, "dV")

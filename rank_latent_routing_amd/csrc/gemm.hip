@@ -4,10 +4,12 @@
 // latent routing", the extra eK, eV of equation 7, and the output
 // projection).  At C <= 256 the reduction is short and the outputs outweigh
 // the input, so the kernel is built around HBM traffic:
-//   - a wave loads its 64 rows of X once into registers, already as the B
+//   - a wave loads its 32 rows of X once into registers, already as the B
 //     operand of Y^T = W^T X^T (lane (g, r): row r, inputs 8g..8g+7 of each
 //     32-wide step), and keeps them for every output column of every
-//     projection, so X is read from HBM once;
+//     projection, so X is read from HBM once (32 rows keep it at 64
+//     registers: two 8-wave workgroups per CU, one loading while the other
+//     computes and stores);
 //   - the weights are rearranged once per call into operand order, in
 //     32-column blocks of 2 KB per k-step; the workgroup streams the blocks
 //     into LDS with buffer loads straight to LDS (four stages, three blocks in
@@ -46,12 +48,14 @@ __global__ __launch_bounds__(256) void swizzle_weights_kernel(const bf16* __rest
   wsw[idx] = w[(int64_t)c * Cout + col];
 }
 
-constexpr int kGemmRowsPerWave = 64;  // four 16-row tiles
+constexpr int kGemmTiles = 2;                          // 16-row tiles per wave
+constexpr int kGemmRowsPerWave = 16 * kGemmTiles;
 constexpr int kGemmWaves = 8;
 constexpr int kGemmRowsPerBlock = kGemmRowsPerWave * kGemmWaves;
 
 template <int CIN>
-__global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * kGemmWaves, 4) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int RB = kGemmTiles;
   constexpr int NW = kGemmWaves;
   constexpr int KS = CIN / 32;
   constexpr int BLK = KS * 2 * 512;  // bf16 elements of one 32-column block
@@ -72,9 +76,9 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_kernel(GemmParam
   const int my_ops = wave * OPW < OPS ? OPW : 0;
 
   // X rows as B operands, held for all output columns.
-  bf16x8 xb[4][KS];
+  bf16x8 xb[RB][KS];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int64_t row = row0 + 16 * rb + r;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -106,9 +110,9 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_kernel(GemmParam
   // Element offset of (row row0 + 16 rb + r, column 0) in the output: row-major
   // [R, Cout], or head-major [B, H, N, D] with R = B N (head 0 of the row's
   // token; a column c adds (c / D) N D + c % D).
-  int64_t row_off[4];
+  int64_t row_off[RB];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int64_t row = min(row0 + 16 * rb + r, p.R - 1);
     if (p.head_major) {
       const int64_t bi = row / p.N, n = row - bi * p.N;
@@ -135,9 +139,9 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_kernel(GemmParam
   auto compute_block = [&](auto stage_tag, int b) {
     constexpr int S = decltype(stage_tag)::value;
     const bf16* st = S == 0 ? s0 : S == 1 ? s1 : S == 2 ? s2 : s3;
-    f32x4 acc[4][2];
+    f32x4 acc[RB][2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) acc[rb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_kernel(GemmParam
       for (int t = 0; t < 2; ++t) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + ((ks * 2 + t) * 64 + lane) * 8);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[rb][t] = mfma_16x16x32(a, xb[rb][ks], acc[rb][t]);
+        for (int rb = 0; rb < RB; ++rb) acc[rb][t] = mfma_16x16x32(a, xb[rb][ks], acc[rb][t]);
       }
     const int pr = b / pairs, pb = b - pr * pairs;
     const int col = 32 * pb + 8 * g;
@@ -156,12 +160,12 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_kernel(GemmParam
       col_off = (int64_t)hd * p.N * p.D + (col - hd * p.D);
     }
     if (full_rows) {
-      // exactly four stores per block: the step's wait counts them
+      // exactly RB stores per block: the step's wait counts them
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) store_row_tile(acc[rb], rb, pr, col_off);
+      for (int rb = 0; rb < RB; ++rb) store_row_tile(acc[rb], rb, pr, col_off);
     } else {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
         if (row0 + 16 * rb + r < p.R) store_row_tile(acc[rb], rb, pr, col_off);
     }
   };
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_kernel(GemmParam
   // Block b lives in stage b % 4.  Step b: start the load of block b + 3,
   // compute and store block b, then wait until this wave's load of block
   // b + 1 has landed (vmcnt counts loads and stores in issue order: the
-  // loads of blocks b + 2 and b + 3 and the four stores of block b may stay
+  // loads of blocks b + 2 and b + 3 and the RB stores of block b may stay
   // in flight) and meet at the barrier.
   auto step = [&](auto stage_tag, int b) {
     constexpr int S = decltype(stage_tag)::value;
@@ -179,11 +183,11 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_kernel(GemmParam
     if (!full_rows)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     else if (later == 2)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * OPW + 4));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * OPW + RB));
     else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(OPW + 4));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(OPW + RB));
     else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(RB));
     barrier_keep_loads();
   };
 

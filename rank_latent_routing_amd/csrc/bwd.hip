@@ -88,6 +88,9 @@ constexpr int tok_bwd_waves() { return ENC ? 8 : 4; }
 
 // v as three bf16 terms, written to e[at], e[at + 1], e[at + 2], whose sum
 // carries v to about fp32 precision.
+// The offset L / c of a padded row: c (S - offset) is then about -2.5e29 |c|
+// for either sign of the exponent scale c, so the row's weight is exactly 0.
+__device__ __forceinline__ float pad_offset(float c) { return c > 0.f ? 1e30f : -1e30f; }
 __device__ __forceinline__ void split3_bf16(float v, bf16x8& e, int at) {
   const bf16 a = (bf16)v;
   float r = v - (float)a;
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
     for (int m = tid; m <= MC * 32; m += 64 * NW) {
       bf16x8 e = {};
       if (m < MC * 32) {
-        float v = 1e30f, dl = 0.f;
+        float v = pad_offset(p.c), dl = 0.f;
         if (m < p.mb) {
           v = p.lse[(int64_t)bh * p.M + p.m0 + m] * kLog2e / p.c;
           for (int d = 0; d < D; ++d) {
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 3) void tok_pair_kernel(TokPair
   for (int m = tid; m <= MC * 32; m += 64 * NW) {
     bf16x8 e = {};
     if (m < MC * 32) {
-      float v = 1e30f, dl = 0.f;
+      float v = pad_offset(p.c), dl = 0.f;
       if (m < p.M) {
         v = p.lse_e[(int64_t)bh * p.M + m] * kLog2e / p.c;
         for (int d = 0; d < D; ++d) {
@@ -614,7 +617,7 @@ __global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
             for (int j = 0; j < 8; ++j) yv[q][j] = zero;
           }
         }
-        l2s[q] = 1e30f;
+        l2s[q] = pad_offset(p.c);
         dls[q] = 0.f;
         if (valid && dc == 0) {
           l2s[q] = p.lse[(int64_t)bh * p.N + n] * kLog2e / p.c;

@@ -582,3 +582,31 @@ def test_sweep_forward_and_pair_backward(case):
     check_grad(f64(dq), dqr, "dQ", dvr)
     check_grad(f64(dk), dkr, "dK", dvr)
     check_bf16(f64(dv), dvr, "dV")
+
+
+@pytest.mark.parametrize("D,M", [(32, 40), (16, 300)])
+def test_negative_scale_forward_and_backward(D, M):
+    # a negative softmax scale is legal SDPA (weights favour the lowest
+    # scores); padded rows and ragged tokens must still get weight 0
+    B, H, N, scale = 2, 2, 777, -0.3
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=M + 1, q_mult=3.0)
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=M + 2)
+    q = x["q"].to(DEV)
+    k, v, dy = hm(x["k"]).contiguous().to(DEV), hm(x["v"]).contiguous().to(DEV), hm(dy_t).contiguous().to(DEV)
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32, scale=scale)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True, scale=scale)
+    dq, dk, dv = rl.flare_encdec_backward(q, k, v, z, lse_e, y, lse_d, dy, scale=scale)
+    dk1, dq1, dz1 = rl.flare_decode_backward(k, q, z, y, lse_d, dy, scale=scale)
+    dq1, dk1, dv1 = rl.flare_encode_backward(q, k, v, z, lse_e, dz1, dq=dq1, dk=dk1, scale=scale,
+                                             flags=rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK)
+    torch.cuda.synchronize()
+    qo, ko, vo = f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"]))
+    zr, _ = oracle.encode(qo, ko, vo, scale)
+    check_bf16(f64(z), zr, "Z")
+    check_bf16(f64(y), oracle.decode(ko, qo, zr, scale), "Y")
+    dqr, dkr, dvr = oracle.flare_encdec_backward(qo, ko, vo, f64(hm(dy_t)), scale)
+    for tag, (a, b_, c_) in (("one call", (dq, dk, dv)), ("two calls", (dq1, dk1, dv1))):
+        check_bf16(f64(a), dqr, f"dQ ({tag})")
+        check_bf16(f64(b_), dkr, f"dK ({tag})")
+        check_bf16(f64(c_), dvr, f"dV ({tag})")

@@ -610,3 +610,30 @@ def test_negative_scale_forward_and_backward(D, M):
         check_bf16(f64(a), dqr, f"dQ ({tag})")
         check_bf16(f64(b_), dkr, f"dK ({tag})")
         check_bf16(f64(c_), dvr, f"dV ({tag})")
+
+
+def test_pair_backward_token_major_gradients():
+    # dK, dV written into token-major [B, N, H, D] fp32 views (strided per head),
+    # through the one-call and the two-call backward
+    B, H, N, D, M = 2, 3, 1100, 32, 96
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=31, q_mult=2.0)
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=32)
+    q = x["q"].to(DEV)
+    k, v, dy = hm(x["k"].to(DEV)), hm(x["v"].to(DEV)), hm(dy_t.to(DEV))
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True)
+    tm = lambda: hm(torch.full((B, N, H, D), float("nan"), dtype=torch.float32, device=DEV))
+    dk, dv = tm(), tm()
+    dq, _, _ = rl.flare_encdec_backward(q, k, v, z, lse_e, y, lse_d, dy, dk=dk, dv=dv)
+    dk2, dv2 = tm(), tm()
+    _, dq2, dz2 = rl.flare_decode_backward(k, q, z, y, lse_d, dy, dk=dk2)
+    dq2, _, _ = rl.flare_encode_backward(q, k, v, z, lse_e, dz2, dq=dq2, dk=dk2, dv=dv2,
+                                         flags=rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK)
+    torch.cuda.synchronize()
+    dqr, dkr, dvr = oracle.flare_encdec_backward(f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"])),
+                                                 f64(hm(dy_t)))
+    for tag, (a, b_, c_) in (("one call", (dq, dk, dv)), ("two calls", (dq2, dk2, dv2))):
+        check_bf16(f64(a), dqr, f"dQ ({tag})")
+        check_bf16(f64(b_), dkr, f"dK ({tag})")
+        check_bf16(f64(c_), dvr, f"dV ({tag})")

@@ -340,6 +340,51 @@ def main():
                                        "operations": round(mwk.flops / fwk.flops, 3),
                                        "shared_time": round(sms / fms, 3),
                                        "shared_operations": round(swk.flops / fwk.flops, 3)}
+        del m, out, mws
+
+        # The small FLARE++ mixer (B=8, N=4096, C=128, H=8, D=16, M=64): a
+        # dozen short launches per call, so launch overhead matters; timed as
+        # eager calls and as replays of one captured HIP graph.
+        sw = inputs.WORKLOADS["mix_bf16_n4k_c128"]
+        sm = {n: t.to(dev) for n, t in inputs.make_mix(sw, seed=0).items()}
+        sout = torch.empty_like(sm["x"])
+        sws = torch.empty(rl.mix_workspace_size(sw.B, sw.N, sw.C, sw.H, sw.M, True, False), dtype=torch.uint8,
+                          device=dev)
+
+        def small_mix(s=stream):
+            rl.flare_mix(sm["x"], sm["w_k"], sm["w_v"], sm["qs"], sw.H, w_ek=sm["w_ek"], w_ev=sm["w_ev"],
+                         out=sout, workspace=sws, stream=s)
+        reps = 50
+        for _ in range(5):
+            small_mix()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            small_mix()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / reps
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()  # capture needs a side stream; replays go on the launch stream
+        with torch.cuda.graph(graph, stream=cap):
+            small_mix(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / reps
+        extra["small_flarepp_mixer"] = {
+            "config": "FLARE++ mixer, B=8, N=4096, C=128, H=8, D=16, M=64, bf16, no W_O",
+            "eager_ms": round(eager_ms, 4), "graph_ms": round(graph_ms, 4),
+            "tokens_per_s_graph": sw.B * sw.N / (graph_ms / 1e3)}
+        del graph, sm, sout, sws
 
     cpu = None
     if not args.no_cpu:

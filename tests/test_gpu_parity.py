@@ -637,3 +637,54 @@ def test_pair_backward_token_major_gradients():
         check_bf16(f64(a), dqr, f"dQ ({tag})")
         check_bf16(f64(b_), dkr, f"dK ({tag})")
         check_bf16(f64(c_), dvr, f"dV ({tag})")
+
+
+def test_graph_capture_replays_match_eager():
+    # flare_mix (FLARE++, B=8, N=4096, C=128, M=64) and the pair backward
+    # captured into HIP graphs: the library issues only kernel launches on the
+    # caller's stream (no memset, allocation or synchronisation), so every
+    # replay, with eager work and synchronisations between replays, must equal
+    # the eager result bit for bit
+    w = inputs.WORKLOADS["mix_bf16_n4k_c128"]
+    m = inputs.make_mix(w, seed=3, q_mult=4.0)
+    g = {n: t.to(DEV) for n, t in m.items()}
+    B, N, C, H, M = w.B, w.N, w.C, w.H, w.M
+    out = torch.empty_like(g["x"])
+    ws = torch.empty(rl.mix_workspace_size(B, N, C, H, M, True, False), dtype=torch.uint8, device=DEV)
+    mix = lambda s: rl.flare_mix(g["x"], g["w_k"], g["w_v"], g["qs"], H, w_ek=g["w_ek"], w_ev=g["w_ev"],
+                                 out=out, workspace=ws, stream=s)
+    D = C // H
+    e = inputs.make_encdec(inputs.Workload("t", "encdec", 2, 3000, 4, 32, 100, "bf16"), seed=5, q_mult=2.0)
+    q = e["q"].to(DEV)
+    k, v = hm(e["k"]).contiguous().to(DEV), hm(e["v"]).contiguous().to(DEV)
+    dy = hm(inputs.normal_tensor((2, 3000, 4, 32), "bf16", seed=6)).contiguous().to(DEV)
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True)
+    dq = torch.empty((4, 100, 32), dtype=torch.float32, device=DEV)
+    dk = torch.empty((2, 4, 3000, 32), dtype=torch.float32, device=DEV)
+    dv = torch.empty_like(dk)
+    wsb = torch.empty(rl.lib().flare_encdec_backward_workspace_size(2, 4, 100, 3000, 32), dtype=torch.uint8,
+                      device=DEV)
+    bwd = lambda s: rl.flare_encdec_backward(q, k, v, z, lse_e, y, lse_d, dy, dq=dq, dk=dk, dv=dv,
+                                             flags=rl.FLARE_SUM_DQ_OVER_BATCH, workspace=wsb, stream=s)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        mix(stream)
+        bwd(stream)
+    torch.cuda.synchronize()
+    ref = [out.clone(), dq.clone(), dk.clone(), dv.clone()]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        mix(stream)
+        bwd(stream)
+    for i in range(4):
+        for t in (out, dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [out, dq, dk, dv]
+        for r, gt, name in zip(ref, got, ("out", "dQ", "dK", "dV")):
+            assert torch.equal(r, gt), (i, name)
+        _ = (g["x"].float() * 2).sum().item()  # eager work between replays
+    say(f"  4 replays equal to the eager run (D={D})")

@@ -166,11 +166,11 @@ int64_t tok_bwd_blocks(int B, int H, int64_t N, int64_t step, int64_t total) {
   return per < 1 ? 1 : per;
 }
 
-// Workgroups per head of the pair pass (12 waves x 32 tokens per step): one
+// Workgroups per head of the pair pass (8 waves x 32 tokens per step): one
 // per CU in all, so each stages its head's latent operands once.
 int64_t tok_pair_blocks(int B, int H, int64_t N) {
   const int64_t bh = (int64_t)B * H;
-  const int64_t steps = (N + 383) / 384;
+  const int64_t steps = (N + 255) / 256;
   int64_t per = (256 + bh - 1) / bh;
   if (per > steps) per = steps;
   return per < 1 ? 1 : per;

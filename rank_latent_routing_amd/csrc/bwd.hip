@@ -301,10 +301,10 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
 //   dv_n = sum_m P_e dZ_m,
 // with P_d, dP_d = dY_n . Z_m from the decoder and P_e, dP_e = dZ_m . V_n from
 // the encoder.  dK is written once, with no second pass reading it back.
-constexpr int kTokPairWaves = 12;
+constexpr int kTokPairWaves = 8;
 
 template <int D>
-__global__ __launch_bounds__(64 * kTokPairWaves, 3) void tok_pair_kernel(TokPairParams p) {
+__global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPairParams p) {
   constexpr int NW = kTokPairWaves;
   constexpr int SD = D / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -353,24 +353,43 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 3) void tok_pair_kernel(TokPair
   const bf16* gbase = reinterpret_cast<const bf16*>(p.dy.data) + b * p.dy.sb + hd * p.dy.sh;
   const float cs = p.c;
   const int64_t stride = (int64_t)gridDim.x * NW * 32;
-  for (int64_t base = ((int64_t)blockIdx.x * NW + wave) * 32; base < p.N; base += stride) {
-    // lane (h, c): token n; B operands hold features 16sd + 8h .. +7
+  // The wave's next 32 tokens are loaded while the current ones are
+  // computed: lane (h, c) holds token n, B operands with features
+  // 16sd + 8h .. +7 of K, V and dY, and the token's normaliser and delta.
+  bf16x8 nk[SD], nv[SD], ng[SD];
+  float nl2 = 0.f, ndd = 0.f;
+  auto fetch = [&](int64_t base) {
+    const int64_t n = base + c;
+    const bool valid = n < p.N;
+#pragma unroll
+    for (int sd = 0; sd < SD; ++sd) {
+      if (valid) {
+        nk[sd] = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 16 * sd + 8 * h);
+        nv[sd] = *reinterpret_cast<const bf16x8*>(vbase + n * p.v.sl + 16 * sd + 8 * h);
+        ng[sd] = *reinterpret_cast<const bf16x8*>(gbase + n * p.dy.sl + 16 * sd + 8 * h);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) nk[sd][j] = nv[sd][j] = ng[sd][j] = (bf16)0.0f;
+      }
+    }
+    nl2 = valid ? p.lse_d[(int64_t)bh * p.N + n] : 0.f;
+    ndd = valid ? p.delta_d[(int64_t)bh * p.N + n] : 0.f;
+  };
+  int64_t base = ((int64_t)blockIdx.x * NW + wave) * 32;
+  if (base < p.N) fetch(base);
+  for (; base < p.N; base += stride) {
     const int64_t n = base + c;
     const bool valid = n < p.N;
     bf16x8 kb[SD], vb[SD], gb[SD];
 #pragma unroll
     for (int sd = 0; sd < SD; ++sd) {
-      if (valid) {
-        kb[sd] = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 16 * sd + 8 * h);
-        vb[sd] = *reinterpret_cast<const bf16x8*>(vbase + n * p.v.sl + 16 * sd + 8 * h);
-        gb[sd] = *reinterpret_cast<const bf16x8*>(gbase + n * p.dy.sl + 16 * sd + 8 * h);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kb[sd][j] = vb[sd][j] = gb[sd][j] = (bf16)0.0f;
-      }
+      kb[sd] = nk[sd];
+      vb[sd] = nv[sd];
+      gb[sd] = ng[sd];
     }
-    const float l2d = valid ? p.lse_d[(int64_t)bh * p.N + n] * kLog2e : 0.f;
-    const float dd = valid ? p.delta_d[(int64_t)bh * p.N + n] : 0.f;
+    const float l2d = nl2 * kLog2e;
+    const float dd = ndd;
+    if (base + stride < p.N) fetch(base + stride);
 
     f32x16 dk = zero16(), dv = zero16();
     for (int ch = 0; ch < MC; ++ch) {

@@ -688,3 +688,34 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(r, gt), (i, name)
         _ = (g["x"].float() * 2).sum().item()  # eager work between replays
     say(f"  4 replays equal to the eager run (D={D})")
+
+
+@pytest.mark.parametrize("qm,flags", [(40.0, 0), (3.0, EXACT)])
+def test_backward_after_exact_forward(qm, flags):
+    # scores far outside the range-checked fast softmax (queries x40: exponents
+    # in the hundreds) send the forward calls through their exact
+    # running-maximum path, whose normalisers the backward then uses; the
+    # same with the exact path forced on ordinary scores
+    B, H, N, D, M = 1, 2, 2000, 32, 64
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=41, q_mult=qm)
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=42)
+    q = x["q"].to(DEV)
+    k, v, dy = hm(x["k"]).contiguous().to(DEV), hm(x["v"]).contiguous().to(DEV), hm(dy_t).contiguous().to(DEV)
+    z, lse_e = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32, flags=flags)
+    y, lse_d = rl.flare_decode(k, q, z, want_lse=True, flags=flags)
+    dq, dk, dv = rl.flare_encdec_backward(q, k, v, z, lse_e, y, lse_d, dy)
+    torch.cuda.synchronize()
+    qo, ko, vo = f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"]))
+    zr, lr = oracle.encode(qo, ko, vo)
+    check_bf16(f64(z), zr, "Z")
+    yr = oracle.decode(ko, qo, zr)
+    check_bf16(f64(y), yr, "Y")
+    _, ld = oracle.sdpa(ko[0, 0], qo[0], zr[0, 0], return_lse=True)
+    el = float(np.max(np.abs(f64(lse_d)[0, 0] - ld)))
+    say(f"  decoder lse (head 0): max abs err {el:.3e}, max |lse| {np.max(np.abs(ld)):.1f}")
+    assert el <= 1e-2 * max(1.0, float(np.max(np.abs(ld))))
+    dqr, dkr, dvr = oracle.flare_encdec_backward(qo, ko, vo, f64(hm(dy_t)))
+    check_grad(f64(dq), dqr, "dQ", dvr)
+    check_grad(f64(dk), dkr, "dK", dvr)
+    check_bf16(f64(dv), dvr, "dV")

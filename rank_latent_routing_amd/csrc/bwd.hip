@@ -12,10 +12,11 @@
 //
 // Every gradient is a sum over one axis of the token x latent score matrix.
 // Sums over latents (dK, dV) run token-parallel in the decoder's layout
-// (tok_bwd_kernel); sums over tokens (dQ, dZ) run latent-parallel over token
-// splits in the encoder's layout (lat_bwd_kernel), with fp32 partials per
-// split added by sum_splits_kernel.  The operand layouts are those of the
-// forward kernels: see encode.hip and decode.hip.
+// (tok_bwd_kernel, one call's role; tok_pair_kernel, both roles of a FLARE
+// encode/decode pair at once); sums over tokens (dQ, dZ) run latent-parallel
+// over token splits in the encoder's layout (lat_bwd_kernel), with fp32
+// partials per split added by sum_splits_kernel.  The operand layouts are
+// those of the forward kernels: see encode.hip and decode.hip.
 #include <algorithm>
 
 #include "common.hpp"
@@ -86,11 +87,12 @@ __device__ __forceinline__ View rows_from(View v, int m0) {
 template <bool ENC>
 constexpr int tok_bwd_waves() { return ENC ? 8 : 4; }
 
-// v as three bf16 terms, written to e[at], e[at + 1], e[at + 2], whose sum
-// carries v to about fp32 precision.
 // The offset L / c of a padded row: c (S - offset) is then about -2.5e29 |c|
 // for either sign of the exponent scale c, so the row's weight is exactly 0.
 __device__ __forceinline__ float pad_offset(float c) { return c > 0.f ? 1e30f : -1e30f; }
+
+// v as three bf16 terms, written to e[at], e[at + 1], e[at + 2], whose sum
+// carries v to about fp32 precision.
 __device__ __forceinline__ void split3_bf16(float v, bf16x8& e, int at) {
   const bf16 a = (bf16)v;
   float r = v - (float)a;
@@ -452,6 +454,13 @@ __device__ __forceinline__ int lat_chunk_pos(int token, int dc) {
   else return token * 2 + (dc ^ ((token >> 2) & 1));
 }
 
+// One workgroup is (batch*head, token split s, block of 32 NW latents); each
+// wave owns 32 latents, one per lane column of its score tiles.  The split's
+// 64-token tiles s, s + S, ... pass through registers (loaded one tile ahead)
+// into LDS, shared by all waves; per tile a wave forms S^T and dP^T for its
+// latents, the weights and score gradients, and adds dQ (and in the decode
+// role dZ) by products with the staged tokens.  It ends by writing its
+// split's fp32 partials.
 template <int D, bool ENC, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
   constexpr int SD = D / 16;

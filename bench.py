@@ -386,6 +386,35 @@ def main():
             "tokens_per_s_graph": sw.B * sw.N / (graph_ms / 1e3)}
         del graph, sm, sout, sws
 
+        # The two other FLARE++ mixer workloads at full size: the sequence
+        # workload (B=32, N=4096, C=256, M=128, no W_O) and the block workload
+        # (B=4, N=262144, C=256, M=512, with W_O).
+        for key, label in (("seq_bf16_b32_n4k", "FLARE++ sequence mixer"), ("block_bf16_n256k", "FLARE++ block")):
+            ww = inputs.WORKLOADS[key]
+            wm = {n: t.to(dev) for n, t in inputs.make_mix(ww, seed=0).items()}
+            wout = torch.empty_like(wm["x"])
+            wws = torch.empty(rl.mix_workspace_size(ww.B, ww.N, ww.C, ww.H, ww.M, True, ww.has_wo),
+                              dtype=torch.uint8, device=dev)
+
+            def run_w():
+                rl.flare_mix(wm["x"], wm["w_k"], wm["w_v"], wm["qs"], ww.H, w_ek=wm["w_ek"], w_ev=wm["w_ev"],
+                             w_o=wm.get("w_o"), out=wout, workspace=wws, stream=stream)
+            for _ in range(3):
+                run_w()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(10):
+                run_w()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wms = e0.elapsed_time(e1) / 10
+            wk = costs.mixer(ww.B, ww.N, ww.C, ww.H, ww.M, dynamic=True, has_wo=ww.has_wo)
+            extra[key] = {"config": f"{label}, B={ww.B}, N={ww.N}, C={ww.C}, H={ww.H}, D={ww.D}, M={ww.M}, bf16"
+                                    + (", with W_O" if ww.has_wo else ""),
+                          "ms": round(wms, 4), "tokens_per_s": ww.B * ww.N / (wms / 1e3),
+                          "tflops": round(wk.flops / (wms / 1e3) / 1e12, 1)}
+            del wm, wout, wws
+
     cpu = None
     if not args.no_cpu:
         import oracle

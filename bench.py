@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-mix", action="store_true", help="skip the FLARE++ mixer measurement")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the sweep over the token count")
     ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle sample")
     ap.add_argument("--y-layout", choices=("token", "head"), default="token")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -414,6 +415,75 @@ def main():
                           "ms": round(wms, 4), "tokens_per_s": ww.B * ww.N / (wms / 1e3),
                           "tflops": round(wk.flops / (wms / 1e3) / 1e12, 1)}
             del wm, wout, wws
+
+    if not args.no_sweep:
+        # Time and memory against the token count, three orders of magnitude
+        # and more (H=8, D=32, M=256, bf16, B=1): FLARE encode+decode, and the
+        # whole FLARE++ mixer with all projections at C=256.  Memory is the peak
+        # of device memory allocated for the call's inputs, outputs and
+        # workspace.
+        sweep = []
+        for n_tok in (1 << 10, 1 << 12, 1 << 14, 1 << 16, 1 << 18, 1 << 20, 1 << 22):
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            base_mem = torch.cuda.memory_allocated()
+            sw_ = inputs.Workload("sweep", "encdec", 1, n_tok, H, D, M, "bf16")
+            sx = inputs.make_encdec(sw_, seed=1)
+            sq = sx["q"].to(dev)
+            sk = sx["k"].to(dev).permute(0, 2, 1, 3).contiguous()
+            sv = sx["v"].to(dev).permute(0, 2, 1, 3).contiguous()
+            del sx
+            sz = torch.empty((1, H, M, D), dtype=torch.bfloat16, device=dev)
+            syt = torch.empty((1, n_tok, H, D), dtype=torch.bfloat16, device=dev)
+            sy = syt.permute(0, 2, 1, 3)
+            sws = torch.empty(rl.encode_workspace_size(1, H, M, n_tok, D), dtype=torch.uint8, device=dev)
+
+            def encdec():
+                rl.flare_encode(sq, sk, sv, z=sz, workspace=sws, stream=stream)
+                rl.flare_decode(sk, sq, sz, y=sy, stream=stream)
+            reps = max(5, min(200, (1 << 24) // n_tok))
+            for _ in range(3):
+                encdec()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                encdec()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ems = e0.elapsed_time(e1) / reps
+            emem = (torch.cuda.max_memory_allocated() - base_mem) / 1e9
+            del sq, sk, sv, sz, syt, sy, sws
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            base_mem = torch.cuda.memory_allocated()
+            mw_ = inputs.Workload("sweep_mix", "mix", 1, n_tok, H, D, M, "bf16", dynamic=True, has_wo=True)
+            mm = {nm: t.to(dev) for nm, t in inputs.make_mix(mw_, seed=1).items()}
+            mout = torch.empty_like(mm["x"])
+            mws2 = torch.empty(rl.mix_workspace_size(1, n_tok, mw_.C, H, M, True, True), dtype=torch.uint8,
+                               device=dev)
+
+            def mixer():
+                rl.flare_mix(mm["x"], mm["w_k"], mm["w_v"], mm["qs"], H, w_ek=mm["w_ek"], w_ev=mm["w_ev"],
+                             w_o=mm["w_o"], out=mout, workspace=mws2, stream=stream)
+            for _ in range(3):
+                mixer()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                mixer()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mms_ = e0.elapsed_time(e1) / reps
+            mmem = (torch.cuda.max_memory_allocated() - base_mem) / 1e9
+            del mm, mout, mws2
+            sweep.append({"N": n_tok, "encdec_ms": round(ems, 4), "encdec_tokens_per_s": n_tok / (ems / 1e3),
+                          "encdec_mem_GB": round(emem, 4), "flarepp_mixer_ms": round(mms_, 4),
+                          "flarepp_mixer_tokens_per_s": n_tok / (mms_ / 1e3), "flarepp_mixer_mem_GB": round(mmem, 4)})
+        extra["n_sweep"] = {"config": "B=1, H=8, D=32, M=256, bf16; FLARE encode+decode, and the FLARE++ mixer "
+                                      "with all projections at C=256; memory = peak device memory of inputs, "
+                                      "outputs and workspace",
+                            "points": sweep}
 
     cpu = None
     if not args.no_cpu:

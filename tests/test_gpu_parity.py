@@ -123,6 +123,32 @@ def test_decode_alone_with_oracle_latents():
     check_bf16(f64(y), yr, "Y(decode only)", per_bh_axes=True)
 
 
+@pytest.mark.parametrize("z_dtype", [torch.float32, torch.bfloat16])
+def test_decode_large_latent_values(z_dtype):
+    # Head 0: latent values near 1e15 and a common score offset of about 55
+    # (feature 0 of every key 8, of every query 39), so the unscaled weights
+    # sum to about e^60 (inside the fast pass's accepted normaliser range) and
+    # the unnormalised outputs overflow fp32: the kernel must notice and redo
+    # the head with the row maximum subtracted.  Head 1: the same magnitudes
+    # without the offset (fast result kept).  Head 2: ordinary values.
+    B, H, N, D, M = 1, 3, 1500, 32, 80
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=11)
+    q, k = x["q"].clone(), x["k"].clone()
+    q[0, :, 0] = 39.0
+    k[:, :, 0, 0] = 8.0
+    z = inputs.normal_tensor((B, H, M, D), "f32", seed=12)
+    z[:, :2] *= 1e15
+    z = z.to(z_dtype)
+    qo, ko = f64(q), f64(hm(k))
+    yr = oracle.decode(ko, qo, f64(z))
+    y = rl.flare_decode(hm(k).contiguous().to(DEV), q.to(DEV), z.to(DEV))
+    torch.cuda.synchronize()
+    got = f64(y)
+    assert np.all(np.isfinite(got))
+    check_bf16(got, yr, "Y(large latents)", per_bh_axes=True)
+
+
 @pytest.mark.parametrize("qm", [1.0, 6.0])
 def test_route_queries_shared_seeds(qm):
     B, H, N, D, M = 3, 4, 2500, 32, 64

@@ -199,13 +199,18 @@ flare_status project_impl(const void* X, const void* const* W, void* const* Y, i
   gp.head_major = head_major;
   gp.N = head_major ? R / B : R;
   gp.D = head_major ? head_dim : Cout;
+  SwizzleParams sp;
+  std::memset(&sp, 0, sizeof(sp));
+  sp.Cin = Cin;
+  sp.Cout = Cout;
   for (int i = 0; i < n_proj; ++i) {
     void* wt = reinterpret_cast<char*>(ws) + i * align_up((size_t)Cin * Cout * 2);
-    hipError_t e = launch_transpose_weights(W[i], wt, Cin, Cout, st);
-    if (e != hipSuccess) return FLARE_E_HIP;
+    sp.w[i] = W[i];
+    sp.wsw[i] = wt;
     gp.wt[i] = wt;
     gp.y[i] = Y[i];
   }
+  if (launch_swizzle_weights(sp, n_proj, st) != hipSuccess) return FLARE_E_HIP;
   return hip_status(launch_gemm_bf16(gp, st));
 }
 

@@ -29,23 +29,26 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // columns as 64 lanes x 8 bf16,
 //   wsw[((pb KS + ks) 2 + t) 512 + 8 lane + j]
 //     = W[32 ks + 8 (lane / 16) + j][32 pb + 8 (m / 4) + 4 t + m % 4],  m = lane % 16.
-__global__ __launch_bounds__(256) void swizzle_weights_kernel(const bf16* __restrict__ w,
-                                                              bf16* __restrict__ wsw, int Cin,
-                                                              int Cout) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)Cin * Cout;
-  if (idx >= total) return;
-  const int j = (int)(idx & 7);
-  const int lane = (int)((idx >> 3) & 63);
-  const int t = (int)((idx >> 9) & 1);
-  const int64_t rest = idx >> 10;
-  const int KS = Cin / 32;
+// One thread writes the 8 values of one (pb, ks, t, lane) as a 16-byte store;
+// blockIdx.y picks the weight, so one launch serves every projection.
+__global__ __launch_bounds__(256) void swizzle_weights_kernel(SwizzleParams p) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (int64_t)p.Cin * p.Cout / 8) return;
+  const bf16* __restrict__ w = reinterpret_cast<const bf16*>(p.w[blockIdx.y]);
+  bf16x8* __restrict__ wsw = reinterpret_cast<bf16x8*>(p.wsw[blockIdx.y]);
+  const int lane = (int)(g & 63);
+  const int t = (int)((g >> 6) & 1);
+  const int64_t rest = g >> 7;
+  const int KS = p.Cin / 32;
   const int ks = (int)(rest % KS);
   const int pb = (int)(rest / KS);
   const int m = lane & 15;
-  const int c = 32 * ks + 8 * (lane >> 4) + j;
+  const int c0 = 32 * ks + 8 * (lane >> 4);
   const int col = 32 * pb + 8 * (m >> 2) + 4 * t + (m & 3);
-  wsw[idx] = w[(int64_t)c * Cout + col];
+  bf16x8 v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = w[(int64_t)(c0 + j) * p.Cout + col];
+  wsw[g] = v;
 }
 
 constexpr int kGemmTiles = 2;                          // 16-row tiles per wave
@@ -207,10 +210,10 @@ __global__ __launch_bounds__(64 * kGemmWaves, 4) void gemm_bf16_kernel(GemmParam
   }
 }
 
-hipError_t launch_transpose_weights(const void* w, void* wt, int Cin, int Cout, hipStream_t st) {
-  const int64_t total = (int64_t)Cin * Cout;
-  hipLaunchKernelGGL(swizzle_weights_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const bf16*>(w), reinterpret_cast<bf16*>(wt), Cin, Cout);
+hipError_t launch_swizzle_weights(const SwizzleParams& p, int n, hipStream_t st) {
+  const int64_t groups = (int64_t)p.Cin * p.Cout / 8;
+  hipLaunchKernelGGL(swizzle_weights_kernel, dim3((unsigned)((groups + 255) / 256), (unsigned)n), dim3(256), 0,
+                     st, p);
   return hipGetLastError();
 }
 

@@ -147,7 +147,13 @@ constexpr int kTokPairMaxM = 256;
 hipError_t launch_tok_pair(const TokPairParams& p, int D, int B, hipStream_t s);
 hipError_t launch_sum_splits(const float* part, float* out, int B, int H, int S, int64_t MD, bool batch_sum,
                              float factor, int accumulate, hipStream_t st);
-hipError_t launch_transpose_weights(const void* w, void* wt, int Cin, int Cout, hipStream_t s);
+// Weights [Cin, Cout] row-major -> the GEMM's A-operand order, up to five at once.
+struct SwizzleParams {
+  const void* w[5];
+  void* wsw[5];
+  int Cin, Cout;
+};
+hipError_t launch_swizzle_weights(const SwizzleParams& p, int n, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
 
 }  // namespace flare

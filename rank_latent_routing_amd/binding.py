@@ -219,8 +219,12 @@ def flare_decode(k, q, z, y=None, scale=0.0, flags=0, stream=None, want_lse=Fals
     return (y, lse) if want_lse else y
 
 
-def _f32_ptr(t):
-    assert t.dtype == torch.float32 and t.is_contiguous()
+def _f32_ptr(t, shape, what):
+    """The raw pointer of a contiguous fp32 tensor of the given shape (the C
+    ABI takes these operands as plain arrays, so their layout is fixed)."""
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be a contiguous float32 tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}{'' if t.is_contiguous() else ' (strided)'}")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -242,8 +246,10 @@ def flare_decode_backward(k, q, z, y, lse, dy, dk=None, dq=None, dz=None, flags=
                                                device=dev)
     dz = dz if dz is not None else torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
     ws = _workspace(lib().flare_decode_backward_workspace_size(B, H, M, N, D), dev, workspace)
-    s = lib().flare_decode_backward(describe(k), describe(q), describe(z), describe(y), _f32_ptr(lse),
-                                    describe(dy), describe(dk), _f32_ptr(dq), _f32_ptr(dz),
+    s = lib().flare_decode_backward(describe(k), describe(q), describe(z), describe(y),
+                                    _f32_ptr(lse, (B, H, N), "lse"), describe(dy), describe(dk),
+                                    _f32_ptr(dq, _dq_shape(B, H, M, D, flags), "dq"),
+                                    _f32_ptr(dz, (B, H, M, D), "dz"),
                                     int(flags), B, H, M, N, D, float(scale), ctypes.c_void_p(ws.data_ptr()),
                                     ws.numel() * ws.element_size(), _stream(stream))
     _check(s, "flare_decode_backward")
@@ -264,8 +270,9 @@ def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, flags=
     dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
     dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
     ws = _workspace(lib().flare_encode_backward_workspace_size(B, H, M, N, D), dev, workspace)
-    s = lib().flare_encode_backward(describe(q), describe(k), describe(v), describe(z), _f32_ptr(lse),
-                                    _f32_ptr(dz), _f32_ptr(dq), describe(dk), describe(dv),
+    s = lib().flare_encode_backward(describe(q), describe(k), describe(v), describe(z),
+                                    _f32_ptr(lse, (B, H, M), "lse"), _f32_ptr(dz, (B, H, M, D), "dz"),
+                                    _f32_ptr(dq, _dq_shape(B, H, M, D, flags), "dq"), describe(dk), describe(dv),
                                     int(flags), B, H, M, N, D, float(scale),
                                     ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                     _stream(stream))
@@ -286,8 +293,10 @@ def flare_encdec_backward(q, k, v, z, lse_enc, y, lse_dec, dy, dq=None, dk=None,
     dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
     dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
     ws = _workspace(lib().flare_encdec_backward_workspace_size(B, H, M, N, D), dev, workspace)
-    s = lib().flare_encdec_backward(describe(q), describe(k), describe(v), describe(z), _f32_ptr(lse_enc),
-                                    describe(y), _f32_ptr(lse_dec), describe(dy), _f32_ptr(dq),
+    s = lib().flare_encdec_backward(describe(q), describe(k), describe(v), describe(z),
+                                    _f32_ptr(lse_enc, (B, H, M), "lse_enc"), describe(y),
+                                    _f32_ptr(lse_dec, (B, H, N), "lse_dec"), describe(dy),
+                                    _f32_ptr(dq, _dq_shape(B, H, M, D, flags), "dq"),
                                     describe(dk), describe(dv), int(flags), B, H, M, N, D, float(scale),
                                     ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
                                     _stream(stream))

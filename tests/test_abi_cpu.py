@@ -69,6 +69,7 @@ def test_encode_rejects_bad_arguments_without_a_device():
     assert call_encode(B=0) == E.FLARE_E_INVALID
     assert call_encode(N=0) == E.FLARE_E_INVALID
     assert call_encode(M=0) == E.FLARE_E_INVALID
+    assert call_encode(B=300, H=300) == E.FLARE_E_INVALID                  # B*H above the grid's y limit
     assert call_encode(D=24) == E.FLARE_E_UNSUPPORTED
     assert call_encode(D=64) == E.FLARE_E_UNSUPPORTED
     assert call_encode(M=513) == E.FLARE_E_UNSUPPORTED
@@ -179,3 +180,17 @@ def test_backward_calls_reject_bad_arguments():
     assert pair(flags=8) == fb.FLARE_E_INVALID
     assert pair(D=8) == fb.FLARE_E_UNSUPPORTED
     assert pair(ws=need - 1) == fb.FLARE_E_WORKSPACE
+
+
+def test_binding_rejects_strided_or_misshaped_arrays():
+    # lse, dQ and dZ cross the C ABI as plain arrays: the binding must refuse
+    # a view whose memory is not that array instead of passing its pointer
+    import torch
+    good = torch.zeros(2, 3, 4, 32)
+    assert fb._f32_ptr(good, (2, 3, 4, 32), "dz").value == good.data_ptr()
+    with pytest.raises(ValueError, match="strided"):
+        fb._f32_ptr(torch.zeros(2, 3, 4, 40)[..., :32], (2, 3, 4, 32), "dz")
+    with pytest.raises(ValueError, match="shape"):
+        fb._f32_ptr(good, (3, 4, 32), "dq")
+    with pytest.raises(ValueError, match="float32"):
+        fb._f32_ptr(good.double(), (2, 3, 4, 32), "dz")

@@ -665,6 +665,61 @@ def test_pair_backward_token_major_gradients():
         check_bf16(f64(c_), dvr, f"dV ({tag})")
 
 
+def test_padded_strides_forward_and_backward():
+    # Every tensor a view into a larger buffer: token rows padded (row stride
+    # H*48 elements for D = 32, batch stride with 3 spare rows), latent rows
+    # padded to 40.  Padding that is read holds NaN, so a kernel that used it
+    # would fail; padding of outputs holds a sentinel that must survive.
+    B, H, N, D, M = 2, 3, 900, 32, 72
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=41, q_mult=3.0)
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=42)
+
+    def tok_in(t):
+        buf = torch.full((B, N + 3, H, 48), float("nan"), dtype=t.dtype, device=DEV)
+        buf[:, :N, :, :D] = t.to(DEV)
+        return hm(buf[:, :N, :, :D])
+
+    def tok_out(dtype):
+        buf = torch.full((B, N + 3, H, 48), 12345.0, dtype=dtype, device=DEV)
+        return buf, hm(buf[:, :N, :, :D])
+
+    def lat_out():
+        buf = torch.full((B, H, M, 40), 12345.0, dtype=torch.float32, device=DEV)
+        return buf, buf[..., :D]
+
+    qbuf = torch.full((H, M, 40), float("nan"), dtype=torch.bfloat16, device=DEV)
+    qbuf[..., :D] = x["q"].to(DEV)
+    q = qbuf[..., :D]
+    k, v, dy = tok_in(x["k"]), tok_in(x["v"]), tok_in(dy_t)
+    zbuf, z = lat_out()
+    z, lse_e = rl.flare_encode(q, k, v, z=z, want_lse=True)
+    ybuf, y = tok_out(torch.bfloat16)
+    y, lse_d = rl.flare_decode(k, q, z, y=y, want_lse=True)
+    dkb, dk = tok_out(torch.float32)
+    dvb, dv = tok_out(torch.float32)
+    dq, _, _ = rl.flare_encdec_backward(q, k, v, z, lse_e, y, lse_d, dy, dk=dk, dv=dv)
+    dkb2, dk2 = tok_out(torch.float32)
+    dvb2, dv2 = tok_out(torch.float32)
+    _, dq2, dz = rl.flare_decode_backward(k, q, z, y, lse_d, dy, dk=dk2)
+    dq2, _, _ = rl.flare_encode_backward(q, k, v, z, lse_e, dz, dq=dq2, dk=dk2, dv=dv2,
+                                         flags=rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK)
+    torch.cuda.synchronize()
+    qo, ko, vo = f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"]))
+    zr, _ = oracle.encode(qo, ko, vo)
+    check_bf16(f64(z), zr, "Z (padded views)")
+    check_bf16(f64(y), oracle.decode(ko, qo, f64(z)), "Y (padded views)")
+    dqr, dkr, dvr = oracle.flare_encdec_backward(qo, ko, vo, f64(hm(dy_t)))
+    for tag, (a, b_, c_) in (("one call", (dq, dk, dv)), ("two calls", (dq2, dk2, dv2))):
+        check_bf16(f64(a), dqr, f"dQ ({tag}, padded views)")
+        check_bf16(f64(b_), dkr, f"dK ({tag}, padded views)")
+        check_bf16(f64(c_), dvr, f"dV ({tag}, padded views)")
+    for name, buf in (("Y", ybuf), ("dK", dkb), ("dV", dvb), ("dK2", dkb2), ("dV2", dvb2)):
+        assert torch.all(buf[:, :N, :, D:] == 12345.0), name
+        assert torch.all(buf[:, N:] == 12345.0), name
+    assert torch.all(zbuf[..., D:] == 12345.0), "Z"
+
+
 def test_graph_capture_replays_match_eager():
     # flare_mix (FLARE++, B=8, N=4096, C=128, M=64) and the pair backward
     # captured into HIP graphs: the library issues only kernel launches on the

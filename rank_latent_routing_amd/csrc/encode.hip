@@ -461,55 +461,93 @@ __global__ __launch_bounds__(256) void encode_f32_kernel(EncodeParams p) {
 
 // ------------------------------------------------------------------- merge
 // L = log2 sum_s 2^{L_s};  Z = sum_s 2^{L_s - L} O_s  (the exact combination
-// of split encoders; an empty split has L_s = -inf and weight 0).  One
-// workgroup per (batch*head, latent): 256 threads = G split groups x D
-// features; every thread folds its splits with an online logsumexp, and the
-// G partial results are combined through LDS.
+// of split encoders; an empty split has L_s = -inf and weight 0).  A
+// workgroup of 256 threads covers 4R consecutive latent features of one
+// batch*head, R = 256 / G: thread (g, r) takes the four features 4r .. 4r + 3
+// of the block (one latent, since D is a multiple of 4), folds the splits
+// g, g + G, ... with an online logsumexp, and for G > 1 the G partial results
+// are combined through LDS.  Each split's part of a block is 16R contiguous
+// bytes read with 16-byte loads; G grows with the number of splits (up to 8)
+// so that each thread folds about eight of them, loaded together.
 constexpr int kMergeThreads = 256;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
-  __shared__ float sm_m[kMergeThreads], sm_l[kMergeThreads], sm_a[kMergeThreads];
-  const int bh = blockIdx.y, m = blockIdx.x, tid = threadIdx.x;
-  const int G = kMergeThreads / p.D;  // split groups
-  const int grp = tid / p.D, d = tid - grp * p.D;
-  const float* pl = p.part_l + (int64_t)bh * p.S * p.M + m;
-  const float* po = p.part_o + ((int64_t)bh * p.S * p.M + m) * p.D + d;
-  float mx = -INFINITY, sum = 0.f, acc = 0.f;
-  for (int s = grp; s < p.S; s += G) {
-    const float ls = pl[(int64_t)s * p.M];
-    const float os = po[(int64_t)s * p.M * p.D];
-    if (ls == -INFINITY) continue;
-    if (ls > mx) {
-      const float a = exp2f(mx - ls);
-      sum *= a;
-      acc *= a;
-      mx = ls;
+  __shared__ float sm_m[kMergeThreads], sm_l[kMergeThreads];
+  __shared__ f32x4 sm_a[kMergeThreads];
+  const int G = p.G, R = kMergeThreads / G;
+  const int tid = threadIdx.x, g = tid / R, r = tid - g * R;
+  const int bh = blockIdx.y;
+  const int64_t MD = (int64_t)p.M * p.D;
+  const int64_t e = ((int64_t)blockIdx.x * R + r) * 4;  // first of the thread's four features
+  const bool valid = e < MD;
+  const int m = valid ? (int)(e / p.D) : 0;
+  const int d = valid ? (int)(e - (int64_t)m * p.D) : 0;
+  float mx = -INFINITY, sum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    const float* pl = p.part_l + (int64_t)bh * p.S * p.M + m;
+    const f32x4* po = reinterpret_cast<const f32x4*>(p.part_o + (int64_t)bh * p.S * MD + e);
+    const int64_t ostep = MD / 4;  // f32x4 per split
+    // eight splits' values are loaded before any is folded, so their loads
+    // are in flight together
+    for (int s0 = g; s0 < p.S; s0 += 8 * G) {
+      float lsv[8];
+      f32x4 osv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = s0 + j * G;
+        lsv[j] = s < p.S ? pl[(int64_t)s * p.M] : -INFINITY;
+        osv[j] = s < p.S ? po[(int64_t)s * ostep] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ls = lsv[j];
+        if (ls == -INFINITY) continue;
+        if (ls > mx) {
+          const float a = exp2f(mx - ls);
+          sum *= a;
+          acc *= a;
+          mx = ls;
+        }
+        const float w = exp2f(ls - mx);
+        sum += w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, osv[j][i], acc[i]);
+      }
     }
-    const float w = exp2f(ls - mx);
-    sum += w;
-    acc = fmaf(w, os, acc);
   }
-  sm_m[tid] = mx;
-  sm_l[tid] = sum;
-  sm_a[tid] = acc;
-  __syncthreads();
-  if (grp != 0) return;
-  float M_ = -INFINITY;
-  for (int q = 0; q < G; ++q) M_ = fmaxf(M_, sm_m[q * p.D + d]);
-  float L = 0.f, A = 0.f;
-  if (M_ != -INFINITY)
-    for (int q = 0; q < G; ++q) {
-      const float w = exp2f(sm_m[q * p.D + d] - M_);
-      L += w * sm_l[q * p.D + d];
-      A += w * sm_a[q * p.D + d];
-    }
-  const float z = L > 0.f ? A / L : 0.f;
+  float M_ = mx, L = sum;
+  f32x4 A = acc;
+  if (G > 1) {
+    sm_m[tid] = mx;
+    sm_l[tid] = sum;
+    sm_a[tid] = acc;
+    __syncthreads();
+    if (g != 0) return;
+    M_ = -INFINITY;
+    for (int q = 0; q < G; ++q) M_ = fmaxf(M_, sm_m[q * R + r]);
+    L = 0.f;
+    A = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (M_ != -INFINITY)
+      for (int q = 0; q < G; ++q) {
+        const float w = exp2f(sm_m[q * R + r] - M_);
+        L += w * sm_l[q * R + r];
+        const f32x4 a = sm_a[q * R + r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[i] += w * a[i];
+      }
+  }
+  if (!valid) return;
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
   const int b = bh / p.H, h = bh - b * p.H;
   const int64_t off = b * p.z_sb + h * p.z_sh + (int64_t)m * p.z_sl + d;
-  if (p.z_f32)
-    reinterpret_cast<float*>(p.z)[off] = z;
-  else
-    reinterpret_cast<bf16*>(p.z)[off] = (bf16)z;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (p.z_f32)
+      reinterpret_cast<float*>(p.z)[off + i] = A[i] * inv;
+    else
+      reinterpret_cast<bf16*>(p.z)[off + i] = (bf16)(A[i] * inv);
+  }
   if (p.lse && d == 0) p.lse[(int64_t)bh * p.M + m] = L > 0.f ? (M_ + log2f(L)) * kLn2 : -INFINITY;
 }
 
@@ -567,8 +605,12 @@ hipError_t launch_encode_f32(const EncodeParams& p, int D, int B, hipStream_t st
 }
 
 hipError_t launch_merge(const MergeParams& p, int B, hipStream_t st) {
-  dim3 grid(p.M, B * p.H);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(kMergeThreads), 0, st, p);
+  MergeParams q = p;
+  q.G = 1;
+  while (q.G < 8 && q.G * 8 < q.S) q.G *= 2;
+  const int64_t features = 4 * (kMergeThreads / q.G);  // per workgroup
+  dim3 grid((unsigned)(((int64_t)q.M * q.D + features - 1) / features), B * q.H);
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(kMergeThreads), 0, st, q);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ struct MergeParams {
   int64_t z_sb, z_sh, z_sl;
   float* lse;         // [B, H, M] natural log, may be null
   int H, M, S, D;
+  int G;              // split groups per feature (set by launch_merge)
 };
 
 struct DecodeParams {

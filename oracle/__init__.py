@@ -15,9 +15,11 @@ page and section the computation follows:
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` (library SDPA, closed forms, invariants, brute
-force).  The full FLARE++ composition ``flare_mix`` is pinned only as the
-composition of pinned parts plus an independent three-call library SDPA
-rendering of the pages' statement.
+force).  The full FLARE++ composition ``flare_mix`` is pinned by the
+composition of pinned parts, by token-permutation equivariance, and by the
+special cases where zero synthesis values or keys reduce it to closed forms;
+beyond those its values are parity unpinned: the pages print no worked
+example of the mixer.
 """
 import ctypes
 import os

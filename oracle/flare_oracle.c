@@ -25,6 +25,12 @@
  * runs in index order.  No blocking, fusion or online rescaling: the softmax
  * is the two-pass stable form (maximum, then normalised exponentials), which
  * equals the textbook definition exactly in real arithmetic.
+ *
+ * Pins (tests/test_oracle_pins.py): library SDPA, closed forms, invariants
+ * and brute force for every function.  The full FLARE++ mixer is pinned by
+ * the composition of pinned parts, token-permutation equivariance and its
+ * zero-synthesis special cases; beyond those it is parity unpinned (the pages
+ * print no worked example of the mixer).
  */
 #include <math.h>
 #include <stdint.h>

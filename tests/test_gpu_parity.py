@@ -764,6 +764,30 @@ def test_concurrent_calls_on_two_streams():
     say("  two streams: both workloads equal to their runs alone")
 
 
+def test_largest_batch_times_heads():
+    # B * H = 65535, the largest grid the calls accept (one workgroup row per
+    # batch*head), with a ragged handful of tokens and latents per head:
+    # forward and the one-call backward against the oracle.
+    B, H, N, D, M = 255, 257, 5, 16, 3
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=61, q_mult=2.0, per_batch_q=True)
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=62)
+    q = x["q"].to(DEV)
+    k, v, dy = hm(x["k"]).contiguous().to(DEV), hm(x["v"]).contiguous().to(DEV), hm(dy_t).contiguous().to(DEV)
+    z, le = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, ld = rl.flare_decode(k, q, z, want_lse=True)
+    dq, dk, dv = rl.flare_encdec_backward(q, k, v, z, le, y, ld, dy)
+    torch.cuda.synchronize()
+    qo, ko, vo = f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"]))
+    zr, _ = oracle.encode(qo, ko, vo)
+    check_bf16(f64(z), zr, "Z (B*H = 65535)")
+    check_bf16(f64(y), oracle.decode(ko, qo, f64(z)), "Y (B*H = 65535)")
+    dqr, dkr, dvr = oracle.flare_encdec_backward(qo, ko, vo, f64(hm(dy_t)))
+    check_bf16(f64(dq), dqr, "dQ (B*H = 65535)")
+    check_bf16(f64(dk), dkr, "dK (B*H = 65535)")
+    check_bf16(f64(dv), dvr, "dV (B*H = 65535)")
+
+
 def test_graph_capture_replays_match_eager():
     # flare_mix (FLARE++, B=8, N=4096, C=128, M=64) and the pair backward
     # captured into HIP graphs: the library issues only kernel launches on the

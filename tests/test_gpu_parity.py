@@ -788,6 +788,54 @@ def test_largest_batch_times_heads():
     check_bf16(f64(dv), dvr, "dV (B*H = 65535)")
 
 
+@pytest.mark.parametrize("case", ["zero_queries", "equal_keys", "zero_values"])
+def test_degenerate_inputs(case):
+    # Degenerate cases of the method, forward and one-call backward:
+    # zero queries (every score 0: uniform weights in both calls), every key
+    # equal (the encoder weights every token alike, so Z is the mean of V),
+    # zero values (Z = 0, so Y = 0 and every gradient through Z vanishes).
+    B, H, N, D, M = 2, 3, 1000, 32, 48
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=71, q_mult=3.0)
+    q, k, v = x["q"].clone(), x["k"].clone(), x["v"].clone()
+    if case == "zero_queries":
+        q.zero_()
+    elif case == "equal_keys":
+        k[:] = k[:, :1]
+    else:
+        v.zero_()
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=72)
+    qd = q.to(DEV)
+    kd, vd, dy = hm(k).contiguous().to(DEV), hm(v).contiguous().to(DEV), hm(dy_t).contiguous().to(DEV)
+    z, le = rl.flare_encode(qd, kd, vd, want_lse=True, z_dtype=torch.float32)
+    y, ld = rl.flare_decode(kd, qd, z, want_lse=True)
+    dq, dk, dv = rl.flare_encdec_backward(qd, kd, vd, z, le, y, ld, dy)
+    torch.cuda.synchronize()
+    qo, ko, vo = f64(q), f64(hm(k)), f64(hm(v))
+    zr, _ = oracle.encode(qo, ko, vo)
+    yr = oracle.decode(ko, qo, zr)
+    dqr, dkr, dvr = oracle.flare_encdec_backward(qo, ko, vo, f64(hm(dy_t)))
+    if case == "zero_values":
+        # exact zeros: no weight times zero values can be anything but zero
+        assert not torch.any(z) and not torch.any(y) and not torch.any(dq) and not torch.any(dk)
+        check_bf16(f64(dv), dvr, f"dV ({case})")
+        return
+    if case == "equal_keys":
+        # Z[m] = mean over tokens of V, whatever the query (within bf16 of V's mean)
+        np.testing.assert_allclose(zr, np.broadcast_to(vo.mean(axis=2, keepdims=True), zr.shape), atol=1e-12)
+    check_bf16(f64(z), zr, f"Z ({case})")
+    check_bf16(f64(y), yr, f"Y ({case})")
+    for name, got, ref in (("dQ", dq, dqr), ("dK", dk, dkr), ("dV", dv, dvr)):
+        nr = float(np.linalg.norm(ref))
+        if nr < 1e-9:
+            # zero in exact arithmetic: held to 1e-2 of the upstream gradient's scale
+            e = float(np.linalg.norm(f64(got))) / float(np.linalg.norm(f64(dy)))
+            say(f"  {name} ({case}): zero in exact arithmetic, |got| / |dY| {e:.3e}")
+            assert e <= BF16_TOL
+        else:
+            check_bf16(f64(got), ref, f"{name} ({case})")
+
+
 def test_graph_capture_replays_match_eager():
     # flare_mix (FLARE++, B=8, N=4096, C=128, M=64) and the pair backward
     # captured into HIP graphs: the library issues only kernel launches on the

@@ -719,28 +719,41 @@ __global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
 // with part[r, b, s, e] at (r S + s) MD + b bstride + e: one (batch, head)
 // row per r when nb = 1, or for a query block shared by the batch one head
 // per r with the batch summed (nb = B, bstride = H S MD).  A workgroup covers
-// 64 consecutive e of one r with four split groups (each thread takes every
-// fourth split, coalesced across the 64 lanes), combined through LDS.
+// 256 consecutive e of one r, four per thread with 16-byte loads (MD is a
+// multiple of 16), in four split groups: each thread takes every fourth
+// split, loading eight of them before adding any.  The groups are combined
+// through LDS.
 __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                          int S, int64_t MD, int nb, int64_t bstride, float factor,
                                                          int accumulate) {
-  __shared__ float red[4][64];
+  __shared__ f32x4 red[4][64];
   const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   const int64_t r = blockIdx.y;
-  const int64_t e = (int64_t)blockIdx.x * 64 + lane;
-  float acc = 0.f;
+  const int64_t e = ((int64_t)blockIdx.x * 64 + lane) * 4;
+  const int64_t step = MD / 4;  // f32x4 per split
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (e < MD) {
     for (int bi = 0; bi < nb; ++bi) {
-      const float* ps = part + r * S * MD + bi * bstride + e;
-      for (int s = grp; s < S; s += 4) acc += ps[(int64_t)s * MD];
+      const f32x4* ps = reinterpret_cast<const f32x4*>(part + r * S * MD + bi * bstride + e);
+      for (int s0 = grp; s0 < S; s0 += 32) {
+        f32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int s = s0 + 4 * j;
+          v[j] = s < S ? ps[(int64_t)s * step] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += v[j];
+      }
     }
   }
   red[grp][lane] = acc;
   __syncthreads();
   if (grp == 0 && e < MD) {
-    const float sum = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
-    const int64_t idx = r * MD + e;
-    out[idx] = (accumulate ? out[idx] : 0.f) + factor * sum;
+    const f32x4 sum = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    float* o = out + r * MD + e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (accumulate ? o[i] : 0.f) + factor * sum[i];
   }
 }
 
@@ -838,7 +851,7 @@ hipError_t launch_sum_splits(const float* part, float* out, int B, int H, int S,
   const int64_t rows = batch_sum ? H : (int64_t)B * H;
   const int nb = batch_sum ? B : 1;
   const int64_t bstride = (int64_t)H * S * MD;
-  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((MD + 63) / 64), (unsigned)rows), dim3(256), 0, st, part,
+  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((MD + 255) / 256), (unsigned)rows), dim3(256), 0, st, part,
                      out, S, MD, nb, bstride, factor, accumulate);
   return hipGetLastError();
 }

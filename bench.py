@@ -159,7 +159,7 @@ def main():
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS["encdec_bf16_n1m"]
     B, N, H, D, M = w.B, w.N, w.H, w.D, w.M
-    x = inputs.make_encdec(w, seed=0)
+    x = inputs.make_encdec(w, seed=0, synth=True)  # q, k, v first; then eK, eV, seeds
     q = x["q"].to(dev)
     k = x["k"].permute(0, 2, 1, 3).contiguous().to(dev)   # head-major [B, H, N, D]
     v = x["v"].permute(0, 2, 1, 3).contiguous().to(dev)
@@ -240,6 +240,40 @@ def main():
     if extra["parity_rel_l2"]["Z_head0"] > 1e-2 or extra["parity_rel_l2"]["Y_head0_64_tokens"] > 1e-2:
         print("bench.py: parity check failed", extra["parity_rel_l2"], file=sys.stderr)
         sys.exit(3)
+
+    # FLARE++ attention at the same sizes: the query synthesis Q(X) =
+    # SDPA(seeds, eK, eV) over separate eK, eV ~ N(0, 1), then the encode and
+    # decode with Q(X) (the metric workload with the synthesis added; no
+    # projections).
+    ek = x["ek"].permute(0, 2, 1, 3).contiguous().to(dev)
+    ev = x["ev"].permute(0, 2, 1, 3).contiguous().to(dev)
+    seeds = x["seeds"].to(dev)
+    qx = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+
+    def pp_step():
+        rl.flare_route_queries(seeds, ek, ev, qx=qx, workspace=ws, stream=stream)
+        rl.flare_encode(qx, k, v, z=z, workspace=ws, stream=stream)
+        rl.flare_decode(k, qx, z, y=y, stream=stream)
+
+    for _ in range(max(2, args.warmup // 2)):
+        pp_step()
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for _ in range(args.steps):
+        pp_step()
+    p1.record(stream)
+    torch.cuda.synchronize()
+    pp_ms = p0.elapsed_time(p1) / args.steps
+    pp_flops = 3 * enc.flops
+    extra["flarepp_encdec"] = {
+        "config": "FLARE++ attention: query synthesis from seeds over eK, eV, then encode and decode; "
+                  "B=1, H=8, D=32, N=1048576, M=256, bf16, no projections",
+        "ms": round(pp_ms, 4), "tokens_per_s": tokens / (pp_ms / 1e3),
+        "tflops": round(pp_flops / (pp_ms / 1e3) / 1e12, 1),
+        "mfma_frac": round(pp_flops / (pp_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "over_flare": round(pp_ms / ms_step, 3)}
+    del ek, ev, seeds, qx
 
     if not args.no_bwd:
         # Backward of the same encode + decode pair: decoder gradient (dK, dQ,

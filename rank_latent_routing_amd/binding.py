@@ -119,8 +119,20 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _dev(t, what="tensor"):
+    """The raw pointer of a tensor in GPU memory (the library's kernels read
+    and write what they are given: a host pointer would fault the device)."""
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a tensor on the GPU, got device {t.device}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt_dev(t, what):
+    return _dev(t, what) if t is not None else ctypes.c_void_p(None)
+
+
 def describe(t: torch.Tensor) -> FlareTensor:
-    """flare_tensor of a [B, H, L, D] (or shared [H, L, D]) view."""
+    """flare_tensor of a [B, H, L, D] (or shared [H, L, D]) view in GPU memory."""
     if t.dim() == 3:
         sb, (sh, sl, sd) = 0, t.stride()
     elif t.dim() == 4:
@@ -129,7 +141,7 @@ def describe(t: torch.Tensor) -> FlareTensor:
         raise ValueError("expected a [B, H, L, D] or [H, L, D] tensor")
     if sd != 1 and t.shape[-1] > 1:
         raise ValueError("the last axis must be contiguous")
-    return FlareTensor(t.data_ptr(), _dtype_code(t), 0, sb, sh, sl)
+    return FlareTensor(_dev(t).value, _dtype_code(t), 0, sb, sh, sl)
 
 
 def token_major(x: torch.Tensor, H: int) -> torch.Tensor:
@@ -177,9 +189,9 @@ def flare_encode(q, k, v, z=None, want_lse=False, scale=0.0, flags=0, workspace=
     lse = torch.empty((B, H, M), dtype=torch.float32, device=k.device) if want_lse else None
     ws = _workspace(encode_workspace_size(B, H, M, N, D), k.device, workspace)
     s = lib().flare_encode(describe(q), describe(k), describe(v), describe(z),
-                           ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
+                           _opt_dev(lse, "lse"),
                            B, H, M, N, D, float(scale), int(flags),
-                           ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                           _dev(ws, "workspace"), ws.numel() * ws.element_size(),
                            _stream(stream))
     _check(s, "flare_encode")
     return (z, lse) if want_lse else z
@@ -196,9 +208,9 @@ def flare_route_queries(seeds, ek, ev, qx=None, scale=0.0, flags=0, workspace=No
     lse = torch.empty((B, H, M), dtype=torch.float32, device=ek.device) if want_lse else None
     ws = _workspace(encode_workspace_size(B, H, M, N, D), ek.device, workspace)
     s = lib().flare_route_queries(describe(seeds), describe(ek), describe(ev), describe(qx),
-                                  ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
+                                  _opt_dev(lse, "lse"),
                                   B, H, M, N, D, float(scale), int(flags),
-                                  ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                  _dev(ws, "workspace"), ws.numel() * ws.element_size(),
                                   _stream(stream))
     _check(s, "flare_route_queries")
     return (qx, lse) if want_lse else qx
@@ -213,7 +225,7 @@ def flare_decode(k, q, z, y=None, scale=0.0, flags=0, stream=None, want_lse=Fals
         y = torch.empty((B, H, N, D), dtype=k.dtype, device=k.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=k.device) if want_lse else None
     s = lib().flare_decode(describe(k), describe(q), describe(z), describe(y),
-                           ctypes.c_void_p(lse.data_ptr() if lse is not None else None),
+                           _opt_dev(lse, "lse"),
                            B, H, M, N, D, float(scale), int(flags), _stream(stream))
     _check(s, "flare_decode")
     return (y, lse) if want_lse else y
@@ -225,7 +237,7 @@ def _f32_ptr(t, shape, what):
     if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
         raise ValueError(f"{what} must be a contiguous float32 tensor of shape {tuple(shape)}, "
                          f"got {t.dtype} {tuple(t.shape)}{'' if t.is_contiguous() else ' (strided)'}")
-    return ctypes.c_void_p(t.data_ptr())
+    return _dev(t, what)
 
 
 def _dq_shape(B, H, M, D, flags):
@@ -250,7 +262,7 @@ def flare_decode_backward(k, q, z, y, lse, dy, dk=None, dq=None, dz=None, flags=
                                     _f32_ptr(lse, (B, H, N), "lse"), describe(dy), describe(dk),
                                     _f32_ptr(dq, _dq_shape(B, H, M, D, flags), "dq"),
                                     _f32_ptr(dz, (B, H, M, D), "dz"),
-                                    int(flags), B, H, M, N, D, float(scale), ctypes.c_void_p(ws.data_ptr()),
+                                    int(flags), B, H, M, N, D, float(scale), _dev(ws, "workspace"),
                                     ws.numel() * ws.element_size(), _stream(stream))
     _check(s, "flare_decode_backward")
     return dk, dq, dz
@@ -274,7 +286,7 @@ def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, flags=
                                     _f32_ptr(lse, (B, H, M), "lse"), _f32_ptr(dz, (B, H, M, D), "dz"),
                                     _f32_ptr(dq, _dq_shape(B, H, M, D, flags), "dq"), describe(dk), describe(dv),
                                     int(flags), B, H, M, N, D, float(scale),
-                                    ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                    _dev(ws, "workspace"), ws.numel() * ws.element_size(),
                                     _stream(stream))
     _check(s, "flare_encode_backward")
     return dq, dk, dv
@@ -298,7 +310,7 @@ def flare_encdec_backward(q, k, v, z, lse_enc, y, lse_dec, dy, dq=None, dk=None,
                                     _f32_ptr(lse_dec, (B, H, N), "lse_dec"), describe(dy),
                                     _f32_ptr(dq, _dq_shape(B, H, M, D, flags), "dq"),
                                     describe(dk), describe(dv), int(flags), B, H, M, N, D, float(scale),
-                                    ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                                    _dev(ws, "workspace"), ws.numel() * ws.element_size(),
                                     _stream(stream))
     _check(s, "flare_encdec_backward")
     return dq, dk, dv
@@ -324,11 +336,11 @@ def flare_project(x, weights, outs=None, head_dim=None, workspace=None, stream=N
         else:
             outs = [torch.empty((R, Cout), dtype=x.dtype, device=x.device) for _ in range(n)]
     ws = _workspace(project_workspace_size(Cin, Cout, n), x.device, workspace)
-    warr = (ctypes.c_void_p * n)(*[w.data_ptr() for w in weights])
-    yarr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
-    s = lib().flare_project(ctypes.c_void_p(x2.data_ptr()), warr, yarr, n, R, Cin, Cout,
+    warr = (ctypes.c_void_p * n)(*[_dev(w, "weight").value for w in weights])
+    yarr = (ctypes.c_void_p * n)(*[_dev(o, "output").value for o in outs])
+    s = lib().flare_project(_dev(x2, "x"), warr, yarr, n, R, Cin, Cout,
                             1 if head_dim else 0, B, head_dim or 0,
-                            ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                            _dev(ws, "workspace"), ws.numel() * ws.element_size(),
                             _stream(stream))
     _check(s, "flare_project")
     return outs
@@ -349,10 +361,10 @@ def flare_mix(x, w_k, w_v, qs, H, w_ek=None, w_ev=None, w_o=None, out=None, scal
         out = torch.empty_like(x)
     dyn, has_wo = w_ek is not None, w_o is not None
     ws = _workspace(mix_workspace_size(B, N, C, H, M, dyn, has_wo), x.device, workspace)
-    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else None)
+    ptr = lambda t: _opt_dev(t, "mixer operand")
     s = lib().flare_mix(ptr(x), ptr(w_k), ptr(w_v), ptr(w_ek), ptr(w_ev), ptr(qs), ptr(w_o),
                         ptr(out), _dtype_code(x), B, N, C, H, M, float(scale), int(flags),
-                        ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+                        _dev(ws, "workspace"), ws.numel() * ws.element_size(),
                         _stream(stream))
     _check(s, "flare_mix")
     return out

@@ -184,13 +184,26 @@ def test_backward_calls_reject_bad_arguments():
 
 def test_binding_rejects_strided_or_misshaped_arrays():
     # lse, dQ and dZ cross the C ABI as plain arrays: the binding must refuse
-    # a view whose memory is not that array instead of passing its pointer
+    # a view whose memory is not that array, or host memory, instead of
+    # passing its pointer
     import torch
     good = torch.zeros(2, 3, 4, 32)
-    assert fb._f32_ptr(good, (2, 3, 4, 32), "dz").value == good.data_ptr()
+    with pytest.raises(ValueError, match="on the GPU"):  # right layout, but host memory
+        fb._f32_ptr(good, (2, 3, 4, 32), "dz")
     with pytest.raises(ValueError, match="strided"):
         fb._f32_ptr(torch.zeros(2, 3, 4, 40)[..., :32], (2, 3, 4, 32), "dz")
     with pytest.raises(ValueError, match="shape"):
         fb._f32_ptr(good, (3, 4, 32), "dq")
     with pytest.raises(ValueError, match="float32"):
         fb._f32_ptr(good.double(), (2, 3, 4, 32), "dz")
+
+
+def test_binding_refuses_host_tensors():
+    # every tensor the kernels touch must be in GPU memory: a host tensor is
+    # refused before the call (never handed to a kernel)
+    import torch
+    k = torch.zeros(1, 2, 16, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fb.describe(k)
+    with pytest.raises(ValueError, match="on the GPU"):
+        fb._dev(torch.zeros(4), "workspace")

@@ -164,8 +164,32 @@ def _check(status: int, what: str):
 
 
 def _dims(k: torch.Tensor):
+    if k.dim() != 4:
+        raise ValueError(f"keys must be [B, H, N, D], got shape {tuple(k.shape)}")
     B, H, N, D = k.shape
     return B, H, N, D
+
+
+# The C ABI sees pointers and strides only: every extent below must match the
+# sizes passed with them, or a kernel would read or write past the tensor.
+def _token(t, B, H, N, D, what):
+    if tuple(t.shape) != (B, H, N, D):
+        raise ValueError(f"{what} must be [B, H, N, D] = {(B, H, N, D)}, got {tuple(t.shape)}")
+
+
+def _latent(t, B, H, M, D, what, shared=True):
+    """[B, H, M, D], or with ``shared`` one [H, M, D] block for the whole batch."""
+    s = tuple(t.shape)
+    if s != (B, H, M, D) and not (shared and s == (H, M, D)):
+        raise ValueError(f"{what} must be [B, H, M, D] = {(B, H, M, D)}"
+                         + (f" or shared [H, M, D] = {(H, M, D)}" if shared else "") + f", got {s}")
+
+
+def _plain(t, shape, what, dtype=torch.bfloat16):
+    """A contiguous tensor of the given shape and dtype (passed as a raw array)."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}{'' if t.is_contiguous() else ' (strided)'}")
 
 
 def encode_workspace_size(B, H, M, N, D) -> int:
@@ -184,8 +208,11 @@ def flare_encode(q, k, v, z=None, want_lse=False, scale=0.0, flags=0, workspace=
     shared [H, M, D].  Returns z (and lse [B, H, M] fp32 when want_lse)."""
     B, H, N, D = _dims(k)
     M = q.shape[-2]
+    _latent(q, B, H, M, D, "q")
+    _token(v, B, H, N, D, "v")
     if z is None:
         z = torch.empty((B, H, M, D), dtype=z_dtype or k.dtype, device=k.device)
+    _latent(z, B, H, M, D, "z", shared=False)
     lse = torch.empty((B, H, M), dtype=torch.float32, device=k.device) if want_lse else None
     ws = _workspace(encode_workspace_size(B, H, M, N, D), k.device, workspace)
     s = lib().flare_encode(describe(q), describe(k), describe(v), describe(z),
@@ -203,8 +230,11 @@ def flare_route_queries(seeds, ek, ev, qx=None, scale=0.0, flags=0, workspace=No
     (and the per-query normaliser lse [B, H, M] fp32 when want_lse)."""
     B, H, N, D = _dims(ek)
     M = seeds.shape[-2]
+    _latent(seeds, B, H, M, D, "seeds")
+    _token(ev, B, H, N, D, "ev")
     if qx is None:
         qx = torch.empty((B, H, M, D), dtype=torch.float32, device=ek.device)
+    _latent(qx, B, H, M, D, "qx", shared=False)
     lse = torch.empty((B, H, M), dtype=torch.float32, device=ek.device) if want_lse else None
     ws = _workspace(encode_workspace_size(B, H, M, N, D), ek.device, workspace)
     s = lib().flare_route_queries(describe(seeds), describe(ek), describe(ev), describe(qx),
@@ -221,8 +251,11 @@ def flare_decode(k, q, z, y=None, scale=0.0, flags=0, stream=None, want_lse=Fals
     y (and the per-token normaliser lse [B, H, N] fp32 when want_lse)."""
     B, H, N, D = _dims(k)
     M = q.shape[-2]
+    _latent(q, B, H, M, D, "q")
+    _latent(z, B, H, M, D, "z")
     if y is None:
         y = torch.empty((B, H, N, D), dtype=k.dtype, device=k.device)
+    _token(y, B, H, N, D, "y")
     lse = torch.empty((B, H, N), dtype=torch.float32, device=k.device) if want_lse else None
     s = lib().flare_decode(describe(k), describe(q), describe(z), describe(y),
                            _opt_dev(lse, "lse"),
@@ -257,6 +290,10 @@ def flare_decode_backward(k, q, z, y, lse, dy, dk=None, dq=None, dz=None, flags=
     dq = dq if dq is not None else torch.empty(_dq_shape(B, H, M, D, flags), dtype=torch.float32,
                                                device=dev)
     dz = dz if dz is not None else torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    _latent(q, B, H, M, D, "q")
+    _latent(z, B, H, M, D, "z")
+    for name, tt in (("y", y), ("dy", dy), ("dk", dk)):
+        _token(tt, B, H, N, D, name)
     ws = _workspace(lib().flare_decode_backward_workspace_size(B, H, M, N, D), dev, workspace)
     s = lib().flare_decode_backward(describe(k), describe(q), describe(z), describe(y),
                                     _f32_ptr(lse, (B, H, N), "lse"), describe(dy), describe(dk),
@@ -281,6 +318,10 @@ def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, flags=
                                                device=dev)
     dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
     dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    _latent(q, B, H, M, D, "q")
+    _latent(z, B, H, M, D, "z")
+    for name, tt in (("v", v), ("dk", dk), ("dv", dv)):
+        _token(tt, B, H, N, D, name)
     ws = _workspace(lib().flare_encode_backward_workspace_size(B, H, M, N, D), dev, workspace)
     s = lib().flare_encode_backward(describe(q), describe(k), describe(v), describe(z),
                                     _f32_ptr(lse, (B, H, M), "lse"), _f32_ptr(dz, (B, H, M, D), "dz"),
@@ -304,6 +345,10 @@ def flare_encdec_backward(q, k, v, z, lse_enc, y, lse_dec, dy, dq=None, dk=None,
                                                device=dev)
     dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
     dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    _latent(q, B, H, M, D, "q")
+    _latent(z, B, H, M, D, "z")
+    for name, tt in (("v", v), ("y", y), ("dy", dy), ("dk", dk), ("dv", dv)):
+        _token(tt, B, H, N, D, name)
     ws = _workspace(lib().flare_encdec_backward_workspace_size(B, H, M, N, D), dev, workspace)
     s = lib().flare_encdec_backward(describe(q), describe(k), describe(v), describe(z),
                                     _f32_ptr(lse_enc, (B, H, M), "lse_enc"), describe(y),
@@ -323,18 +368,27 @@ def project_workspace_size(C_in, C_out, n_proj) -> int:
 def flare_project(x, weights, outs=None, head_dim=None, workspace=None, stream=None):
     """Y_p = X W_p for x [B, N, C_in] (or [R, C_in]) bf16, weights [C_in, C_out].
     With head_dim the outputs are head-major [B, H, N, head_dim]."""
-    x2 = x.reshape(-1, x.shape[-1])
+    x2 = x.reshape(-1, x.shape[-1]).contiguous()
     R, Cin = x2.shape
     Cout = weights[0].shape[1]
     B = x.shape[0] if x.dim() == 3 else 1
     n = len(weights)
+    for i, w in enumerate(weights):
+        _plain(w, (Cin, Cout), f"weight {i}", x.dtype)
+    if head_dim:
+        if Cout % head_dim or R % B:
+            raise ValueError("head-major outputs need C_out divisible by head_dim and R by B")
+        oshape = (B, Cout // head_dim, R // B, head_dim)
+    else:
+        oshape = (R, Cout)
     if outs is None:
-        if head_dim:
-            N = R // B
-            outs = [torch.empty((B, Cout // head_dim, N, head_dim), dtype=x.dtype, device=x.device)
-                    for _ in range(n)]
-        else:
-            outs = [torch.empty((R, Cout), dtype=x.dtype, device=x.device) for _ in range(n)]
+        outs = [torch.empty(oshape, dtype=x.dtype, device=x.device) for _ in range(n)]
+    for i, o in enumerate(outs):
+        # row-major outputs may also carry x's leading shape, [..., C_out]
+        shape = oshape
+        if not head_dim and tuple(o.shape) == tuple(x.shape[:-1]) + (Cout,):
+            shape = tuple(o.shape)
+        _plain(o, shape, f"output {i}", x.dtype)
     ws = _workspace(project_workspace_size(Cin, Cout, n), x.device, workspace)
     warr = (ctypes.c_void_p * n)(*[_dev(w, "weight").value for w in weights])
     yarr = (ctypes.c_void_p * n)(*[_dev(o, "output").value for o in outs])
@@ -357,8 +411,16 @@ def flare_mix(x, w_k, w_v, qs, H, w_ek=None, w_ev=None, w_o=None, out=None, scal
     output projection.  Returns out [B, N, C]."""
     B, N, C = x.shape
     M = qs.shape[1]
+    if C % H:
+        raise ValueError(f"C = {C} is not divisible by H = {H}")
+    _plain(x, (B, N, C), "x", x.dtype)
+    for name, w in (("w_k", w_k), ("w_v", w_v), ("w_ek", w_ek), ("w_ev", w_ev), ("w_o", w_o)):
+        if w is not None:
+            _plain(w, (C, C), name, x.dtype)
+    _plain(qs, (H, M, C // H), "qs", x.dtype)
     if out is None:
         out = torch.empty_like(x)
+    _plain(out, (B, N, C), "out", x.dtype)
     dyn, has_wo = w_ek is not None, w_o is not None
     ws = _workspace(mix_workspace_size(B, N, C, H, M, dyn, has_wo), x.device, workspace)
     ptr = lambda t: _opt_dev(t, "mixer operand")

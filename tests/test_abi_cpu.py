@@ -207,3 +207,26 @@ def test_binding_refuses_host_tensors():
         fb.describe(k)
     with pytest.raises(ValueError, match="on the GPU"):
         fb._dev(torch.zeros(4), "workspace")
+
+
+def test_binding_checks_extents_before_any_call():
+    # extents that disagree with the sizes the binding passes are refused
+    # before the library is called (shape checks come before the device check)
+    import torch
+    bf = torch.bfloat16
+    k = torch.zeros(2, 3, 64, 32, dtype=bf)
+    with pytest.raises(ValueError, match="q must be"):
+        fb.flare_encode(torch.zeros(3, 8, 16, dtype=bf), k, k)           # D of q differs
+    with pytest.raises(ValueError, match="q must be"):
+        fb.flare_encode(torch.zeros(1, 3, 8, 32, dtype=bf), k, k)        # [1, H, M, D] with B = 2
+    with pytest.raises(ValueError, match="v must be"):
+        fb.flare_encode(torch.zeros(3, 8, 32, dtype=bf), k, k[:, :, :32])
+    with pytest.raises(ValueError, match="y must be"):
+        fb.flare_decode(k, torch.zeros(3, 8, 32, dtype=bf), torch.zeros(2, 3, 8, 32),
+                        y=torch.zeros(2, 3, 63, 32, dtype=bf))
+    with pytest.raises(ValueError, match="weight 1"):
+        fb.flare_project(torch.zeros(2, 10, 64, dtype=bf), [torch.zeros(64, 64, dtype=bf),
+                                                             torch.zeros(64, 32, dtype=bf)])
+    with pytest.raises(ValueError, match="qs must be"):
+        fb.flare_mix(torch.zeros(1, 10, 64, dtype=bf), torch.zeros(64, 64, dtype=bf),
+                     torch.zeros(64, 64, dtype=bf), torch.zeros(2, 8, 16, dtype=bf), 2)

@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--no-mix", action="store_true", help="skip the FLARE++ mixer measurement")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-sweep", action="store_true", help="skip the sweep over the token count")
-    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle sample")
     ap.add_argument("--y-layout", choices=("token", "head"), default="token")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))

@@ -319,6 +319,15 @@ def main():
             return b0.elapsed_time(b1) / bsteps
         bms = time_bwd(pair)
         sms = time_bwd(two_calls)
+        dk_h = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+        dv_h = torch.empty_like(dk_h)
+
+        def pair_bf16():
+            rl.flare_encdec_backward(q, k, v, zf, lse_e, yb, lse_d, dy, dq=dq_b, dk=dk_h, dv=dv_h,
+                                     workspace=wsp, stream=stream)
+
+        hms = time_bwd(pair_bf16)
+        del dk_h, dv_h
         bwk = costs.encdec_backward(B, H, N, M, D)
         extra["encdec_backward"] = {
             "config": "gradients of FLARE encode+decode (dQ, dK, dV) at the bench sizes, bf16 inputs, "
@@ -326,7 +335,8 @@ def main():
             "ms": round(bms, 4), "tokens_per_s": tokens / (bms / 1e3),
             "tflops": round(bwk.flops / (bms / 1e3) / 1e12, 1),
             "over_forward": round(bms / ms_step, 3),
-            "two_calls_ms": round(sms, 4)}
+            "two_calls_ms": round(sms, 4),
+            "bf16_gradients_ms": round(hms, 4)}
         del zf, yb, dy, dk_b, dv_b, dq_b, dz_b, wsd, wse, wsp
 
     if not args.no_mix:

@@ -191,7 +191,10 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V,
  *   dq = scale sum dS k,  dk = scale sum dS q,  dv = sum P do.
  * P is recomputed from the normaliser the forward call returned (lse).
  * Token-side inputs (K, V, Y, dY) must be bf16; token-side gradients (dK,
- * dV) are fp32 [B, H, N, D] views; dZ and dQ are contiguous fp32 arrays,
+ * dV) are [B, H, N, D] views in fp32 or bf16, both of one dtype (bf16
+ * gradients are formed in fp32 and rounded once when written; accumulation
+ * adds the stored value in fp32 before that rounding); dZ and dQ are
+ * contiguous fp32 arrays,
  * dZ [B, H, M, D], dQ [B, H, M, D] or, with FLARE_SUM_DQ_OVER_BATCH, [H, M, D]
  * holding the sum over the batch (the gradient of a query block shared by
  * the batch: FLARE's learned queries, FLARE++'s seeds).
@@ -248,7 +251,8 @@ flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
  *   Y, lse_dec      flare_decode's output and its [B, H, N] normalisers
  *   dY              upstream gradient of Y (bf16, like K, V, Y)
  *   dQ              fp32 [B, H, M, D] (or [H, M, D] with
- *                   FLARE_SUM_DQ_OVER_BATCH); dK, dV fp32 [B, H, N, D] views
+ *                   FLARE_SUM_DQ_OVER_BATCH); dK, dV [B, H, N, D] views, both fp32
+ *                   or both bf16
  * Flags as for the two calls (accumulation into dQ / dK, batch sum of dQ).
  * M above 256 runs the two calls internally.  Workspace:
  * flare_encdec_backward_workspace_size bytes, 256-byte aligned. */

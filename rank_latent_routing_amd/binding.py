@@ -278,15 +278,15 @@ def _dq_shape(B, H, M, D, flags):
 
 
 def flare_decode_backward(k, q, z, y, lse, dy, dk=None, dq=None, dz=None, flags=0, scale=0.0,
-                          workspace=None, stream=None):
-    """Gradients (dk [B, H, N, D] fp32, dq, dz [B, H, M, D] fp32) of
-    sum(dy * Y) for Y = flare_decode(k, q, z) with its lse.  ``flags``:
-    FLARE_ACCUMULATE_DQ / _DK add into the given dq / dk;
+                          workspace=None, stream=None, grad_dtype=torch.float32):
+    """Gradients (dk [B, H, N, D] in grad_dtype (fp32 or bf16), dq, dz
+    [B, H, M, D] fp32) of sum(dy * Y) for Y = flare_decode(k, q, z) with its
+    lse.  ``flags``: FLARE_ACCUMULATE_DQ / _DK add into the given dq / dk;
     FLARE_SUM_DQ_OVER_BATCH makes dq [H, M, D], summed over the batch."""
     B, H, N, D = _dims(k)
     M = q.shape[-2]
     dev = k.device
-    dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=grad_dtype, device=dev)
     dq = dq if dq is not None else torch.empty(_dq_shape(B, H, M, D, flags), dtype=torch.float32,
                                                device=dev)
     dz = dz if dz is not None else torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
@@ -306,9 +306,10 @@ def flare_decode_backward(k, q, z, y, lse, dy, dk=None, dq=None, dz=None, flags=
 
 
 def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, flags=0,
-                          scale=0.0, workspace=None, stream=None):
-    """Gradients (dq [B, H, M, D] fp32, dk, dv [B, H, N, D] fp32) of sum(dz * Z)
-    for Z = flare_encode(q, k, v) (or flare_route_queries) with its lse.
+                          scale=0.0, workspace=None, stream=None, grad_dtype=torch.float32):
+    """Gradients (dq [B, H, M, D] fp32, dk, dv [B, H, N, D] in grad_dtype, fp32
+    or bf16) of sum(dz * Z) for Z = flare_encode(q, k, v) (or
+    flare_route_queries) with its lse.
     ``flags``: FLARE_ACCUMULATE_DQ / _DK add into the given dq / dk;
     FLARE_SUM_DQ_OVER_BATCH makes dq [H, M, D], summed over the batch."""
     B, H, N, D = _dims(k)
@@ -316,8 +317,8 @@ def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, flags=
     dev = k.device
     dq = dq if dq is not None else torch.empty(_dq_shape(B, H, M, D, flags), dtype=torch.float32,
                                                device=dev)
-    dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
-    dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=grad_dtype, device=dev)
+    dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=dk.dtype, device=dev)
     _latent(q, B, H, M, D, "q")
     _latent(z, B, H, M, D, "z")
     for name, tt in (("v", v), ("dk", dk), ("dv", dv)):
@@ -334,17 +335,18 @@ def flare_encode_backward(q, k, v, z, lse, dz, dq=None, dk=None, dv=None, flags=
 
 
 def flare_encdec_backward(q, k, v, z, lse_enc, y, lse_dec, dy, dq=None, dk=None, dv=None, flags=0,
-                          scale=0.0, workspace=None, stream=None):
-    """Gradients (dq fp32, dk, dv [B, H, N, D] fp32) of sum(dy * Y) through the
-    FLARE pair Z = flare_encode(q, k, v), Y = flare_decode(k, q, z), given
-    both calls' outputs and normalisers.  ``flags`` as for the two calls."""
+                          scale=0.0, workspace=None, stream=None, grad_dtype=torch.float32):
+    """Gradients (dq fp32, dk, dv [B, H, N, D] in grad_dtype, fp32 or bf16) of
+    sum(dy * Y) through the FLARE pair Z = flare_encode(q, k, v),
+    Y = flare_decode(k, q, z), given both calls' outputs and normalisers.
+    ``flags`` as for the two calls."""
     B, H, N, D = _dims(k)
     M = q.shape[-2]
     dev = k.device
     dq = dq if dq is not None else torch.empty(_dq_shape(B, H, M, D, flags), dtype=torch.float32,
                                                device=dev)
-    dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
-    dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    dk = dk if dk is not None else torch.empty((B, H, N, D), dtype=grad_dtype, device=dev)
+    dv = dv if dv is not None else torch.empty((B, H, N, D), dtype=dk.dtype, device=dev)
     _latent(q, B, H, M, D, "q")
     _latent(z, B, H, M, D, "z")
     for name, tt in (("v", v), ("y", y), ("dy", dy), ("dk", dk), ("dv", dv)):

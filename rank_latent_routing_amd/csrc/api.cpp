@@ -145,6 +145,9 @@ bool f32_ptr_ok(const void* p) { return p && reinterpret_cast<uintptr_t>(p) % 4 
 
 constexpr unsigned kBwdFlags = FLARE_ACCUMULATE_DQ | FLARE_ACCUMULATE_DK | FLARE_SUM_DQ_OVER_BATCH;
 
+// Token-side gradients (dK, dV) are written in fp32 or bf16.
+bool grad_dtype_ok(int32_t d) { return d == FLARE_F32 || d == FLARE_BF16; }
+
 flare_status bwd_common_checks(int B, int H, int M, int64_t N, int D, float scale) {
   if (!sizes_ok(B, H, M, N, D)) {
     if (B >= 1 && H >= 1 && M >= 1 && N >= 1 && (M > kMaxM || !(D == 16 || D == 32)))
@@ -473,7 +476,7 @@ flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q,
   if (!token_tensor_ok(K) || !token_tensor_ok(Y) || !token_tensor_ok(dY) || !token_tensor_ok(dK) ||
       !latent_tensor_ok(Q) || !latent_tensor_ok(Z))
     return FLARE_E_INVALID;
-  if (K->dtype != FLARE_BF16 || Y->dtype != FLARE_BF16 || dY->dtype != FLARE_BF16 || dK->dtype != FLARE_F32)
+  if (K->dtype != FLARE_BF16 || Y->dtype != FLARE_BF16 || dY->dtype != FLARE_BF16 || !grad_dtype_ok(dK->dtype))
     return FLARE_E_UNSUPPORTED;
   if (!f32_ptr_ok(lse) || !f32_ptr_ok(dQ) || !f32_ptr_ok(dZ)) return FLARE_E_INVALID;
   if (flags & ~kBwdFlags) return FLARE_E_INVALID;
@@ -496,7 +499,8 @@ flare_status flare_decode_backward(const flare_tensor* K, const flare_tensor* Q,
   tp.w = view_of(Z);
   tp.z = tp.w;
   tp.lse = lse;
-  tp.dk = reinterpret_cast<float*>(dK->data);
+  tp.dk = dK->data;
+  tp.grad_bf16 = dK->dtype == FLARE_BF16;
   tp.dk_sb = dK->stride_b;
   tp.dk_sh = dK->stride_h;
   tp.dk_sl = dK->stride_l;
@@ -546,7 +550,7 @@ flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
   if (!token_tensor_ok(K) || !token_tensor_ok(V) || !token_tensor_ok(dK) || !token_tensor_ok(dV) ||
       !latent_tensor_ok(Q) || !latent_tensor_ok(Z))
     return FLARE_E_INVALID;
-  if (K->dtype != FLARE_BF16 || V->dtype != FLARE_BF16 || dK->dtype != FLARE_F32 || dV->dtype != FLARE_F32)
+  if (K->dtype != FLARE_BF16 || V->dtype != FLARE_BF16 || !grad_dtype_ok(dK->dtype) || dV->dtype != dK->dtype)
     return FLARE_E_UNSUPPORTED;
   if (!f32_ptr_ok(lse) || !f32_ptr_ok(dZ) || !f32_ptr_ok(dQ)) return FLARE_E_INVALID;
   if (flags & ~kBwdFlags) return FLARE_E_INVALID;
@@ -593,11 +597,12 @@ flare_status flare_encode_backward(const flare_tensor* Q, const flare_tensor* K,
   tp.w = dzv;
   tp.z = lp.z;
   tp.lse = lse;
-  tp.dk = reinterpret_cast<float*>(dK->data);
+  tp.dk = dK->data;
+  tp.grad_bf16 = dK->dtype == FLARE_BF16;
   tp.dk_sb = dK->stride_b;
   tp.dk_sh = dK->stride_h;
   tp.dk_sl = dK->stride_l;
-  tp.dv = reinterpret_cast<float*>(dV->data);
+  tp.dv = dV->data;
   tp.dv_sb = dV->stride_b;
   tp.dv_sh = dV->stride_h;
   tp.dv_sl = dV->stride_l;
@@ -632,7 +637,7 @@ flare_status flare_encdec_backward(const flare_tensor* Q, const flare_tensor* K,
       !token_tensor_ok(dK) || !token_tensor_ok(dV) || !latent_tensor_ok(Q) || !latent_tensor_ok(Z))
     return FLARE_E_INVALID;
   if (K->dtype != FLARE_BF16 || V->dtype != FLARE_BF16 || Y->dtype != FLARE_BF16 || dY->dtype != FLARE_BF16 ||
-      dK->dtype != FLARE_F32 || dV->dtype != FLARE_F32)
+      !grad_dtype_ok(dK->dtype) || dV->dtype != dK->dtype)
     return FLARE_E_UNSUPPORTED;
   if (!f32_ptr_ok(lse_enc) || !f32_ptr_ok(lse_dec) || !f32_ptr_ok(dQ)) return FLARE_E_INVALID;
   if (flags & ~kBwdFlags) return FLARE_E_INVALID;
@@ -723,11 +728,12 @@ flare_status flare_encdec_backward(const flare_tensor* Q, const flare_tensor* K,
   tp.lse_e = lse_enc;
   tp.lse_d = lse_dec;
   tp.delta_d = delta;
-  tp.dk = reinterpret_cast<float*>(dK->data);
+  tp.dk = dK->data;
+  tp.grad_bf16 = dK->dtype == FLARE_BF16;
   tp.dk_sb = dK->stride_b;
   tp.dk_sh = dK->stride_h;
   tp.dk_sl = dK->stride_l;
-  tp.dv = reinterpret_cast<float*>(dV->data);
+  tp.dv = dV->data;
   tp.dv_sb = dV->stride_b;
   tp.dv_sh = dV->stride_h;
   tp.dv_sl = dV->stride_l;

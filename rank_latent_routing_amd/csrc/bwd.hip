@@ -81,6 +81,31 @@ __device__ __forceinline__ View rows_from(View v, int m0) {
   return v;
 }
 
+// Store 16 gradient values of one lane (features f .. f + 15 of a token) at
+// p: fp32 as four 16-byte stores, or bf16 as two; with accumulate the old
+// values are added first (in fp32; the bf16 sum rounds once).
+__device__ __forceinline__ void store_grad16(void* p, bool bf16_out, bool accumulate, const float (&v)[16]) {
+  if (bf16_out) {
+    bf16x8* q = reinterpret_cast<bf16x8*>(p);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 o;
+      const bf16x8 old = accumulate ? q[half] : bf16x8{};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = (bf16)(accumulate ? v[8 * half + j] + (float)old[j] : v[8 * half + j]);
+      q[half] = o;
+    }
+  } else {
+    f32x4* q = reinterpret_cast<f32x4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 o = {v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+      if (accumulate) o += q[j];
+      q[j] = o;
+    }
+  }
+}
+
 // ------------------------------------------------------- token-parallel pass
 // waves per workgroup: 4 in the decode role, 8 in the encode role (whose
 // larger latent staging leaves one workgroup per CU)
@@ -274,21 +299,17 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
     for (int tb = 0; tb < 2; ++tb) {
       const int64_t n = base + 32 * tb + c;
       if (n >= p.N || 16 * h >= D) continue;
-      float* kp = p.dk + b * p.dk_sb + hd * p.dk_sh + n * p.dk_sl + 16 * h;
+      const int es = p.grad_bf16 ? 2 : 4;  // bytes per gradient element
+      float g[16];
 #pragma unroll
-      for (int j = 0; j < 16; j += 4) {
-        f32x4 v = {dk[tb][j] * p.scale, dk[tb][j + 1] * p.scale, dk[tb][j + 2] * p.scale, dk[tb][j + 3] * p.scale};
-        if (p.accumulate) v += *reinterpret_cast<const f32x4*>(kp + j);
-        *reinterpret_cast<f32x4*>(kp + j) = v;
-      }
+      for (int j = 0; j < 16; ++j) g[j] = dk[tb][j] * p.scale;
+      store_grad16(reinterpret_cast<char*>(p.dk) + (b * p.dk_sb + hd * p.dk_sh + n * p.dk_sl + 16 * h) * es,
+                   p.grad_bf16, p.accumulate, g);
       if constexpr (ENC) {
-        float* vp = p.dv + b * p.dv_sb + hd * p.dv_sh + n * p.dv_sl + 16 * h;
 #pragma unroll
-        for (int j = 0; j < 16; j += 4) {
-          f32x4 vv = {dv[tb][j], dv[tb][j + 1], dv[tb][j + 2], dv[tb][j + 3]};
-          if (p.accumulate_v) vv += *reinterpret_cast<const f32x4*>(vp + j);
-          *reinterpret_cast<f32x4*>(vp + j) = vv;
-        }
+        for (int j = 0; j < 16; ++j) g[j] = dv[tb][j];
+        store_grad16(reinterpret_cast<char*>(p.dv) + (b * p.dv_sb + hd * p.dv_sh + n * p.dv_sl + 16 * h) * es,
+                     p.grad_bf16, p.accumulate_v, g);
       }
     }
   }
@@ -423,15 +444,16 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
     }
     // lane (h, c): token n, features 16h .. 16h + 15
     if (valid && 16 * h < D) {
-      float* kp = p.dk + b * p.dk_sb + hd * p.dk_sh + n * p.dk_sl + 16 * h;
-      float* vp = p.dv + b * p.dv_sb + hd * p.dv_sh + n * p.dv_sl + 16 * h;
+      const int es = p.grad_bf16 ? 2 : 4;  // bytes per gradient element
+      float g[16];
 #pragma unroll
-      for (int j = 0; j < 16; j += 4) {
-        f32x4 kv = {dk[j] * p.scale, dk[j + 1] * p.scale, dk[j + 2] * p.scale, dk[j + 3] * p.scale};
-        if (p.accumulate) kv += *reinterpret_cast<const f32x4*>(kp + j);
-        *reinterpret_cast<f32x4*>(kp + j) = kv;
-        *reinterpret_cast<f32x4*>(vp + j) = f32x4{dv[j], dv[j + 1], dv[j + 2], dv[j + 3]};
-      }
+      for (int j = 0; j < 16; ++j) g[j] = dk[j] * p.scale;
+      store_grad16(reinterpret_cast<char*>(p.dk) + (b * p.dk_sb + hd * p.dk_sh + n * p.dk_sl + 16 * h) * es,
+                   p.grad_bf16, p.accumulate, g);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) g[j] = dv[j];
+      store_grad16(reinterpret_cast<char*>(p.dv) + (b * p.dv_sb + hd * p.dv_sh + n * p.dv_sl + 16 * h) * es,
+                   p.grad_bf16, false, g);
     }
   }
 }

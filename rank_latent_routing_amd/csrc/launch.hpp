@@ -59,10 +59,11 @@ struct TokBwdParams {
   View k, x, y;          // token-side bf16 [B, H, N, D]; y: decode role only
   View q, w, z;          // latent-side [B, H, M, D]; z: encode role only
   const float* lse;      // natural-log normalisers: [B, H, N] (decode) or [B, H, M] (encode)
-  float* dk;             // fp32 [B, H, N, D] view
+  void* dk;              // [B, H, N, D] view, fp32 or (grad_bf16) bf16
   int64_t dk_sb, dk_sh, dk_sl;
-  float* dv;             // encode role only
+  void* dv;              // encode role only; same dtype as dk
   int64_t dv_sb, dv_sh, dv_sl;
+  int grad_bf16;         // dk and dv are bf16 (accumulation adds in fp32, then rounds)
   float* delta;          // decode role: [B, H, N] written
   int H, M;
   int64_t N;
@@ -83,10 +84,11 @@ struct TokPairParams {
   const float* lse_e;    // encoder normalisers [B, H, M], natural log
   const float* lse_d;    // decoder normalisers [B, H, N], natural log
   const float* delta_d;  // dY . Y [B, H, N]
-  float* dk;             // fp32 [B, H, N, D] views
+  void* dk;              // [B, H, N, D] views, fp32 or (grad_bf16) bf16
   int64_t dk_sb, dk_sh, dk_sl;
-  float* dv;
+  void* dv;
   int64_t dv_sb, dv_sh, dv_sl;
+  int grad_bf16;
   int H, M;
   int64_t N;
   float c, scale;

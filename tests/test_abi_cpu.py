@@ -146,11 +146,13 @@ def test_backward_calls_reject_bad_arguments():
     ws = ctypes.c_void_p(FAKE)
     need = L.flare_decode_backward_workspace_size(1, 1, 8, 10, 32)
     assert need > 0 and L.flare_encode_backward_workspace_size(1, 1, 8, 10, 32) > 0
-    # token-side inputs must be bf16, token-side gradients fp32
+    # token-side inputs must be bf16; token-side gradients fp32 or bf16 (one
+    # dtype for dK and dV), nothing else
     assert L.flare_decode_backward(r(f32), r(ok), r(ok), r(ok), p, r(ok), r(f32), p, p, 0, 1, 1, 8, 10, 32,
                                    0.0, ws, need, None) == fb.FLARE_E_UNSUPPORTED
-    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), p, r(ok), r(ok), p, p, 0, 1, 1, 8, 10, 32,
-                                   0.0, ws, need, None) == fb.FLARE_E_UNSUPPORTED
+    bad_dtype = T(dtype=5)
+    assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), p, r(ok), r(bad_dtype), p, p, 0, 1, 1, 8, 10,
+                                   32, 0.0, ws, need, None) == fb.FLARE_E_INVALID
     # the normaliser is required; sizes; workspace
     assert L.flare_decode_backward(r(ok), r(ok), r(ok), r(ok), None, r(ok), r(f32), p, p, 0, 1, 1, 8, 10, 32,
                                    0.0, ws, need, None) == fb.FLARE_E_INVALID
@@ -164,6 +166,7 @@ def test_backward_calls_reject_bad_arguments():
     need = L.flare_encode_backward_workspace_size(1, 1, 8, 10, 32)
     assert L.flare_encode_backward(r(ok), r(ok), r(ok), r(ok), p, p, p, r(f32), r(f32), 8, 1, 1, 8, 10, 32,
                                    0.0, ws, need, None) == fb.FLARE_E_INVALID
+    # dK bf16 with dV fp32: the two gradients must share one dtype
     assert L.flare_encode_backward(r(ok), r(ok), r(ok), r(ok), p, p, p, r(ok), r(f32), 0, 1, 1, 8, 10, 32,
                                    0.0, ws, need, None) == fb.FLARE_E_UNSUPPORTED
     assert L.flare_encode_backward(r(ok), r(ok), r(ok), r(ok), p, p, p, r(f32), r(f32), 0, 1, 1, 8, 10, 32,

@@ -836,6 +836,41 @@ def test_degenerate_inputs(case):
             check_bf16(f64(got), ref, f"{name} ({case})")
 
 
+@pytest.mark.parametrize("B,H,N,D,M,qm", [(2, 3, 777, 32, 200, 4.0), (1, 2, 1000, 16, 64, 2.0),
+                                           (1, 2, 900, 32, 300, 3.0)])
+def test_backward_bf16_gradients(B, H, N, D, M, qm):
+    # dK, dV written in bf16 (formed in fp32, rounded once; accumulation in
+    # the two-call chain, and over the 256-latent blocks at M = 300, adds in
+    # fp32 before rounding): against the oracle at the bf16 bar, and against
+    # the same calls' fp32 gradients within a few bf16 roundings
+    w = inputs.Workload("t", "encdec", B, N, H, D, M, "bf16")
+    x = inputs.make_encdec(w, seed=N + M, q_mult=qm)
+    dy_t = inputs.normal_tensor((B, N, H, D), "bf16", seed=N + 1)
+    q = x["q"].to(DEV)
+    k, v, dy = hm(x["k"]).contiguous().to(DEV), hm(x["v"]).contiguous().to(DEV), hm(dy_t).contiguous().to(DEV)
+    z, le = rl.flare_encode(q, k, v, want_lse=True, z_dtype=torch.float32)
+    y, ld = rl.flare_decode(k, q, z, want_lse=True)
+    acc = rl.FLARE_ACCUMULATE_DQ | rl.FLARE_ACCUMULATE_DK
+    res = {}
+    for gd in (torch.float32, torch.bfloat16):
+        one = rl.flare_encdec_backward(q, k, v, z, le, y, ld, dy, grad_dtype=gd)
+        dk2, dq2, dz2 = rl.flare_decode_backward(k, q, z, y, ld, dy, grad_dtype=gd)
+        two = rl.flare_encode_backward(q, k, v, z, le, dz2, dq=dq2, dk=dk2, flags=acc, grad_dtype=gd)
+        res[gd] = (one, two)
+    torch.cuda.synchronize()
+    dqr, dkr, dvr = oracle.flare_encdec_backward(f64(x["q"]), f64(hm(x["k"])), f64(hm(x["v"])), f64(hm(dy_t)))
+    for form in (0, 1):
+        tag = ("one call", "two calls")[form]
+        g16, g32 = res[torch.bfloat16][form], res[torch.float32][form]
+        assert g16[1].dtype == torch.bfloat16 and g16[2].dtype == torch.bfloat16
+        for name, i, ref in (("dQ", 0, dqr), ("dK", 1, dkr), ("dV", 2, dvr)):
+            check_bf16(f64(g16[i]), ref, f"{name} ({tag}, bf16 gradients)")
+        for name, i in (("dK", 1), ("dV", 2)):
+            e = rel_l2(f64(g16[i]), f64(g32[i]))
+            say(f"  {name} ({tag}): bf16 against fp32 gradients rel-L2 {e:.2e}")
+            assert e <= 6e-3
+
+
 def test_graph_capture_replays_match_eager():
     # flare_mix (FLARE++, B=8, N=4096, C=128, M=64) and the pair backward
     # captured into HIP graphs: the library issues only kernel launches on the

@@ -51,15 +51,15 @@ __global__ __launch_bounds__(256) void swizzle_weights_kernel(SwizzleParams p) {
   wsw[g] = v;
 }
 
-constexpr int kGemmTiles = 2;                          // 16-row tiles per wave
-constexpr int kGemmRowsPerWave = 16 * kGemmTiles;
 constexpr int kGemmWaves = 8;
-constexpr int kGemmRowsPerBlock = kGemmRowsPerWave * kGemmWaves;
 
-template <int CIN>
+// RB 16-row tiles per wave (two, or one for small R so that the grid still
+// covers the chip), eight waves per workgroup.
+template <int CIN, int RB>
 __global__ __launch_bounds__(64 * kGemmWaves, 4) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int RB = kGemmTiles;
   constexpr int NW = kGemmWaves;
+  constexpr int kGemmRowsPerWave = 16 * RB;
+  constexpr int kGemmRowsPerBlock = kGemmRowsPerWave * NW;
   constexpr int KS = CIN / 32;
   constexpr int BLK = KS * 2 * 512;  // bf16 elements of one 32-column block
   constexpr int OPS = BLK / 512;     // 1 KB loads per block
@@ -218,16 +218,24 @@ hipError_t launch_swizzle_weights(const SwizzleParams& p, int n, hipStream_t st)
 }
 
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t st) {
-  const int64_t blocks = (p.R + kGemmRowsPerBlock - 1) / kGemmRowsPerBlock;
-  dim3 grid((unsigned)blocks);
+  // two row tiles per wave once that still gives 512 workgroups (two per CU)
+  const int rb = (p.R + 16 * 2 * kGemmWaves - 1) / (16 * 2 * kGemmWaves) >= 512 ? 2 : 1;
+  const int64_t rows_per_block = 16 * rb * kGemmWaves;
+  dim3 grid((unsigned)((p.R + rows_per_block - 1) / rows_per_block));
   dim3 block(64 * kGemmWaves);
+#define FLARE_GEMM(C)                                                                  \
+  if (rb == 2)                                                                       \
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, 2>), grid, block, 0, st, p);             \
+  else                                                                               \
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, 1>), grid, block, 0, st, p)
   switch (p.Cin) {
-    case 32: hipLaunchKernelGGL((gemm_bf16_kernel<32>), grid, block, 0, st, p); break;
-    case 64: hipLaunchKernelGGL((gemm_bf16_kernel<64>), grid, block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL((gemm_bf16_kernel<128>), grid, block, 0, st, p); break;
-    case 256: hipLaunchKernelGGL((gemm_bf16_kernel<256>), grid, block, 0, st, p); break;
+    case 32: FLARE_GEMM(32); break;
+    case 64: FLARE_GEMM(64); break;
+    case 128: FLARE_GEMM(128); break;
+    case 256: FLARE_GEMM(256); break;
     default: return hipErrorInvalidValue;
   }
+#undef FLARE_GEMM
   return hipGetLastError();
 }
 

@@ -143,7 +143,7 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU (asked for --gpus {args.gpus}); "
               "multi-GPU sharding of the encoder is a design note, not built.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

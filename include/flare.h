@@ -44,7 +44,7 @@ extern "C" {
 typedef enum flare_status {
   FLARE_OK = 0,
   FLARE_E_INVALID = -1,     /* null pointer, size out of range, bad stride/alignment */
-  FLARE_E_UNSUPPORTED = -2, /* valid request outside what this build implements */
+  FLARE_E_UNSUPPORTED = -2, /* valid request outside what the library implements */
   FLARE_E_WORKSPACE = -3,   /* workspace NULL or smaller than required */
   FLARE_E_HIP = -4          /* a HIP launch/runtime error */
 } flare_status;

@@ -497,7 +497,34 @@ def main():
             torch.cuda.synchronize()
             ems = e0.elapsed_time(e1) / reps
             emem = (torch.cuda.max_memory_allocated() - base_mem) / 1e9
-            del sq, sk, sv, sz, syt, sy, sws
+            # the pair backward at the same size (one call, fp32 gradients);
+            # its memory is the peak of the forward and backward buffers
+            szf, sle = rl.flare_encode(sq, sk, sv, want_lse=True, z_dtype=torch.float32, workspace=sws,
+                                       stream=stream)
+            syb, sld = rl.flare_decode(sk, sq, szf, want_lse=True, stream=stream)
+            sdy = torch.randn(syb.shape, generator=torch.Generator(device=dev).manual_seed(1), device=dev,
+                              dtype=torch.float32).to(torch.bfloat16)
+            sdq = torch.empty((1, H, M, D), dtype=torch.float32, device=dev)
+            sdk = torch.empty((1, H, n_tok, D), dtype=torch.float32, device=dev)
+            sdv = torch.empty_like(sdk)
+            swb = torch.empty(rl.lib().flare_encdec_backward_workspace_size(1, H, M, n_tok, D), dtype=torch.uint8,
+                              device=dev)
+
+            def pair_bwd():
+                rl.flare_encdec_backward(sq, sk, sv, szf, sle, syb, sld, sdy, dq=sdq, dk=sdk, dv=sdv,
+                                         workspace=swb, stream=stream)
+            breps = max(3, reps // 3)
+            for _ in range(2):
+                pair_bwd()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(breps):
+                pair_bwd()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            bms_ = e0.elapsed_time(e1) / breps
+            bmem = (torch.cuda.max_memory_allocated() - base_mem) / 1e9
+            del sq, sk, sv, sz, syt, sy, sws, szf, sle, syb, sld, sdy, sdq, sdk, sdv, swb
             torch.cuda.empty_cache()
             torch.cuda.reset_peak_memory_stats()
             base_mem = torch.cuda.memory_allocated()
@@ -522,11 +549,13 @@ def main():
             mmem = (torch.cuda.max_memory_allocated() - base_mem) / 1e9
             del mm, mout, mws2
             sweep.append({"N": n_tok, "encdec_ms": round(ems, 4), "encdec_tokens_per_s": n_tok / (ems / 1e3),
-                          "encdec_mem_GB": round(emem, 4), "flarepp_mixer_ms": round(mms_, 4),
+                          "encdec_mem_GB": round(emem, 4), "backward_ms": round(bms_, 4),
+                          "backward_tokens_per_s": n_tok / (bms_ / 1e3), "fwd_bwd_mem_GB": round(bmem, 4),
+                          "flarepp_mixer_ms": round(mms_, 4),
                           "flarepp_mixer_tokens_per_s": n_tok / (mms_ / 1e3), "flarepp_mixer_mem_GB": round(mmem, 4)})
-        extra["n_sweep"] = {"config": "B=1, H=8, D=32, M=256, bf16; FLARE encode+decode, and the FLARE++ mixer "
-                                      "with all projections at C=256; memory = peak device memory of inputs, "
-                                      "outputs and workspace",
+        extra["n_sweep"] = {"config": "B=1, H=8, D=32, M=256, bf16; FLARE encode+decode, its one-call backward "
+                                      "(fp32 dK, dV), and the FLARE++ mixer with all projections at C=256; "
+                                      "memory = peak device memory of inputs, outputs, gradients and workspace",
                             "points": sweep}
 
     cpu = None

@@ -53,8 +53,11 @@ typedef enum flare_dtype { FLARE_F32 = 0, FLARE_BF16 = 1 } flare_dtype;
 
 /* Force the exact running-maximum softmax in every kernel.  Without it the
  * kernels first try a range-checked form without the maximum and fall back
- * to the exact form for any tile whose normaliser leaves [2^-100, 2^100];
- * both give the same softmax up to rounding. */
+ * to the exact form for any token split (encoder) or token group (decoder)
+ * in which a normaliser l summing n weights leaves [n 2^-102, 2^100]; inside
+ * that range no weight overflows and the weights the exponential flushes to
+ * zero carry less than 2^-24 of l, so both forms give the same softmax up to
+ * fp32 rounding. */
 #define FLARE_FLAG_EXACT_SOFTMAX 1u
 
 /*

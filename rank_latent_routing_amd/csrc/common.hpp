@@ -31,10 +31,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Range inside which a softmax normaliser computed without the running
-// maximum is accepted (see the encode and decode kernels).
-constexpr float kSafeLo = 7.888609052210118e-31f;  // 2^-100
-constexpr float kSafeHi = 1.2676506002282294e30f;  // 2^100
+// Acceptance of a softmax normaliser l computed without the running maximum
+// (weights 2^x relative to 2^0; see the encode and decode kernels).
+//  - Upper end: l <= 2^100 keeps every weight and every sum of weights finite.
+//  - Lower end: v_exp_f32 returns 0 for results below 2^-126, so each of the
+//    n weights a normaliser sums may lose up to 2^-126 of mass, n 2^-126 in
+//    all.  Requiring l >= n 2^-102 bounds that loss by 2^-24 l, below the
+//    rounding of the fp32 sum itself, for any n.
+constexpr float kSafeLoPerTerm = 1.9721522630525295e-31f;  // 2^-102
+constexpr float kSafeHi = 1.2676506002282294e30f;          // 2^100
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -7,8 +7,9 @@
 // A workgroup stages its head's latent side once in LDS, already in matrix-core
 // operand order: Q in bf16 (A operand of S^T = Q K^T) and Z transposed (A
 // operand of Y^T = Z^T P^T).  Each wave then streams 64-token groups of K
-// straight from HBM into registers (prefetching the next group while it
-// computes the current one) and walks the latents 32 at a time with
+// from HBM into a private LDS slot by buffer loads that write LDS directly
+// (the next group's load is in flight while the current group is computed),
+// reads the B operands from that slot, and walks the latents 32 at a time with
 // v_mfma_f32_32x32x16_bf16.  A lane's 16 scores of a chunk all belong to its
 // token, so every token's softmax stays in two lanes: the weights are packed
 // to bf16 in place as the B operand of Z^T P^T, the normaliser is the dot2 sum
@@ -17,9 +18,11 @@
 // token.
 //
 // As in the encoder, the first pass uses weights 2^x without a maximum; a
-// 64-token group whose normaliser leaves [2^-100, 2^100] (or whose output is
-// not finite) is recomputed with the exact two-pass softmax (row maximum
-// first).  FLARE_FLAG_EXACT_SOFTMAX forces it.
+// 64-token group in which some token's normaliser over its M latents leaves
+// [M 2^-102, 2^100] (or whose output is not finite) is recomputed with the
+// exact two-pass softmax (row maximum first).  The bounds keep the weights
+// finite and the mass of flushed weights below fp32 rounding.
+// FLARE_FLAG_EXACT_SOFTMAX forces the exact form.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -106,11 +109,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
     for (int u = lane; u < KSLOT / 8; u += 64) reinterpret_cast<bf16x8*>(kslot)[u] = z8;
   }
   // Each weight is at most the normaliser l it sums into, so with every
-  // |Z| < 2^26 and l within [2^-100, 2^100] the unnormalised outputs stay
-  // below 2^126: only l needs checking before the fast result is kept.
+  // |Z| < 2^26 and l <= 2^100 the unnormalised outputs stay below 2^126:
+  // only l needs checking before the fast result is kept.
   const bool z_small = __syncthreads_and(z_bounded) != 0;
 
-  const bf16 zero = (bf16)0.0f;
   const float cs = p.c;
   const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + hd * p.k.sh;
   // Workgroup b takes the (NW x 64)-token passes b, b + G, b + 2G, ... of its
@@ -119,16 +121,21 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
   const int64_t n_end = p.N;
   const int64_t pass_stride = (int64_t)gridDim.x * kDecGroup * NW;
 
-  // K of a 64-token group comes by buffer loads straight into the wave's LDS
-  // slot (uniform descriptor, loop-invariant 32-bit lane offsets; tokens past
-  // the end fall outside the descriptor's range).  The next group's load is in
-  // flight while the current group is computed.
-  // Load t covers tokens 16t/ROWC*4 ..: its lane offset is the same for every
-  // t (the swizzle depends on token bits 2..3 only) plus a uniform part.
+  // K of a 64-token group comes by buffer loads into the wave's LDS slot
+  // (a uniform descriptor covering exactly the group's valid rows, and
+  // loop-invariant 32-bit lane offsets).  The next group's load is in flight
+  // while the current group is computed.
+  // Load t covers tokens (64 / ROWC) t .. +63 / ROWC; lane l reads token
+  // (64 / ROWC) t + l / ROWC.  The swizzle depends on token bits 2..3 only,
+  // so it is the same for every t.  The whole byte offset sits in the lane
+  // (VGPR) operand, the part the hardware compares with the descriptor's
+  // range: a lane whose token is past the end reads zeros instead of memory
+  // beyond the tensor.  (The scalar offset operand is not range-checked, so
+  // it stays 0.)
   const int k_tok = lane / ROWC, k_sw = lane % ROWC;
   const int k_dc = D == 32 ? (k_sw ^ ((k_tok >> 2) & 3)) : (k_sw ^ ((k_tok >> 2) & 1));
-  const uint32_t k_off = (uint32_t)((k_tok * p.k.sl + k_dc * 8) * (int64_t)sizeof(bf16));
-  const int k_step = (int)((64 / ROWC) * p.k.sl * (int64_t)sizeof(bf16));  // bytes per load
+  const uint32_t k_off0 = (uint32_t)((k_tok * p.k.sl + k_dc * 8) * (int64_t)sizeof(bf16));
+  const uint32_t k_step = (uint32_t)((64 / ROWC) * p.k.sl * (int64_t)sizeof(bf16));  // bytes per load
   auto issue_k = [&](int64_t g0) {
     const int64_t rows = g0 < n_end ? min((int64_t)kDecGroup, n_end - g0) : 0;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
         (int)(rows * p.k.sl * (int64_t)sizeof(bf16)), kBufferFlags);
 #pragma unroll
     for (int t = 0; t < KOPS; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(kslot + t * 512), 16, k_off, t * k_step, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(kslot + t * 512), 16, k_off0 + t * k_step, 0, 0, 0);
   };
 
   int64_t base = (int64_t)blockIdx.x * kDecGroup * NW + kDecGroup * wave;
@@ -240,11 +247,13 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
 
     bool exact = p.exact != 0;
     if (!exact) {
+      // each token's normaliser sums 32 MC weights
+      const float lsum_lo = (float)(32 * MC) * kSafeLoPerTerm;
       pass(std::integral_constant<bool, false>());
       bool bad = false;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        bool ok = lsum[tb] >= kSafeLo && lsum[tb] <= kSafeHi;
+        bool ok = lsum[tb] >= lsum_lo && lsum[tb] <= kSafeHi;
         if (!z_small) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) ok = ok && __builtin_isfinite(yacc[tb][i]);

@@ -26,12 +26,14 @@
 // matrix-core and vector work largely add up rather than overlap, so this
 // per-score instruction count is what the design minimises.
 //
-// The first pass runs without a running maximum (weights relative to 2^0);
-// a split is accepted when every latent's normaliser lies in [2^-100, 2^100]
-// and its output is finite, which rules out overflow and underflow, and the
-// weights are then the max-shifted ones up to rounding.  Otherwise the
-// workgroup reruns the split with the exact running-maximum online softmax
-// (always used with FLARE_FLAG_EXACT_SOFTMAX).
+// The first pass runs without a running maximum (weights relative to 2^0).
+// A split of n tokens is accepted when every latent's normaliser l lies in
+// [n 2^-102, 2^100] and its output is finite.  The upper end rules out
+// overflow.  At the lower end, the weights the exponential flushes to zero
+// (each below 2^-126) carry less than 2^-24 of l, so the result equals the
+// max-shifted softmax up to fp32 rounding.  Otherwise the workgroup reruns
+// the split with the exact running-maximum online softmax (always used with
+// FLARE_FLAG_EXACT_SOFTMAX).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -367,7 +369,9 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 4 : 3)) void encode_bf16_kernel
     encode_pass<D, NW, false>(p, kbase, vbase, s, p.S, n_end, ntiles, k0, k1, k2, k3, v0, v1, v2, v3, qop, o, ls, mrun);
     const float lp = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     float l = lp + shfl_xor_f(lp, 32);
-    bool ok = l >= kSafeLo && l <= kSafeHi;
+    // the split sums at most ntiles * kEncT weights
+    const float lo = (float)ntiles * (float)kEncT * kSafeLoPerTerm;
+    bool ok = l >= lo && l <= kSafeHi;
 #pragma unroll
     for (int i = 0; i < 16; ++i) ok = ok && __builtin_isfinite(o[i]);
     const bool bad = m_lane < p.M && !ok;

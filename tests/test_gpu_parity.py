@@ -951,3 +951,95 @@ def test_backward_after_exact_forward(qm, flags):
     check_grad(f64(dq), dqr, "dQ", dvr)
     check_grad(f64(dk), dkr, "dK", dvr)
     check_bf16(f64(dv), dvr, "dV")
+
+
+# ------------------------------------------------ fast softmax acceptance range
+# The first pass of the encoder forms weights 2^x with no running maximum and
+# keeps a split when every latent's normaliser l (a sum of n weights) lies in
+# [n 2^-102, 2^100].  The exponential returns 0 for results below 2^-126, so
+# a split whose weights mostly fall just below that threshold loses up to
+# n 2^-126 of its mass; the lower end scales with n so that this loss stays
+# below fp32 rounding and any split beyond it is recomputed exactly.
+
+def _flush_band_inputs(N, H, D, M):
+    """One head-major block [1, H, N, D] of keys and values and [H, M, D]
+    queries.  With scale ln 2 (base-2 scores s = q.k), latents j < 4 score
+    every token but the last one at s = -126.125 - 0.125 j (weights just below
+    the flush threshold) and the last token at s = -99.875 + 0.125 j.  Those
+    latents weigh only features 0..3 of the keys, where the bulk tokens hold
+    (1, 0, 1, 0) and the last one (0, 1, 0, 1); features 4.. of the bulk keys,
+    the other latents and the values are random, so every other softmax is an
+    ordinary one.  The designed scores are exact in bf16 arithmetic.  The bulk
+    values have mean zero: a large mean shared by every latent's Z would leave
+    the decoder's gradient dependent on differences between Z rows far below
+    bf16 resolution (Z enters the decoder's matrix products in bf16)."""
+    g = np.random.default_rng(4242)
+    k = np.zeros((1, H, N, D), np.float32)
+    k[..., :-1, 4:] = g.standard_normal((1, H, N - 1, D - 4), dtype=np.float32)
+    k[..., :-1, 0] = 1.0
+    k[..., :-1, 2] = 1.0          # bulk tokens: s = q0 + q2
+    k[..., -1, 1] = 1.0
+    k[..., -1, 3] = 1.0           # last token: s = q1 + q3
+    ramp = np.arange(D, dtype=np.float32) / 64.0
+    v = np.empty((1, H, N, D), np.float32)
+    v[..., :-1, :] = 0.5 * g.standard_normal((1, H, N - 1, D), dtype=np.float32)
+    v[..., -1, :] = 1.0 - ramp
+    q = (g.standard_normal((H, M, D)) * 0.5).astype(np.float32)
+    for j in range(4):
+        q[:, j, :] = 0.0
+        q[:, j, 0] = -126.0
+        q[:, j, 2] = -0.125 * (j + 1)
+        q[:, j, 1] = -96.0
+        q[:, j, 3] = -3.875 + 0.125 * j
+    to = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    return to(q), to(k), to(v)
+
+
+def test_fast_softmax_long_split_near_flush_threshold():
+    # B*H = 1024 gives one split per (batch, head): every workgroup sums all
+    # 2^20 tokens.  The batch shares one block of keys and values (stride 0),
+    # so all B results equal the oracle's per-head result.
+    B, H, N, D, M = 128, 8, 1 << 20, 32, 32
+    scale = math.log(2.0)
+    qt, kt, vt = _flush_band_inputs(N, H, D, M)
+    parts = B * H * 1 * M
+    ws_one_split = (parts * D * 4 + 255) // 256 * 256 + (parts * 4 + 255) // 256 * 256
+    assert rl.encode_workspace_size(B, H, M, N, D) == ws_one_split
+    say(f"encode B={B} H={H} N={N} D={D} M={M}, one split per head")
+    q = qt.to(DEV)
+    k1 = kt.to(DEV)
+    v1 = vt.to(DEV)
+    k = k1.expand(B, H, N, D)
+    v = v1.expand(B, H, N, D)
+    z, lse = rl.flare_encode(q, k, v, want_lse=True, scale=scale, z_dtype=torch.float32)
+    torch.cuda.synchronize()
+    zr, lr = oracle.encode(f64(qt), f64(kt), f64(vt), scale)
+    # Every latent within the bf16 bar.  The flush-band latents' weights take
+    # two values (bulk and last token), each rounded once to bf16, which moves
+    # their ratio r ~ 1e-2 by at most 2^-8 relative: an error near 1e-4 of Z.
+    # They are held to 1e-3; flushing the bulk mass unseen would cost r / (1 + r),
+    # 0.8 to 1.3 %.
+    for b in (0, B - 1):
+        for h in range(H):
+            for m in range(M):
+                e = rel_l2(f64(z[b, h, m]), zr[0, h, m])
+                assert e <= (1e-3 if m < 4 else BF16_TOL), (b, h, m, e)
+        check_bf16(f64(lse[b]), lr[0], f"lse batch {b}")
+    worst = max(rel_l2(f64(z[0, h, j]), zr[0, h, j]) for h in range(H) for j in range(4))
+    say(f"  flush-band latents: worst per-latent rel-L2 {worst:.3e}")
+
+    # The backward of the pair on one batch element, from this forward's Z and
+    # lse (the encoder's normalisers of the long split), against the oracle's
+    # chain rule on heads 0 and 1.
+    zb, lseb = z[0:1].contiguous(), lse[0:1].contiguous()
+    y, lse_d = rl.flare_decode(k1, q, zb, want_lse=True, scale=scale)
+    dy_t = inputs.normal_tensor((1, N, H, D), "bf16", seed=91)
+    dy = hm(dy_t).contiguous().to(DEV)
+    dq, dk, dv = rl.flare_encdec_backward(q, k1, v1, zb, lseb, y, lse_d, dy, scale=scale)
+    torch.cuda.synchronize()
+    say("oracle: chain-rule gradients of heads 0 and 1 over all tokens")
+    dqr, dkr, dvr = oracle.flare_encdec_backward(f64(qt[0:2]), f64(kt[:, 0:2]), f64(vt[:, 0:2]),
+                                                 f64(hm(dy_t)[:, 0:2]), scale)
+    check_grad(f64(dq[:, 0:2]), dqr, "dQ heads 0-1", dqr)
+    check_grad(f64(dk[:, 0:2]), dkr, "dK heads 0-1", dkr)
+    check_grad(f64(dv[:, 0:2]), dvr, "dV heads 0-1", dvr)

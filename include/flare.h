@@ -46,7 +46,8 @@ typedef enum flare_status {
   FLARE_E_INVALID = -1,     /* null pointer, size out of range, bad stride/alignment */
   FLARE_E_UNSUPPORTED = -2, /* valid request outside what the library implements */
   FLARE_E_WORKSPACE = -3,   /* workspace NULL or smaller than required */
-  FLARE_E_HIP = -4          /* a HIP launch/runtime error */
+  FLARE_E_HIP = -4,         /* a HIP launch/runtime error */
+  FLARE_E_SCRATCH = -5      /* sizes beyond flare_encode_static's static scratch */
 } flare_status;
 
 typedef enum flare_dtype { FLARE_F32 = 0, FLARE_BF16 = 1 } flare_dtype;
@@ -270,6 +271,29 @@ flare_status flare_encdec_backward(const flare_tensor* Q, const flare_tensor* K,
                                    int B, int H, int M, int64_t N, int D,
                                    float scale, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/*
+ * flare_encode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Arguments, layouts, results and errors are those of
+ * flare_encode.  The split partials live in a static device array of
+ * flare_encode_static_scratch_bytes() bytes (64 MiB), one per GPU, held from
+ * the library's first use on that GPU until the process ends; the call itself
+ * allocates nothing.  When the encoder's own split plan needs more, the call
+ * uses fewer, longer splits (the merged result then differs from flare_encode's
+ * by rounding only); when even one split per (batch, head) needs more
+ * (B*H*M*(D+1)*4 bytes, rounded up to 256-byte blocks), it returns
+ * FLARE_E_SCRATCH before launching anything.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, two host threads) race on it and must be ordered by the
+ * caller.  The stream must belong to the current device.
+ */
+size_t flare_encode_static_scratch_bytes(void);
+flare_status flare_encode_static(const flare_tensor* Q, const flare_tensor* K,
+                                 const flare_tensor* V, const flare_tensor* Z,
+                                 float* lse, int B, int H, int M, int64_t N,
+                                 int D, float scale, unsigned flags,
+                                 void* stream);
 
 /* Static text for a status code. */
 const char* flare_status_string(int status);

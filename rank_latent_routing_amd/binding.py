@@ -23,6 +23,7 @@ FLARE_E_INVALID = -1
 FLARE_E_UNSUPPORTED = -2
 FLARE_E_WORKSPACE = -3
 FLARE_E_HIP = -4
+FLARE_E_SCRATCH = -5
 FLARE_F32 = 0
 FLARE_BF16 = 1
 FLARE_FLAG_EXACT_SOFTMAX = 1
@@ -37,6 +38,7 @@ EXPORTS = ("flare_encode_workspace_size", "flare_encode", "flare_route_queries",
            "flare_decode_backward_workspace_size", "flare_decode_backward",
            "flare_encode_backward_workspace_size", "flare_encode_backward",
            "flare_encdec_backward_workspace_size", "flare_encdec_backward",
+           "flare_encode_static_scratch_bytes", "flare_encode_static",
            "flare_status_string", "flare_version")
 
 
@@ -73,6 +75,9 @@ def lib():
     L.flare_encode.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
     L.flare_route_queries.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
     L.flare_decode.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp]
+    L.flare_encode_static.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp]
+    L.flare_encode_static_scratch_bytes.argtypes = []
+    L.flare_encode_static_scratch_bytes.restype = sz
     L.flare_decode_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32]
     L.flare_decode_backward_workspace_size.restype = sz
     L.flare_decode_backward.argtypes = [T, T, T, T, vp, T, T, vp, vp, u32, i32, i32, i32, i64, i32,
@@ -93,7 +98,8 @@ def lib():
     L.flare_mix_workspace_size.restype = sz
     L.flare_mix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32,
                             f32, u32, vp, sz, vp]
-    for f in ("flare_encode", "flare_route_queries", "flare_decode", "flare_project", "flare_mix",
+    for f in ("flare_encode", "flare_encode_static", "flare_route_queries", "flare_decode",
+              "flare_project", "flare_mix",
               "flare_decode_backward", "flare_encode_backward", "flare_encdec_backward"):
         getattr(L, f).restype = ctypes.c_int
     L.flare_status_string.argtypes = [i32]
@@ -222,6 +228,31 @@ def flare_encode(q, k, v, z=None, want_lse=False, scale=0.0, flags=0, workspace=
                            _stream(stream))
     _check(s, "flare_encode")
     return (z, lse) if want_lse else z
+
+
+def flare_encode_static(q, k, v, z=None, want_lse=False, scale=0.0, flags=0, stream=None,
+                        z_dtype=None):
+    """flare_encode without a workspace: the split partials live in the
+    library's static per-GPU scratch (see include/flare.h), so nothing is
+    allocated for them.  Calls that overlap on one GPU share that scratch and
+    must be ordered by the caller."""
+    B, H, N, D = _dims(k)
+    M = q.shape[-2]
+    _latent(q, B, H, M, D, "q")
+    _token(v, B, H, N, D, "v")
+    if z is None:
+        z = torch.empty((B, H, M, D), dtype=z_dtype or k.dtype, device=k.device)
+    _latent(z, B, H, M, D, "z", shared=False)
+    lse = torch.empty((B, H, M), dtype=torch.float32, device=k.device) if want_lse else None
+    s = lib().flare_encode_static(describe(q), describe(k), describe(v), describe(z),
+                                  _opt_dev(lse, "lse"), B, H, M, N, D, float(scale), int(flags),
+                                  _stream(stream))
+    _check(s, "flare_encode_static")
+    return (z, lse) if want_lse else z
+
+
+def encode_static_scratch_bytes() -> int:
+    return lib().flare_encode_static_scratch_bytes()
 
 
 def flare_route_queries(seeds, ek, ev, qx=None, scale=0.0, flags=0, workspace=None,

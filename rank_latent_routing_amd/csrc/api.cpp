@@ -12,6 +12,7 @@
 #include <cstring>
 
 #include "../../include/flare.h"
+#include "api_internal.hpp"
 #include "launch.hpp"
 
 using namespace flare;
@@ -70,17 +71,20 @@ View view_of(const flare_tensor* t) {
 
 flare_status hip_status(hipError_t e) { return e == hipSuccess ? FLARE_OK : FLARE_E_HIP; }
 
-size_t encode_ws(int B, int H, int M, int64_t N, int D, int is_f32) {
-  const EncodePlan pl = plan_encode(B, H, M, N, D, is_f32);
+size_t encode_ws(int B, int H, int M, int64_t N, int D, int is_f32, int max_splits = 0) {
+  const EncodePlan pl = plan_encode(B, H, M, N, D, is_f32, max_splits);
   const size_t parts = (size_t)B * H * pl.S * M;
   return align_up(parts * D * sizeof(float)) + align_up(parts * sizeof(float));
 }
 
 // Encoder on validated arguments: split kernel + merge into Z (and lse).
+// max_splits > 0 caps the split count (the workspace then needs
+// encode_ws(..., max_splits) bytes).
 flare_status encode_impl(const View& q, const View& k, const View& v, void* z, int z_f32,
                          int64_t z_sb, int64_t z_sh, int64_t z_sl, float* lse, int B, int H, int M,
-                         int64_t N, int D, float c, unsigned flags, void* ws, hipStream_t st) {
-  const EncodePlan pl = plan_encode(B, H, M, N, D, k.is_f32);
+                         int64_t N, int D, float c, unsigned flags, void* ws, hipStream_t st,
+                         int max_splits = 0) {
+  const EncodePlan pl = plan_encode(B, H, M, N, D, k.is_f32, max_splits);
   const size_t parts = (size_t)B * H * pl.S * M;
   EncodeParams ep;
   ep.q = q;
@@ -219,6 +223,45 @@ flare_status project_impl(const void* X, const void* const* W, void* const* Y, i
 
 }  // namespace
 
+namespace flare {
+
+flare_status encode_validate(const flare_tensor* Q, const flare_tensor* K, const flare_tensor* V,
+                             const flare_tensor* Z, const float* lse, int B, int H, int M, int64_t N,
+                             int D, float scale, unsigned flags) {
+  if (!sizes_ok(B, H, M, N, D)) {
+    if (B >= 1 && H >= 1 && M >= 1 && N >= 1 && (M > kMaxM || !(D == 16 || D == 32)))
+      return FLARE_E_UNSUPPORTED;
+    return FLARE_E_INVALID;
+  }
+  if (!latent_tensor_ok(Q) || !token_tensor_ok(K) || !token_tensor_ok(V) || !latent_tensor_ok(Z))
+    return FLARE_E_INVALID;
+  if (K->dtype != V->dtype) return FLARE_E_INVALID;
+  if (!scale_ok(scale) || (flags & ~FLARE_FLAG_EXACT_SOFTMAX)) return FLARE_E_INVALID;
+  if (lse && reinterpret_cast<uintptr_t>(lse) % 4) return FLARE_E_INVALID;
+  return FLARE_OK;
+}
+
+int encode_splits_within(int B, int H, int M, int64_t N, int D, int is_f32, size_t max_bytes) {
+  int S = plan_encode(B, H, M, N, D, is_f32).S;
+  while (S > 1 && encode_ws(B, H, M, N, D, is_f32, S) > max_bytes) {
+    // the bytes are linear in S: jump close to the largest S that fits
+    const size_t one = encode_ws(B, H, M, N, D, is_f32, 1);
+    const int fit = (int)std::max<size_t>(1, max_bytes / std::max<size_t>(one, 1));
+    S = std::min(S - 1, fit);
+  }
+  return encode_ws(B, H, M, N, D, is_f32, S) <= max_bytes ? S : 0;
+}
+
+flare_status encode_run(const flare_tensor* Q, const flare_tensor* K, const flare_tensor* V,
+                        const flare_tensor* Z, float* lse, int B, int H, int M, int64_t N, int D,
+                        float scale, unsigned flags, void* ws, int max_splits, void* stream) {
+  return encode_impl(view_of(Q), view_of(K), view_of(V), Z->data, Z->dtype == FLARE_F32, Z->stride_b,
+                     Z->stride_h, Z->stride_l, lse, B, H, M, N, D, log2_scale(scale, D), flags, ws,
+                     reinterpret_cast<hipStream_t>(stream), max_splits);
+}
+
+}  // namespace flare
+
 extern "C" {
 
 const char* flare_version(void) { return "0.1.0"; }
@@ -230,6 +273,7 @@ const char* flare_status_string(int s) {
     case FLARE_E_UNSUPPORTED: return "unsupported configuration";
     case FLARE_E_WORKSPACE: return "workspace missing or too small";
     case FLARE_E_HIP: return "HIP runtime error";
+    case FLARE_E_SCRATCH: return "sizes exceed the static scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -244,22 +288,12 @@ static flare_status encode_checked(const flare_tensor* Q, const flare_tensor* K,
                                    const flare_tensor* Z, float* lse, int B, int H, int M, int64_t N,
                                    int D, float scale, unsigned flags, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  if (!sizes_ok(B, H, M, N, D)) {
-    if (B >= 1 && H >= 1 && M >= 1 && N >= 1 && (M > kMaxM || !(D == 16 || D == 32)))
-      return FLARE_E_UNSUPPORTED;
-    return FLARE_E_INVALID;
-  }
-  if (!latent_tensor_ok(Q) || !token_tensor_ok(K) || !token_tensor_ok(V) || !latent_tensor_ok(Z))
-    return FLARE_E_INVALID;
-  if (K->dtype != V->dtype) return FLARE_E_INVALID;
-  if (!scale_ok(scale) || (flags & ~FLARE_FLAG_EXACT_SOFTMAX)) return FLARE_E_INVALID;
-  if (lse && reinterpret_cast<uintptr_t>(lse) % 4) return FLARE_E_INVALID;
+  const flare_status v = flare::encode_validate(Q, K, V, Z, lse, B, H, M, N, D, scale, flags);
+  if (v != FLARE_OK) return v;
   const size_t need = encode_ws(B, H, M, N, D, K->dtype == FLARE_F32);
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 16)
     return FLARE_E_WORKSPACE;
-  return encode_impl(view_of(Q), view_of(K), view_of(V), Z->data, Z->dtype == FLARE_F32, Z->stride_b,
-                     Z->stride_h, Z->stride_l, lse, B, H, M, N, D, log2_scale(scale, D), flags,
-                     workspace, reinterpret_cast<hipStream_t>(stream));
+  return flare::encode_run(Q, K, V, Z, lse, B, H, M, N, D, scale, flags, workspace, 0, stream);
 }
 
 flare_status flare_encode(const flare_tensor* Q, const flare_tensor* K, const flare_tensor* V,

@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
 
 // ---------------------------------------------------------------- launchers
 
-EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32) {
+EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32, int max_splits) {
   (void)D;
   (void)is_f32;
   EncodePlan pl;
@@ -576,6 +576,7 @@ EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32) {
   int64_t max_s = tiles / 2;
   if (max_s < 1) max_s = 1;
   if (S > max_s) S = max_s;
+  if (max_splits > 0 && S > max_splits) S = max_splits;
   if (S < 1) S = 1;
   pl.S = (int)S;
   pl.tokens_per_split = (tiles + S - 1) / S * kEncT;

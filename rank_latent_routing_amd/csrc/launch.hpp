@@ -133,7 +133,9 @@ struct EncodePlan {
   int waves;                // waves per workgroup (bf16 path)
   int lat_blocks;           // 16-latent blocks per wave (bf16 path)
 };
-EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32);
+// max_splits > 0 caps the number of splits (fewer, longer splits need less
+// scratch for their partial results; the merged result differs by rounding).
+EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32, int max_splits = 0);
 
 hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, int lat_blocks, hipStream_t s);
 hipError_t launch_encode_f32(const EncodeParams& p, int D, int B, hipStream_t s);

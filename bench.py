@@ -44,7 +44,24 @@ def parse():
     ap.add_argument("--y-layout", choices=("token", "head"), default="token")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
+    ap.add_argument("--summarize", nargs="+", metavar=("NAME", "INPUT"),
+                    help="host only: write profiles/<NAME>.md from rocprofv3 output (NAME: units, "
+                         "issue_rates TIMING.md PMC_DIRS..., stats TRACE_DIR)")
     return ap.parse_args()
+
+
+def summarize(name, inputs):
+    """Writes one committed profile summary from rocprofv3 output directories."""
+    from rank_latent_routing_amd import profiling
+    os.makedirs(PROFILES, exist_ok=True)
+    if name == "units":
+        b = profiling.write_units(os.path.join(PROFILES, "units.encdec_n1m.md"), inputs)
+        for k, v in b.items():
+            print(f"{k}: {v['cycles']:.0f} cycles per block, VALU issue {v['issue']:.0f}, none {v['idle']:.0f}")
+    elif name == "issue_rates":
+        profiling.write_issue_rates(os.path.join(PROFILES, "issue_rates.gfx950.md"), inputs[1:], inputs[0])
+    else:
+        raise SystemExit(f"unknown summary {name}")
 
 
 # Sources whose change invalidates a stored counter reading of a kernel
@@ -150,6 +167,8 @@ def main():
         return copy_calibration()
     if args.write_traffic:
         return write_traffic(*args.write_traffic)
+    if args.summarize:
+        return summarize(args.summarize[0], args.summarize[1:])
 
     import numpy as np
     import torch

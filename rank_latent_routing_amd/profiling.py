@@ -1,0 +1,262 @@
+"""Summaries of rocprofv3 output for the committed profiles (host only).
+
+Every markdown file under ``profiles/`` that reports counters or kernel times
+is written by this module from the CSV files rocprofv3 leaves in its output
+directories, through ``python bench.py --summarize NAME DIR [DIR ...]``.  Each
+recipe below names the rocprofv3 commands that produce its inputs; the file
+it writes repeats them.  Nothing here touches a GPU.
+
+Counter conventions on gfx950 (rocprofv3's descriptions, checked against the
+issue-rate probes of ``probes/issue.hip``, whose instruction mix is known):
+
+* ``GRBM_GUI_ACTIVE`` is summed over the 8 XCDs: kernel cycles = value / 8.
+* ``SQ_ACTIVE_INST_VALU`` counts VALU issue quad-cycles (4 cycles) summed over
+  waves: one per VALU instruction or matrix-core issue, two per
+  transcendental instruction.
+* ``SQ_ACTIVE_INST_VALU2`` counts quad-cycles in which a SIMD issued two VALU
+  instructions from two waves; while the matrix core is busy it stays near 0.
+* ``SQ_VALU_MFMA_BUSY_CYCLES`` counts matrix-core busy cycles per SIMD (32 per
+  v_mfma_f32_32x32x16_bf16).
+* ``SQ_BUSY_CYCLES`` and ``SQ_CYCLES`` are per shader engine (32 of them):
+  their ratio is the share of the kernel's time an engine held any wave.
+"""
+import collections
+import csv
+import glob
+import os
+
+XCDS = 8
+SIMDS = 1024  # 256 compute units x 4
+
+# VALU issue quads a 32 x 32 score block needs by the method: 4 matrix-core
+# issues, 16 scale multiplies, 16 exponentials (2 quads each), 8 bf16 packs
+# and 8 dot2 row sums.
+BLOCK_FLOOR_QUADS = 4 + 16 + 32 + 8 + 8
+
+BENCH_ARGS = "--steps 2 --warmup 1 --no-cpu --no-mix --no-bwd --no-sweep"
+PASSES = [
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_VALU2 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_LDS "
+    "SQ_WAIT_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE",
+    "SQ_INST_LEVEL_LDS SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_MISC "
+    "SQ_INSTS_SMEM SQ_INSTS_BRANCH SQ_CYCLES GRBM_GUI_ACTIVE",
+]
+PROBE_MIXES = "mfma,mul,exp,cvt,dot2,mul+exp,mfma+8mul,mfma+16exp,block,block-dep,block-nomul,block-hilo"
+PROBE_ITERS = 4000
+
+
+def _pmc_commands(target, regex, outdir):
+    return ["export TMPDIR=/tmp"] + [
+        f"timeout -s KILL 90 rocprofv3 --pmc {p} --kernel-include-regex \"{regex}\" -f csv "
+        f"-d gpurun_out/{outdir}{i + 1} -o run -- {target}" for i, p in enumerate(PASSES)]
+
+
+BUDGET_CMDS = _pmc_commands(f"python3 -u bench.py {BENCH_ARGS}", "encode_bf16|decode_bf16|merge_kernel",
+                            "pmc/bench")
+PROBE_CMDS = _pmc_commands(
+    f"python3 -u rank_latent_routing_amd/probes/run_probes.py --mixes {PROBE_MIXES} --wps 4 --no-split "
+    f"--iters {PROBE_ITERS}", "probe_kernel", "pmc/probe")
+
+
+def _csvs(dirs, pattern):
+    out = []
+    for d in dirs:
+        out += sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not out:
+        raise FileNotFoundError(f"no {pattern} under {dirs}")
+    return out
+
+
+def short_name(kernel):
+    """'void flare::encode_bf16_kernel<32, 8>(flare::EncodeParams)' -> 'encode_bf16_kernel<32, 8>'."""
+    k = kernel.split("(")[0]
+    for pre in ("void ", "flare::"):
+        k = k.replace(pre, "")
+    return k.strip()
+
+
+def dispatch_counters(dirs, select=None, by_pass=False):
+    """{kernel: [ {counter: value} per dispatch ]} from every counter CSV under
+    the given rocprofv3 output directories (the rows of a dispatch summed).
+    With by_pass, {kernel: {csv path: [dispatches]}} instead."""
+    per = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    for path in _csvs(dirs, "*counter_collection.csv"):
+        for row in csv.DictReader(open(path)):
+            k = short_name(row["Kernel_Name"])
+            if select and not any(s in k for s in select):
+                continue
+            per[k][(path, row["Dispatch_Id"])][row["Counter_Name"]] += float(row["Counter_Value"])
+    if by_pass:
+        out = collections.defaultdict(lambda: collections.defaultdict(list))
+        for k, d in per.items():
+            for (path, _), v in d.items():
+                out[k][path].append(v)
+        return out
+    return {k: list(d.values()) for k, d in per.items()}
+
+
+def counter_means(dirs, select=None):
+    """{kernel: {counter: mean over the dispatches that read it}}."""
+    out = {}
+    for k, ds in dispatch_counters(dirs, select).items():
+        acc = collections.defaultdict(list)
+        for d in ds:
+            for c, v in d.items():
+                acc[c].append(v)
+        out[k] = {c: sum(v) / len(v) for c, v in acc.items()}
+    return out
+
+
+def cycle_budget(c, units, floor_quads):
+    """Per-unit SIMD-cycle budget from counter means c (units: 32 x 32 score
+    blocks per dispatch, or probe loop iterations of all waves)."""
+    cycles = c["GRBM_GUI_ACTIVE"] / XCDS
+    nan = float("nan")
+    valu_q = c["SQ_ACTIVE_INST_VALU"] / units
+    dual_q = c.get("SQ_ACTIVE_INST_VALU2", 0.0) / units
+    issue = 4.0 * (valu_q - dual_q)
+    simd = cycles * SIMDS / units
+    return {
+        "cycles": simd, "valu_quads": valu_q, "dual_quads": dual_q, "issue": issue,
+        "floor": 4.0 * floor_quads, "extra": issue - 4.0 * floor_quads, "idle": simd - issue,
+        "mfma_busy": c.get("SQ_VALU_MFMA_BUSY_CYCLES", nan) / units,
+        "coexec": c.get("SQ_VALU_MFMA_COEXEC_CYCLES", nan) / units,
+        "valu": c.get("SQ_INSTS_VALU", nan) / units, "trans": c.get("SQ_INSTS_VALU_TRANS_F32", nan) / units,
+        "mfma": c.get("SQ_INSTS_MFMA", nan) / units, "lds": c.get("SQ_INSTS_LDS", nan) / units,
+        "salu": c.get("SQ_INSTS_SALU", nan) / units,
+        "se_busy": c["SQ_BUSY_CYCLES"] / c["SQ_CYCLES"] if "SQ_BUSY_CYCLES" in c and "SQ_CYCLES" in c else nan,
+    }
+
+
+def _budget_rows(means, units, floor_quads):
+    rows = ["| kernel | SIMD cycles per block | VALU issue | of which the method's floor | other VALU "
+            "| no VALU issued | dual issue (quads) | MFMA busy | MFMA busy while VALU issues | VALU instr. "
+            "| exp | MFMA | LDS instr. | SALU instr. | engines busy |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    budgets = {}
+    for k in sorted(means):
+        b = cycle_budget(means[k], units, floor_quads)
+        budgets[k] = b
+        rows.append(f"| `{k}` | {b['cycles']:.0f} | {b['issue']:.0f} ({b['valu_quads']:.1f} quads) "
+                    f"| {b['floor']:.0f} | {b['extra']:.0f} | {b['idle']:.0f} | {b['dual_quads']:.2f} "
+                    f"| {b['mfma_busy']:.0f} | {b['coexec']:.0f} | {b['valu']:.1f} | {b['trans']:.1f} "
+                    f"| {b['mfma']:.1f} | {b['lds']:.1f} | {b['salu']:.1f} | {100 * b['se_busy']:.0f}% |")
+    return rows, budgets
+
+
+def write_units(out, dirs):
+    """profiles/units.encdec_n1m.md: the per-block cycle budget of the bench's
+    encode and decode kernels."""
+    blocks = 8 * (1 << 20) * 256 // (32 * 32)
+    means = counter_means(dirs, ["encode_bf16", "decode_bf16"])
+    rows, b = _budget_rows(means, blocks, BLOCK_FLOOR_QUADS)
+    text = ["# Cycle budget of the encode and decode kernels, bench workload (FLARE encode+decode, B=1, H=8, D=32, "
+            "N=1048576, M=256, bf16)", "",
+            "Commands (repo root, one MI355X; three counter passes, each a run of its own), then "
+            "`python bench.py --summarize units gpurun_out/pmc/bench1 gpurun_out/pmc/bench2 gpurun_out/pmc/bench3`:",
+            "", "```"] + BUDGET_CMDS + ["```", "",
+            f"Values are means over every dispatch of a kernel in the three runs.  A block is 32 tokens x 32 "
+            f"latents of one head ({blocks} per dispatch).  Cycles are SIMD cycles at the clock the kernel ran "
+            "at: GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs, per block.  The counter readings are calibrated on "
+            "probe kernels of known instruction mix in `issue_rates.gfx950.md`.", ""] + rows + ["",
+            "How the columns add up, per block and SIMD:", "",
+            "- *VALU issue* is 4 x (SQ_ACTIVE_INST_VALU - SQ_ACTIVE_INST_VALU2) per block: the cycles the SIMD's "
+            "VALU port spends issuing. One quad per VALU instruction or matrix-core issue, two per exponential.",
+            f"- *The method's floor* is {BLOCK_FLOOR_QUADS} quads: 4 matrix-core issues, 16 scale multiplies, "
+            "16 exponentials, 8 bf16 packs and 8 dot2 row sums. *Other VALU* is the rest of the issue time "
+            "(accumulator copies, address and range arithmetic, the epilogue, amortised per block).",
+            "- *No VALU issued* is the kernel's cycles minus the issue time: cycles in which no wave of the SIMD "
+            "had a VALU instruction ready (waiting on LDS, on the tile barrier, on the matrix core's result or "
+            "its issue), plus the time a SIMD holds fewer waves (workgroup start-up and the tail; *engines busy* "
+            "is SQ_BUSY_CYCLES / SQ_CYCLES).",
+            "- *MFMA busy* runs under the VALU issue: the matrix core works while the VALU port issues "
+            "(the co-execution column), and no dual issue happens while it is busy. The 4 products of a block "
+            "take 128 cycles, below the floor's VALU issue time, so the exponentials and the other per-score "
+            "VALU work set the pace, not the matrix core or HBM."]
+    open(out, "w").write("\n".join(text) + "\n")
+    return b
+
+
+PROBE_NAMES = {0: "mfma", 1: "mul", 2: "exp", 3: "cvt", 4: "dot2", 5: "mul+exp", 7: "mfma+8mul", 11: "mfma+16exp",
+               12: "block", 13: "block-nomul", 15: "block-dep", 23: "block-hilo"}
+# (VALU instructions, MFMA instructions, exponentials) per loop iteration of one wave
+PROBE_MIX = {0: (8, 8, 0), 1: (32, 0, 0), 2: (32, 0, 32), 3: (16, 0, 0), 4: (16, 0, 0), 5: (32, 0, 16),
+             7: (72, 8, 0), 11: (136, 8, 128), 12: (52, 4, 16), 13: (36, 4, 16), 15: (52, 4, 16), 23: (38, 6, 16)}
+
+
+def write_issue_rates(out, dirs, timing_md):
+    """profiles/issue_rates.gfx950.md: the probes' timing table (run_probes
+    output) and their counter readings, which calibrate the counters."""
+    passes = dispatch_counters(dirs, ["probe_kernel"], by_pass=True)
+    per = {}
+    for k, byp in passes.items():
+        # each mix runs a short warm-up launch, then the measured one: take the
+        # longer launch of every pass and merge the passes' counters
+        merged = {}
+        for ds in byp.values():
+            merged.update(max(ds, key=lambda x: x.get("GRBM_GUI_ACTIVE", 0.0)))
+        per[k] = [merged]
+    waves = 256 * 16
+    rows = ["| probe mix | waves/SIMD | SQ_INSTS_VALU per iteration (expected) | SQ_ACTIVE_INST_VALU quads "
+            "(expected: 1 per instruction, 2 per exp) | dual-issue quads | MFMA busy cycles (expected 32 per "
+            "product) | SIMD cycles per iteration |", "|---|---|---|---|---|---|---|"]
+    for k in sorted(per, key=lambda s: int(s.split("<")[1].split(",")[0])):
+        idx = int(k.split("<")[1].split(",")[0])
+        d = max(per[k], key=lambda x: x.get("GRBM_GUI_ACTIVE", 0.0))  # the measured launch (not the warm-up)
+        n = waves * PROBE_ITERS
+        v, m, e = PROBE_MIX.get(idx, (0, 0, 0))
+        vi = d.get("SQ_INSTS_VALU", float("nan")) / n
+        q = d.get("SQ_ACTIVE_INST_VALU", float("nan")) / n
+        dq = d.get("SQ_ACTIVE_INST_VALU2", float("nan")) / n
+        mb = d.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / n
+        cyc = d["GRBM_GUI_ACTIVE"] / XCDS * SIMDS / n  # SIMD cycles per wave-iteration
+        rows.append(f"| {PROBE_NAMES.get(idx, idx)} | 4 | {vi:.1f} ({v}) | {q:.1f} ({v + e}) | {dq:.2f} "
+                    f"| {mb:.0f} ({32 * m}) | {cyc:.0f} |")
+    text = ["# Issue rates of the inner-loop instructions on gfx950 (MI355X)", "",
+            "Probe kernels (`rank_latent_routing_amd/probes/issue.hip`) loop over fixed instruction mixes on "
+            "independent registers, one workgroup per compute unit.", "",
+            "Timing (repo root, one MI355X): `python -m rank_latent_routing_amd.probes.run_probes`", "",
+            open(timing_md).read().strip(), "",
+            "## Counter calibration", "",
+            "The same probes under the counter passes the kernels' cycle budget uses "
+            "(`units.encdec_n1m.md`), then `python bench.py --summarize issue_rates gpurun_out/probes.md "
+            "gpurun_out/pmc/probe1 gpurun_out/pmc/probe2 gpurun_out/pmc/probe3`:", "", "```"] + PROBE_CMDS + [
+            "```", "", f"Per loop iteration of one wave ({waves} waves, {PROBE_ITERS} iterations):", ""] + rows + [
+            "", "Reading:", "",
+            "- SQ_ACTIVE_INST_VALU counts one quad-cycle per VALU instruction or matrix-core issue and two per "
+            "v_exp_f32; the matrix core counts 32 busy cycles per 32x32x16 product.",
+            "- Two waves can issue VALU in the same quad (the `mul` mix dual-issues), but not while an "
+            "exponential is in flight or the matrix core is busy: the mixed streams issue one VALU "
+            "instruction per 4 cycles.",
+            "- A block's mix (4 products, 16 multiplies, 16 exponentials, 8 packs, 8 row-sum dot2) is 68 issue "
+            "quads, 272 cycles; its 4 products (128 cycles) run under that issue time."]
+    open(out, "w").write("\n".join(text) + "\n")
+
+
+def write_kernel_stats(out, trace_dir, title, command, notes=()):
+    """A kernel-time table from rocprofv3 --kernel-trace --stats output."""
+    path = _csvs([trace_dir], "*kernel_stats.csv")[0]
+    rows = list(csv.DictReader(open(path)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# {title}", "", "Command (repo root, one MI355X), then `python bench.py --summarize stats "
+             f"{trace_dir}`:", "", "```", "export TMPDIR=/tmp", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} "
+                     f"| {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} "
+                     f"| {100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    lines += [""] + list(notes)
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def trace_durations(trace_dir, select):
+    """Durations (us) of each launch of the kernels matching `select`, in dispatch order."""
+    path = _csvs([trace_dir], "*kernel_trace.csv")[0]
+    out = collections.defaultdict(list)
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
+        k = short_name(r["Kernel_Name"])
+        if any(s in k for s in select):
+            out[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return dict(out)

@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     ap.add_argument("--summarize", nargs="+", metavar=("NAME", "INPUT"),
                     help="host only: write profiles/<NAME>.md from rocprofv3 output (NAME: units, "
-                         "issue_rates TIMING.md PMC_DIRS..., stats TRACE_DIR)")
+                         "units_gemm, issue_rates TIMING.md PMC_DIRS...)")
     return ap.parse_args()
 
 
@@ -58,6 +58,8 @@ def summarize(name, inputs):
         b = profiling.write_units(os.path.join(PROFILES, "units.encdec_n1m.md"), inputs)
         for k, v in b.items():
             print(f"{k}: {v['cycles']:.0f} cycles per block, VALU issue {v['issue']:.0f}, none {v['idle']:.0f}")
+    elif name == "units_gemm":
+        profiling.write_units_gemm(os.path.join(PROFILES, "units_gemm.mix_n1m.md"), inputs, PROFILES)
     elif name == "issue_rates":
         profiling.write_issue_rates(os.path.join(PROFILES, "issue_rates.gfx950.md"), inputs[1:], inputs[0])
     else:

@@ -54,8 +54,13 @@ __global__ __launch_bounds__(256) void swizzle_weights_kernel(SwizzleParams p) {
 constexpr int kGemmWaves = 8;
 
 // RB 16-row tiles per wave (two, or one for small R so that the grid still
-// covers the chip), eight waves per workgroup.
-template <int CIN, int RB>
+// covers the chip), eight waves per workgroup.  PAIR (row-major outputs with
+// an even number of 32-column blocks): the results of an even block are held
+// in registers until the next block is computed, and both are stored
+// together, so each 128-byte line of an output row (64 columns) is written
+// whole by one wave within a few instructions instead of in two halves a
+// block apart.
+template <int CIN, int RB, bool PAIR>
 __global__ __launch_bounds__(64 * kGemmWaves, 4) void gemm_bf16_kernel(GemmParams p) {
   constexpr int NW = kGemmWaves;
   constexpr int kGemmRowsPerWave = 16 * RB;
@@ -128,15 +133,19 @@ __global__ __launch_bounds__(64 * kGemmWaves, 4) void gemm_bf16_kernel(GemmParam
   // Store of one output row tile: lane (g, r) holds columns 8g .. 8g+7 of
   // block pb (tile 0 gives 8g..8g+3, tile 1 gives 8g+4..8g+7) for row
   // row0 + 16 rb + r.
-  auto store_row_tile = [&](const f32x4 (&acc)[2], int rb, int pr, int64_t col_off) {
+  auto pack_row_tile = [&](const f32x4 (&acc)[2]) {
     bf16x8 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[i] = (bf16)acc[0][i];
       v[4 + i] = (bf16)acc[1][i];
     }
+    return v;
+  };
+  auto store_packed = [&](bf16x8 v, int rb, int pr, int64_t col_off) {
     *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(p.y[pr]) + row_off[rb] + col_off) = v;
   };
+  bf16x8 carry[RB];  // PAIR: the packed results of the last even block
 
   const bool full_rows = row0 + kGemmRowsPerWave <= p.R;  // uniform in the wave
   auto compute_block = [&](auto stage_tag, int b) {
@@ -162,35 +171,61 @@ __global__ __launch_bounds__(64 * kGemmWaves, 4) void gemm_bf16_kernel(GemmParam
       const int hd = col / p.D;
       col_off = (int64_t)hd * p.N * p.D + (col - hd * p.D);
     }
-    if (full_rows) {
-      // exactly RB stores per block: the step's wait counts them
+    if constexpr (PAIR) {
+      if ((pb & 1) == 0) {  // uniform: kept for the next block
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) store_row_tile(acc[rb], rb, pr, col_off);
-    } else {
+        for (int rb = 0; rb < RB; ++rb) carry[rb] = pack_row_tile(acc[rb]);
+        return;
+      }
+    }
+    // full rows: exactly RB stores per block (2 RB for a pair), which the
+    // step's wait counts
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        if (row0 + 16 * rb + r < p.R) store_row_tile(acc[rb], rb, pr, col_off);
+    for (int rb = 0; rb < RB; ++rb) {
+      if (full_rows || row0 + 16 * rb + r < p.R) {
+        if constexpr (PAIR) store_packed(carry[rb], rb, pr, col_off - 32);
+        store_packed(pack_row_tile(acc[rb]), rb, pr, col_off);
+      }
     }
   };
 
   // Block b lives in stage b % 4.  Step b: start the load of block b + 3,
   // compute and store block b, then wait until this wave's load of block
-  // b + 1 has landed (vmcnt counts loads and stores in issue order: the
-  // loads of blocks b + 2 and b + 3 and the RB stores of block b may stay
-  // in flight) and meet at the barrier.
+  // b + 1 has landed and meet at the barrier.  vmcnt counts loads and
+  // stores in issue order, so the wait allows exactly the operations issued
+  // after that load: the loads of blocks b + 2 and b + 3 and the stores
+  // between them (RB per block; with PAIR, 2 RB at odd blocks and none at
+  // even ones, so the stores of block b - 1 when b is even).
   auto step = [&](auto stage_tag, int b) {
     constexpr int S = decltype(stage_tag)::value;
     if (b + 3 < nblk) issue(std::integral_constant<int, (S + 3) % 4>(), b + 3);
     compute_block(stage_tag, b);
     const int later = ((b + 3 < nblk) + (b + 2 < nblk)) * (my_ops != 0);  // loads issued after block b + 1
+    const int stores = PAIR ? (b > 0 ? 2 * RB : 0) : RB;  // stores issued after block b + 1's load
     if (!full_rows)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    else if (later == 2)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * OPW + RB));
-    else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(OPW + RB));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(RB));
+    else if (stores == 0) {
+      if (later == 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * OPW));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(OPW));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    } else if (stores == RB) {
+      if (later == 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * OPW + RB));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(OPW + RB));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(RB));
+    } else {
+      if (later == 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * OPW + 2 * RB));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(OPW + 2 * RB));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * RB));
+    }
     barrier_keep_loads();
   };
 
@@ -223,11 +258,18 @@ hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t st) {
   const int64_t rows_per_block = 16 * rb * kGemmWaves;
   dim3 grid((unsigned)((p.R + rows_per_block - 1) / rows_per_block));
   dim3 block(64 * kGemmWaves);
+  // whole 128-byte output lines per wave for row-major outputs of an even
+  // number of 32-column blocks
+  const bool pair = !p.head_major && (p.Cout / 32) % 2 == 0;
 #define FLARE_GEMM(C)                                                                  \
-  if (rb == 2)                                                                       \
-    hipLaunchKernelGGL((gemm_bf16_kernel<C, 2>), grid, block, 0, st, p);             \
+  if (rb == 2 && pair)                                                               \
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, 2, true>), grid, block, 0, st, p);       \
+  else if (rb == 2)                                                                  \
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, 2, false>), grid, block, 0, st, p);      \
+  else if (pair)                                                                     \
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, 1, true>), grid, block, 0, st, p);       \
   else                                                                               \
-    hipLaunchKernelGGL((gemm_bf16_kernel<C, 1>), grid, block, 0, st, p)
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, 1, false>), grid, block, 0, st, p)
   switch (p.Cin) {
     case 32: FLARE_GEMM(32); break;
     case 64: FLARE_GEMM(64); break;

@@ -198,7 +198,10 @@ def test_fp32_path_ragged_and_sharp():
 
 @pytest.mark.parametrize("R,Cin,Cout,nproj,head_dim", [
     (1000, 128, 128, 4, 16), (4096, 256, 256, 2, 32), (333, 256, 256, 5, None),
-    (64, 64, 96, 1, None), (2048, 32, 64, 3, 32)])
+    (64, 64, 96, 1, None), (2048, 32, 64, 3, 32),
+    # row-major outputs with paired column blocks and two row tiles per wave
+    # (R of at least 512 workgroups), ragged last rows
+    (140001, 256, 256, 1, None), (131331, 128, 192, 2, None), (140000, 64, 96, 1, None)])
 def test_projection_gemm(R, Cin, Cout, nproj, head_dim):
     B = 2 if head_dim and R % 2 == 0 else 1
     xs = inputs.normal_tensor((B, R // B, Cin), "bf16", seed=R)

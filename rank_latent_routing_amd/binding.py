@@ -11,35 +11,15 @@ contiguous last axis), or 3-d ``[H, L, D]`` for a block shared by the batch.
 without copying.
 """
 import ctypes
-import os
 
 import torch
 
-_HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_build", "libflare.so")
-
-FLARE_OK = 0
-FLARE_E_INVALID = -1
-FLARE_E_UNSUPPORTED = -2
-FLARE_E_WORKSPACE = -3
-FLARE_E_HIP = -4
-FLARE_E_SCRATCH = -5
-FLARE_F32 = 0
-FLARE_BF16 = 1
-FLARE_FLAG_EXACT_SOFTMAX = 1
-
-FLARE_ACCUMULATE_DQ = 1
-FLARE_ACCUMULATE_DK = 2
-FLARE_SUM_DQ_OVER_BATCH = 4
-
-EXPORTS = ("flare_encode_workspace_size", "flare_encode", "flare_route_queries",
-           "flare_decode", "flare_project_workspace_size", "flare_project",
-           "flare_mix_workspace_size", "flare_mix",
-           "flare_decode_backward_workspace_size", "flare_decode_backward",
-           "flare_encode_backward_workspace_size", "flare_encode_backward",
-           "flare_encdec_backward_workspace_size", "flare_encdec_backward",
-           "flare_encode_static_scratch_bytes", "flare_encode_static",
-           "flare_status_string", "flare_version")
+from .cabi import (EXPORTS, FLARE_ACCUMULATE_DK, FLARE_ACCUMULATE_DQ,  # noqa: F401
+                   FLARE_BF16, FLARE_E_HIP, FLARE_E_INVALID, FLARE_E_SCRATCH,
+                   FLARE_E_UNSUPPORTED, FLARE_E_WORKSPACE, FLARE_F32,
+                   FLARE_FLAG_EXACT_SOFTMAX, FLARE_OK, FLARE_SUM_DQ_OVER_BATCH,
+                   LIB_PATH, FlareTensor)
+from . import cabi as _cabi
 
 
 class FlareError(RuntimeError):
@@ -48,65 +28,15 @@ class FlareError(RuntimeError):
         super().__init__(f"{what}: {status_string(status)} ({status})")
 
 
-class FlareTensor(ctypes.Structure):
-    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("stride_b", ctypes.c_int64),
-                ("stride_h", ctypes.c_int64), ("stride_l", ctypes.c_int64)]
-
-
 _lib = None
 
 
 def lib():
-    """The loaded library; raises if it has not been built."""
+    """The loaded gfx950 library; raises if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(
-            f"HIP library not built ({LIB_PATH} missing): run __graft_entry__.build() "
-            "or python rank_latent_routing_amd/build.py")
-    L = ctypes.CDLL(LIB_PATH)
-    vp, i32, i64, f32, u32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
-                                  ctypes.c_float, ctypes.c_uint, ctypes.c_size_t)
-    T = ctypes.POINTER(FlareTensor)
-    L.flare_encode_workspace_size.argtypes = [i32, i32, i32, i64, i32]
-    L.flare_encode_workspace_size.restype = sz
-    L.flare_encode.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
-    L.flare_route_queries.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp, sz, vp]
-    L.flare_decode.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp]
-    L.flare_encode_static.argtypes = [T, T, T, T, vp, i32, i32, i32, i64, i32, f32, u32, vp]
-    L.flare_encode_static_scratch_bytes.argtypes = []
-    L.flare_encode_static_scratch_bytes.restype = sz
-    L.flare_decode_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32]
-    L.flare_decode_backward_workspace_size.restype = sz
-    L.flare_decode_backward.argtypes = [T, T, T, T, vp, T, T, vp, vp, u32, i32, i32, i32, i64, i32,
-                                        f32, vp, sz, vp]
-    L.flare_encode_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32]
-    L.flare_encode_backward_workspace_size.restype = sz
-    L.flare_encode_backward.argtypes = [T, T, T, T, vp, vp, vp, T, T, u32, i32, i32, i32, i64, i32,
-                                        f32, vp, sz, vp]
-    L.flare_encdec_backward_workspace_size.argtypes = [i32, i32, i32, i64, i32]
-    L.flare_encdec_backward_workspace_size.restype = sz
-    L.flare_encdec_backward.argtypes = [T, T, T, T, vp, T, vp, T, vp, T, T, u32, i32, i32, i32, i64, i32,
-                                        f32, vp, sz, vp]
-    L.flare_project_workspace_size.argtypes = [i32, i32, i32]
-    L.flare_project_workspace_size.restype = sz
-    L.flare_project.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i32,
-                                i32, i32, i32, i32, vp, sz, vp]
-    L.flare_mix_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
-    L.flare_mix_workspace_size.restype = sz
-    L.flare_mix.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32,
-                            f32, u32, vp, sz, vp]
-    for f in ("flare_encode", "flare_encode_static", "flare_route_queries", "flare_decode",
-              "flare_project", "flare_mix",
-              "flare_decode_backward", "flare_encode_backward", "flare_encdec_backward"):
-        getattr(L, f).restype = ctypes.c_int
-    L.flare_status_string.argtypes = [i32]
-    L.flare_status_string.restype = ctypes.c_char_p
-    L.flare_version.restype = ctypes.c_char_p
-    _lib = L
-    return L
+    if _lib is None:
+        _lib = _cabi.load(LIB_PATH)
+    return _lib
 
 
 def status_string(s: int) -> str:

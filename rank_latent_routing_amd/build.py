@@ -3,6 +3,11 @@
 Every source is compiled for gfx950 only, with packed-fp32 instruction
 selection disabled, and linked into one shared library that exports the C
 ABI of include/flare.h.
+
+build_host() links the same host code (argument checks, planners, workspace
+carving) with stand-ins for the kernel launchers into _build/libflare_host.so,
+with g++ and no device code; sanitize=True adds AddressSanitizer and
+UndefinedBehaviorSanitizer (host code only) as _build/libflare_host_san.so.
 """
 import concurrent.futures as cf
 import os
@@ -14,7 +19,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libflare.so")
-SOURCES = ["api.cpp", "encode.hip", "decode.hip", "gemm.hip", "bwd.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "encode.hip", "decode.hip", "gemm.hip", "bwd.hip", "noalloc.hip"]
+HOST_SOURCES = ["api.cpp", "plan.cpp", "launch_stub.cpp"]
+HOST_LIB = os.path.join(OUT_DIR, "libflare_host.so")
+HOST_SAN_LIB = os.path.join(OUT_DIR, "libflare_host_san.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -50,5 +58,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host(sanitize: bool = False, verbose: bool = False) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    out = HOST_SAN_LIB if sanitize else HOST_LIB
+    cmd = [os.environ.get("CXX", "g++"), "-O1" if sanitize else "-O2", "-g", "-std=c++17", "-fPIC", "-shared",
+           "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include")]
+    if sanitize:
+        cmd += ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+    cmd += [os.path.join(CSRC, s) for s in HOST_SOURCES]
+    cmd += ["-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host build failed:\n{r.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_host(verbose="-v" in sys.argv))
+    print(build_host(sanitize=True, verbose="-v" in sys.argv))

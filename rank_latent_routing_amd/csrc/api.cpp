@@ -4,7 +4,7 @@
 // so a rejected call never touches the device), split planning, carving of
 // the caller's workspace, and kernel launches on the caller's stream.  The
 // library allocates nothing and keeps no mutable state.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
 #include <cstdint>
@@ -362,7 +362,7 @@ namespace {
 struct MixLayout {
   size_t kv, qx, z, y, wsw, wosw, enc, total;
 };
-MixLayout mix_layout(int B, int64_t N, int C, int H, int M, int dynamic, int has_wo) {
+static MixLayout mix_layout(int B, int64_t N, int C, int H, int M, int dynamic, int has_wo) {
   MixLayout L;
   const int D = C / H;
   const size_t act = align_up((size_t)B * N * C * 2);
@@ -386,7 +386,7 @@ MixLayout mix_layout(int B, int64_t N, int C, int H, int M, int dynamic, int has
   L.total = off;
   return L;
 }
-bool mix_shape_ok(int B, int64_t N, int C, int H, int M) {
+static bool mix_shape_ok(int B, int64_t N, int C, int H, int M) {
   if (B < 1 || N < 1 || C < 1 || H < 1 || M < 1 || C % H) return false;
   return sizes_ok(B, H, M, N, C / H) && (C == 32 || C == 64 || C == 128 || C == 256) &&
          ((int64_t)B * N + 255) / 256 <= 0x7fffffff;

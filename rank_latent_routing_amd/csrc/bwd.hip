@@ -459,7 +459,6 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
 }
 
 // ------------------------------------------------------ latent-parallel pass
-constexpr int kLatBwdTile = 64;  // tokens per LDS tile
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -780,15 +779,6 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------- launchers
-
-int plan_bwd_splits(int B, int H, int M, int64_t N) {
-  const int64_t bh = (int64_t)B * H * ((M + 255) / 256);
-  const int64_t tiles = (N + kLatBwdTile - 1) / kLatBwdTile;
-  int64_t S = (1024 + bh - 1) / bh;
-  if (S > tiles) S = tiles;
-  if (S < 1) S = 1;
-  return (int)S;
-}
 
 static size_t tok_bwd_lds(int M, int D, bool enc) {
   const int MC = (M + 31) / 32;

@@ -34,8 +34,6 @@ __device__ __forceinline__ int chunk_latent(int ch, int u, int h, int j) {
   return 32 * ch + 16 * u + (j < 4 ? 4 * h + j : 8 + 4 * h + (j - 4));
 }
 
-constexpr int kDecWaves = 12;  // one workgroup per compute unit, 3 waves per SIMD
-constexpr int kDecGroup = 64;  // tokens per wave per step
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -376,29 +374,6 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------- launchers
-
-size_t decode_bf16_lds(int M, int D) {
-  const int MC = (M + 31) / 32;
-  return (size_t)MC * (D / 16) * 64 * 16 + (size_t)MC * 2 * 64 * 16 +
-         (size_t)kDecWaves * kDecGroup * D * sizeof(bf16);
-}
-
-// A persistent grid: as many workgroups as fit on the 256 compute units at
-// once (LDS and the 3-waves-per-SIMD register budget decide), spread evenly
-// over the heads; each takes every G-th pass of its head.
-int64_t plan_decode_bf16(int B, int H, int M, int64_t N, int D) {
-  const int64_t lds = (int64_t)decode_bf16_lds(M, D);
-  int64_t per_cu = (160 * 1024) / lds;
-  if (per_cu > 12 / kDecWaves) per_cu = 12 / kDecWaves;
-  if (per_cu < 1) per_cu = 1;
-  const int64_t bh = (int64_t)B * H;
-  const int64_t pass = (int64_t)kDecWaves * kDecGroup;
-  const int64_t passes = (N + pass - 1) / pass;
-  int64_t per_bh = (256 * per_cu + bh - 1) / bh;
-  if (per_bh > passes) per_bh = passes;
-  if (per_bh < 1) per_bh = 1;
-  return per_bh;
-}
 
 // Kernels that stage more than 64 KB of LDS must opt in to the larger limit.
 template <typename K>

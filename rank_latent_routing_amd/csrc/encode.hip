@@ -8,7 +8,7 @@
 // The N tokens of each (batch, head) are cut into S contiguous splits.  One
 // workgroup owns one split and all latents of its head, 32 per wave: it
 // streams 128-token K/V tiles from HBM straight into LDS with
-// global_load_lds_dwordx4 (three LDS stages, two tiles in flight, one barrier
+// global_load_lds_dwordx4 (four LDS stages, three tiles in flight, one barrier
 // per tile, no registers or vector instructions spent on staging) and every
 // wave multiplies them against its latents on bf16 matrix cores, 32 tokens at
 // a time.  V stays token-major in LDS; the transposed B operand of P V comes
@@ -38,9 +38,6 @@
 #include "launch.hpp"
 
 namespace flare {
-
-constexpr int kEncT = 128;  // tokens per LDS tile (four 32-token quarters)
-constexpr int kStages = 4;   // LDS tiles: one computed, three in flight
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -82,7 +79,6 @@ __device__ __forceinline__ void encode_pass(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
   const int i16 = lane & 15;
   const float cs = p.c;
-  const bf16 zero = (bf16)0.0f;
 
   o = zero16();
 #pragma unroll
@@ -556,32 +552,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
 }
 
 // ---------------------------------------------------------------- launchers
-
-EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32, int max_splits) {
-  (void)D;
-  (void)is_f32;
-  EncodePlan pl;
-  const int64_t bh = (int64_t)B * H;
-  // 32 latents per wave, up to 256 latents (8 waves) per workgroup; more
-  // latents take further workgroups along grid.z.
-  pl.waves = M <= 64 ? 2 : M <= 128 ? 4 : 8;
-  pl.lat_blocks = (M + 255) / 256;
-  // About 1024 workgroups in all (a few per compute unit, a few rounds), at
-  // least two 128-token tiles per split when there are enough tokens.  The
-  // matrix-core path gives split s the tiles s, s + S, ...; the fp32 path
-  // takes S contiguous ranges of tokens_per_split tokens (the last ones may
-  // be empty and merge with weight 0).
-  const int64_t tiles = (N + kEncT - 1) / kEncT;
-  int64_t S = (1024 + bh - 1) / bh;
-  int64_t max_s = tiles / 2;
-  if (max_s < 1) max_s = 1;
-  if (S > max_s) S = max_s;
-  if (max_splits > 0 && S > max_splits) S = max_splits;
-  if (S < 1) S = 1;
-  pl.S = (int)S;
-  pl.tokens_per_split = (tiles + S - 1) / S * kEncT;
-  return pl;
-}
 
 hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, int lat_blocks, hipStream_t st) {
   dim3 grid(p.S, B * p.H, lat_blocks);

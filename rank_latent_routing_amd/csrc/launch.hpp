@@ -2,10 +2,17 @@
 // library; the public surface is include/flare.h).
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace flare {
+
+// Tile sizes shared by the kernels and the host-side planners (plan.cpp).
+constexpr int kEncT = 128;        // encoder: tokens per LDS tile (four 32-token quarters)
+constexpr int kDecWaves = 12;     // decoder: one workgroup per compute unit, 3 waves per SIMD
+constexpr int kDecGroup = 64;     // decoder: tokens per wave per step
+constexpr int kLatBwdTile = 64;   // backward latent pass: tokens per LDS tile
 
 // Strided [B, H, L, D] view in elements, D contiguous.
 struct View {
@@ -142,6 +149,8 @@ hipError_t launch_encode_f32(const EncodeParams& p, int D, int B, hipStream_t s)
 hipError_t launch_merge(const MergeParams& p, int B, hipStream_t s);
 // Workgroups per (batch, head) of the bf16 decoder.
 int64_t plan_decode_bf16(int B, int H, int M, int64_t N, int D);
+// LDS bytes of one decoder workgroup.
+size_t decode_bf16_lds(int M, int D);
 hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams& p, int D, int B, hipStream_t s);
 int plan_bwd_splits(int B, int H, int M, int64_t N);

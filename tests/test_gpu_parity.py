@@ -38,6 +38,22 @@ def max_rel(a, b):
     return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
 
 
+def elementwise_max_rel(a, b, floor=1e-3):
+    """max |a_i - b_i| / |b_i| over the outputs with |b_i| >= floor * ||b||_inf (an elementwise
+    ratio on outputs near zero would measure their conditioning, not the kernel)."""
+    big = np.abs(b) >= floor * np.max(np.abs(b))
+    return float(np.max(np.abs(a - b)[big] / np.abs(b)[big]))
+
+
+def check_f32(got, ref, what):
+    """Normwise max-rel within the fp32 bar; the elementwise max-rel over the outputs above
+    1e-3 of the largest is reported, and held to the bound the normwise bar implies."""
+    e, ee = max_rel(got, ref), elementwise_max_rel(got, ref)
+    say(f"  {what}: max-rel (normwise) {e:.2e}, elementwise over |r| >= 1e-3 max|r|: {ee:.2e}")
+    assert e <= F32_TOL, what
+    assert ee <= F32_TOL / 1e-3, what
+
+
 def say(*a):
     print(*a, flush=True)
 
@@ -174,10 +190,11 @@ def test_fp32_path_encdec_n1k(flags):
     torch.cuda.synchronize()
     yr, zr, lr = oracle.flare_encdec(f64(x["q"]), f64(x["k"]).reshape(1, 1024, 64),
                                      f64(x["v"]).reshape(1, 1024, 64), 4, want_latents=True)
-    ez, ey = max_rel(f64(z), zr), max_rel(f64(y).reshape(1, 1024, 64), yr)
+    check_f32(f64(z), zr, "Z")
+    check_f32(f64(y).reshape(1, 1024, 64), yr, "Y")
     el = float(np.max(np.abs(f64(lse) - lr)))
-    say(f"  fp32: Z max-rel {ez:.2e}, Y max-rel {ey:.2e}, lse abs {el:.2e}")
-    assert ez <= F32_TOL and ey <= F32_TOL and el <= 1e-4
+    say(f"  lse abs {el:.2e}")
+    assert el <= 1e-4
 
 
 def test_fp32_path_ragged_and_sharp():
@@ -192,8 +209,8 @@ def test_fp32_path_ragged_and_sharp():
     ko, vo, qo = f64(hm(x["k"])), f64(hm(x["v"])), f64(x["q"])
     zr, _ = oracle.encode(qo, ko, vo)
     yr = oracle.decode(ko, qo, zr)
-    assert max_rel(f64(z), zr) <= F32_TOL
-    assert max_rel(f64(hm(y)), yr) <= F32_TOL
+    check_f32(f64(z), zr, "Z")
+    check_f32(f64(hm(y)), yr, "Y")
 
 
 @pytest.mark.parametrize("R,Cin,Cout,nproj,head_dim", [

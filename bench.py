@@ -5,16 +5,26 @@ N=1,048,576 tokens, M=256 latents per head (K, V and Q ~ N(0, 1), seed 0).
 One step = flare_encode (split-token kernel + logsumexp merge) followed by
 flare_decode, on inputs already resident in HBM.  Prints ONE JSON line.
 
-Also measured in the same run (reported under "extra"): the whole FLARE++
-mixer at the same sizes (C = 256: four input projections, query synthesis,
-encode, decode, output projection) via flare_mix, and the oracle on a bounded
-sample on the host cores ("cpu_baseline").
+The roofline object also carries the shader clock measured live under the
+dominant kernel (a one-wave sampler on a second stream), the matrix-core
+fraction against the peak scaled to that clock, and the exponential unit's
+share of its rate at that clock.
+
+Also measured in the same run (reported under "extra"): the same workload
+with sharp scores (Q x 40, which sends every split to the exact-softmax
+rerun), FLARE++ attention, the backward pair, the whole FLARE++ mixer at the
+same sizes (C = 256: four input projections, query synthesis, encode, decode,
+output projection) via flare_mix and its variants, the smaller FLARE++
+workloads, a sweep over the token count, and the oracle on a bounded sample
+on the host cores ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
        python bench.py --copy-calibration   (plain device copy, for PMC scaling)
        python bench.py --write-traffic FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
            (host only: turns rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of
             the bench kernels and of the copy into profiles/traffic_<kernel>.json)
+       python bench.py --summarize NAME DIR [DIR ...]
+           (host only: writes a profiles/*.md summary from rocprofv3 output)
 """
 import argparse
 import hashlib
@@ -27,6 +37,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_CLOCK_GHZ = 2.4             # engine clock the published peaks assume
+# v_exp_f32 retires one wave64 instruction per 8 cycles per SIMD (8.3 measured
+# at 4 waves per SIMD, profiles/issue_rates.gfx950.md): 8 exponentials per
+# cycle per SIMD, 1024 SIMDs.
+EXP_PER_CYCLE = 8 * 1024
+REALTIME_HZ = 1e8                # the 100 MHz real-time counter of gfx950
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E (published)
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -46,7 +62,7 @@ def parse():
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     ap.add_argument("--summarize", nargs="+", metavar=("NAME", "INPUT"),
                     help="host only: write profiles/<NAME>.md from rocprofv3 output (NAME: units, "
-                         "units_gemm, issue_rates TIMING.md PMC_DIRS...)")
+                         "units_gemm, units_bwd, clock, stats, issue_rates TIMING.md PMC_DIRS...)")
     return ap.parse_args()
 
 
@@ -62,6 +78,12 @@ def summarize(name, inputs):
         profiling.write_units_gemm(os.path.join(PROFILES, "units_gemm.mix_n1m.md"), inputs, PROFILES)
     elif name == "issue_rates":
         profiling.write_issue_rates(os.path.join(PROFILES, "issue_rates.gfx950.md"), inputs[1:], inputs[0])
+    elif name == "stats":
+        profiling.write_stats(os.path.join(PROFILES, "kernel_stats.encdec_n1m.md"), inputs[0])
+    elif name == "clock":
+        profiling.write_clock(os.path.join(PROFILES, "clock.encdec_n1m.md"), inputs)
+    elif name == "units_bwd":
+        profiling.write_units_bwd(os.path.join(PROFILES, "units_bwd.encdec_n1m.md"), inputs)
     else:
         raise SystemExit(f"unknown summary {name}")
 
@@ -75,6 +97,42 @@ KERNEL_SOURCES = {
     "decode_bf16_kernel": ["decode.hip", "common.hpp", "launch.hpp", "api.cpp"],
 }
 COPY_BYTES = 1 << 30  # bytes read (and written) per launch of the calibration copy
+
+
+class ClockSampler:
+    """The shader clock while a kernel runs: a one-wave sampler kernel (the
+    probes library's clock_sample) spins on a second stream for WINDOW_MS of
+    real time, reading the shader clock and the real-time counters, while the
+    kernel is launched back to back on the main stream for about twice that
+    long.  The sampler starts first on an idle GPU, so its window lies inside
+    the kernel launches; it holds one wave slot of one compute unit."""
+    WINDOW_MS = 2.0
+
+    def __init__(self, torch):
+        import ctypes
+        from rank_latent_routing_amd.probes import run_probes
+        if not os.path.exists(run_probes.LIB):
+            raise RuntimeError(f"{run_probes.LIB} missing: run __graft_entry__.build()")
+        self.torch = torch
+        self.lib = ctypes.CDLL(run_probes.LIB)
+        self.lib.clock_sample.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_void_p]
+        self.lib.clock_sample.restype = ctypes.c_int
+        self.out = torch.zeros(4, dtype=torch.int64, device="cuda:0")
+        self.side = torch.cuda.Stream()
+
+    def under(self, launch, ms_per_launch):
+        torch = self.torch
+        torch.cuda.synchronize()
+        n = int(2 * self.WINDOW_MS / max(ms_per_launch, 1e-3)) + 2
+        rc = self.lib.clock_sample(self.out.data_ptr(), int(self.WINDOW_MS * 1e-3 * REALTIME_HZ),
+                                   self.side.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"clock_sample failed ({rc})")
+        for _ in range(n):
+            launch()
+        torch.cuda.synchronize()
+        r0, r1, c0, c1 = self.out.tolist()
+        return (c1 - c0) / ((r1 - r0) / REALTIME_HZ) / 1e9
 
 
 def kernel_source_sha(kernel):
@@ -237,7 +295,31 @@ def main():
                 "hbm_algorithmic_GBs": round(kwork.bytes / (kms / 1e3) / 1e9, 1),
                 "hbm_frac": round(kwork.bytes / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    # The shader clock under each kernel (the chip runs below its 2.4 GHz
+    # peak clock under this load), and the roofline again at that clock: the
+    # matrix-core fraction against the peak scaled to the clock, and the
+    # share of the exponential unit's rate at that clock.
+    # The clock that prices the roofline is the one under the timed loop's
+    # own pattern (encode and decode alternating); each kernel launched alone
+    # back to back draws a different power, so its clock is reported apart.
+    sampler = ClockSampler(torch)
+    step_clk = sampler.under(step, ms_step)
+    enc_clk = sampler.under(lambda: rl.flare_encode(q, k, v, z=z, workspace=ws, stream=stream), enc_ms)
+    dec_clk = sampler.under(lambda: rl.flare_decode(k, q, z, y=y, stream=stream), dec_ms)
+    kclk = step_clk
+    roofline["clock_GHz"] = round(kclk, 3)
+    roofline["frac_at_clock"] = round(achieved / (MFMA_BF16_PEAK_TFLOPS * kclk / PEAK_CLOCK_GHZ), 4)
+    roofline["exp_pipe_frac"] = round(kwork.exps / (kms / 1e3) / (EXP_PER_CYCLE * kclk * 1e9), 4)
+
     extra = {"encode_ms": round(enc_ms, 4), "decode_ms": round(dec_ms, 4),
+             "clock_GHz": {"step": round(step_clk, 3), "encode_alone": round(enc_clk, 3),
+                           "decode_alone": round(dec_clk, 3)},
+             "encode_frac_at_clock": round(enc.flops / (enc_ms / 1e3) / 1e12 /
+                                           (MFMA_BF16_PEAK_TFLOPS * step_clk / PEAK_CLOCK_GHZ), 4),
+             "encode_exp_pipe_frac": round(enc.exps / (enc_ms / 1e3) / (EXP_PER_CYCLE * step_clk * 1e9), 4),
+             "decode_frac_at_clock": round(dec.flops / (dec_ms / 1e3) / 1e12 /
+                                           (MFMA_BF16_PEAK_TFLOPS * step_clk / PEAK_CLOCK_GHZ), 4),
+             "decode_exp_pipe_frac": round(dec.exps / (dec_ms / 1e3) / (EXP_PER_CYCLE * step_clk * 1e9), 4),
              "encode_tflops": round(enc.flops / (enc_ms / 1e3) / 1e12, 1),
              "decode_tflops": round(dec.flops / (dec_ms / 1e3) / 1e12, 1),
              "step_tflops": round(tflops_step, 1),
@@ -261,6 +343,40 @@ def main():
     if extra["parity_rel_l2"]["Z_head0"] > 1e-2 or extra["parity_rel_l2"]["Y_head0_64_tokens"] > 1e-2:
         print("bench.py: parity check failed", extra["parity_rel_l2"], file=sys.stderr)
         sys.exit(3)
+
+    # Sharp scores: the same workload with Q x 40 (rounded to bf16 once), so
+    # that a latent's scores span hundreds of units in base 2.  The fast
+    # softmax's range check then fails in every split and token group and the
+    # exact running-maximum pass reruns them: "default" is that cost, next to
+    # FLARE_FLAG_EXACT_SOFTMAX (the exact pass alone) and the metric workload.
+    q40 = (q.float() * 40.0).to(torch.bfloat16)
+
+    def timed(f, n):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0e.record(stream)
+        for _ in range(n):
+            f()
+        t1e.record(stream)
+        torch.cuda.synchronize()
+        return t0e.elapsed_time(t1e) / n
+
+    def sharp(flags):
+        def f():
+            rl.flare_encode(q40, k, v, z=z, workspace=ws, flags=flags, stream=stream)
+            rl.flare_decode(k, q40, z, y=y, flags=flags, stream=stream)
+        return f
+    sn = max(3, args.steps // 2)
+    sharp_ms = timed(sharp(0), sn)
+    exact_ms = timed(sharp(rl.FLARE_FLAG_EXACT_SOFTMAX), sn)
+    extra["sharp_q40"] = {
+        "config": "metric workload with Q x 40 (scores of a few hundred in base 2): every split and token group "
+                  "fails the fast softmax's range check and reruns with the exact running maximum",
+        "ms": round(sharp_ms, 4), "exact_flag_ms": round(exact_ms, 4), "metric_ms": round(ms_step, 4),
+        "fallback_cost": round(sharp_ms / ms_step, 3), "over_exact": round(sharp_ms / exact_ms, 3)}
+    del q40
 
     # FLARE++ attention at the same sizes: the query synthesis Q(X) =
     # SDPA(seeds, eK, eV) over separate eK, eV ~ N(0, 1), then the encode and

@@ -170,10 +170,13 @@ def write_units(out, dirs):
             "had a VALU instruction ready (waiting on LDS, on the tile barrier, on the matrix core's result or "
             "its issue), plus the time a SIMD holds fewer waves (workgroup start-up and the tail; *engines busy* "
             "is SQ_BUSY_CYCLES / SQ_CYCLES).",
-            "- *MFMA busy* runs under the VALU issue: the matrix core works while the VALU port issues "
-            "(the co-execution column), and no dual issue happens while it is busy. The 4 products of a block "
-            "take 128 cycles, below the floor's VALU issue time, so the exponentials and the other per-score "
-            "VALU work set the pace, not the matrix core or HBM."]
+            "- *MFMA busy* overlaps the VALU issue only in part (the co-execution column), and no dual issue "
+            "happens while the matrix core is busy. A block's time answers to both: timed variants of the two "
+            "kernels (not kept) that fold the scale into bf16 Q, 16 multiplies fewer (-64 issue cycles), took "
+            "28 (encode) and 36 (decode) cycles less per block; variants that instead feed Q x scale as a bf16 "
+            "high and low pair, no multiplies but 2 more products (+64 matrix-core cycles), took 70 and 38 "
+            "cycles more.  HBM is not the limit (the traffic files: 1.03-1.04 x the algorithmic bytes at under "
+            "30 % of the peak rate)."]
     open(out, "w").write("\n".join(text) + "\n")
     return b
 
@@ -331,3 +334,170 @@ def write_units_gemm(out, dirs, profiles_dir):
               "- The matrix cores are busy for about 40 % of SIMD cycles in the four-output launch; the kernel sits "
               "between the matrix-core and HBM bounds."]
     open(out, "w").write("\n".join(lines) + "\n")
+
+
+# ---------------------------------------------------------------- kernel time
+
+STATS_CMD = ("timeout -k 10 900 rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_bench -o run "
+             "-- python3 -u bench.py")
+STATS_NOTES = [
+    "The run is the default bench: 5 warm-up and 20 timed encode+decode steps; the FLARE++ attention extra "
+    "at the same sizes; the sharp-score extra (Q x 40: default and exact softmax); the backward leg (the "
+    "one-call pair backward, the two-call chain, the one-call form with bf16 dK and dV); the shader-clock "
+    "samples; the three mixer extras at N=1048576, C=256 with all projections; the small FLARE++ mixer "
+    "(eager and graph replays); the sequence and block FLARE++ workloads; the sweep over the token count; "
+    "and the oracle CPU sample.",
+    "",
+    "Each mixer call launches the projection GEMMs, the query synthesis (an encode) and one encode and decode "
+    "of its own sizes, so the encode/decode rows average over every use; the bench line's roofline times the "
+    "metric workload's launches alone, with HIP events on the launching stream."]
+
+
+def write_stats(out, trace_dir):
+    """profiles/kernel_stats.encdec_n1m.md from a --kernel-trace --stats run of the default bench."""
+    write_kernel_stats(out, trace_dir, "Kernel time, default bench run (metric workload: FLARE encode+decode, "
+                       "B=1, H=8, D=32, N=1048576, M=256, bf16; plus every extra)", STATS_CMD, STATS_NOTES)
+
+
+# ---------------------------------------------------------------- shader clock
+
+CLOCK_CMD = ("timeout -s KILL 120 rocprofv3 --pmc GRBM_GUI_ACTIVE --kernel-trace --kernel-include-regex "
+             "\"encode_bf16|decode_bf16|merge_kernel\" -f csv -d gpurun_out/clk_bench -o run -- python3 -u "
+             "bench.py --steps 5 --warmup 2 --no-cpu --no-mix --no-bwd --no-sweep")
+
+
+def kernel_trace(dirs, select=None):
+    """{kernel: [duration ns per dispatch]} and {(kernel, dispatch id): duration ns} from kernel traces."""
+    per, by_id = collections.defaultdict(list), {}
+    for path in _csvs(dirs, "*kernel_trace.csv"):
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"])
+            if select and not any(s in k for s in select):
+                continue
+            d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            per[k].append(d)
+            by_id[(path, k, r["Dispatch_Id"])] = d
+    return per, by_id
+
+
+def write_clock(out, dirs):
+    """profiles/clock.encdec_n1m.md: the shader clock under the bench's encode and decode kernels,
+    from GRBM_GUI_ACTIVE (summed over the XCDs) over each dispatch's traced duration."""
+    sel = ["encode_bf16", "decode_bf16", "merge_kernel"]
+    per, _ = kernel_trace(dirs, sel)
+    grbm = {k: [d["GRBM_GUI_ACTIVE"] for d in ds if "GRBM_GUI_ACTIVE" in d]
+            for k, ds in dispatch_counters(dirs, sel).items()}
+    lines = ["# Shader clock under load, bench workload (FLARE encode+decode, B=1, H=8, D=32, N=1048576, M=256, "
+             "bf16)", "", "Command (repo root, one MI355X), then `python bench.py --summarize clock "
+             "gpurun_out/clk_bench`:", "", "```", "export TMPDIR=/tmp", CLOCK_CMD, "```", "",
+             "GRBM_GUI_ACTIVE is summed over the 8 XCDs; clock = cycles / 8 / kernel duration (kernel trace of "
+             "the same run).  bench.py also samples the clock live (a one-wave sampler kernel on a second "
+             "stream reading the shader and the 100 MHz real-time counters while the kernel runs), and reports "
+             "it with the roofline.", "",
+             "| kernel | dispatches | mean duration (us) | GRBM_GUI_ACTIVE per dispatch | clock (GHz) |",
+             "|---|---|---|---|---|"]
+    for k in sorted(per):
+        if not grbm.get(k):
+            continue
+        dur = sum(per[k]) / len(per[k])
+        g = sum(grbm[k]) / len(grbm[k])
+        lines.append(f"| `{k}` | {len(per[k])} | {dur / 1e3:.1f} | {g:.4g} | {g / XCDS / dur:.3f} |")
+    lines += ["", "For a kernel of a few tens of microseconds (the merge) the counter window reaches past the "
+              "kernel, so its figure is not a clock."]
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+# ------------------------------------------------------------- backward units
+
+BWD_ARGS = "--steps 2 --warmup 1 --no-cpu --no-mix --no-sweep"
+BWD_PASSES = [
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VALU2 "
+    "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU_TRANS_F32 "
+    "SQ_LDS_BANK_CONFLICT SQ_INSTS_SALU SQ_CYCLES GRBM_GUI_ACTIVE",
+]
+BWD_CMDS = ["export TMPDIR=/tmp"] + [
+    f"timeout -s KILL 120 rocprofv3 --pmc {p} --kernel-include-regex \"tok_bwd|lat_bwd|tok_pair\" -f csv "
+    f"-d gpurun_out/bpmc{i + 1} -o run -- python3 -u bench.py {BWD_ARGS}" for i, p in enumerate(BWD_PASSES)]
+# The backward leg of `bench.py BWD_ARGS` runs three forms, 5 calls each (2 warm-up, 3 timed): the
+# one-call pair backward with fp32 dK, dV; the two-call chain; the one-call form with bf16 dK, dV.
+# Each kernel's dispatches, in order, split into the forms it runs in.
+BWD_GROUPS = [
+    ("tok_pair_kernel<32>", 0, 5, "token pass, both roles (`tok_pair_kernel<32>`, one-call backward, fp32 dK, dV)"),
+    ("tok_pair_kernel<32>", 5, 10, "the same with bf16 dK, dV"),
+    ("lat_bwd_kernel<32, false, 8>", 0, 5,
+     "latent pass, decoder role, computing delta from Y (`lat_bwd_kernel<32, false, 8>`, one-call)"),
+    ("lat_bwd_kernel<32, false, 8>", 5, 10, "latent pass, decoder role (`lat_bwd_kernel<32, false, 8>`, two-call chain)"),
+    ("lat_bwd_kernel<32, false, 8>", 10, 15, "the one-call form's latent pass again, in the bf16 dK, dV calls"),
+    ("lat_bwd_kernel<32, true, 8>", 0, 15, "latent pass, encoder role (`lat_bwd_kernel<32, true, 8>`, all forms)"),
+    ("tok_bwd_kernel<32, false>", 0, 5, "token pass, decoder role (`tok_bwd_kernel<32, false>`, two-call chain)"),
+    ("tok_bwd_kernel<32, true>", 0, 5, "token pass, encoder role (`tok_bwd_kernel<32, true>`, two-call chain)"),
+]
+
+
+def _ordered_dispatches(dirs, select):
+    """{kernel: {csv path: [counters per dispatch, in dispatch order]}}."""
+    per = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    for path in _csvs(dirs, "*counter_collection.csv"):
+        for row in csv.DictReader(open(path)):
+            k = short_name(row["Kernel_Name"])
+            if select and not any(s in k for s in select):
+                continue
+            per[k][(path, int(row["Dispatch_Id"]))][row["Counter_Name"]] += float(row["Counter_Value"])
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for k, d in per.items():
+        for (path, _), v in sorted(d.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+            out[k][path].append(v)
+    return out
+
+
+def write_units_bwd(out, dirs):
+    """profiles/units_bwd.encdec_n1m.md: execution-unit counters of the backward kernels."""
+    blocks = 8 * (1 << 20) * 256 // (32 * 32)
+    od = _ordered_dispatches(dirs, ["tok_bwd", "lat_bwd", "tok_pair"])
+    rows = ["| kernel | dispatches | cycles | SIMD-cycles per block | MFMA per block | MFMA busy | co-exec "
+            "| VALU per block | VALU issue per block | transcendental per block | LDS instructions per block "
+            "| LDS bank conflicts | waiting on operands | waiting (any) |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    nan = float("nan")
+    for kernel, lo, hi, label in BWD_GROUPS:
+        if kernel not in od:
+            continue
+        acc = collections.defaultdict(list)
+        n = 0
+        for path, ds in od[kernel].items():
+            part = ds[lo:hi]
+            n = max(n, len(part))
+            for d in part:
+                for c, v in d.items():
+                    acc[c].append(v)
+        if not acc:
+            continue
+        c = {k: sum(v) / len(v) for k, v in acc.items()}
+        cyc = c.get("GRBM_GUI_ACTIVE", nan) / XCDS
+        simd = cyc * SIMDS / blocks
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", nan) / (cyc * SIMDS)
+        coexec = c.get("SQ_VALU_MFMA_COEXEC_CYCLES", nan) / c.get("SQ_VALU_MFMA_BUSY_CYCLES", nan)
+        issue = 4.0 * (c.get("SQ_ACTIVE_INST_VALU", nan) - c.get("SQ_ACTIVE_INST_VALU2", 0.0)) / blocks
+        wait = c.get("SQ_WAIT_INST_ANY", nan) / c.get("SQ_WAVE_CYCLES", nan)
+        wait_any = c.get("SQ_WAIT_ANY", nan) / c.get("SQ_WAVE_CYCLES", nan)
+        rows.append(f"| {label} | {n} | {cyc:.4g} | {simd:.0f} | {c.get('SQ_INSTS_MFMA', nan) / blocks:.2f} "
+                    f"| **{100 * busy:.1f}%** | {100 * coexec:.0f}% | {c.get('SQ_INSTS_VALU', nan) / blocks:.1f} "
+                    f"| {issue:.0f} | {c.get('SQ_INSTS_VALU_TRANS_F32', nan) / blocks:.1f} "
+                    f"| {c.get('SQ_INSTS_LDS', nan) / blocks:.1f} | {c.get('SQ_LDS_BANK_CONFLICT', nan):.0f} "
+                    f"| {100 * wait:.0f}% | {100 * wait_any:.0f}% |")
+    text = ["# Execution units, backward of the bench workload (FLARE encode+decode, B=1, H=8, D=32, N=1048576, "
+            "M=256)", "", "Commands (repo root, one MI355X; two counter passes, each a run of its own), then "
+            "`python bench.py --summarize units_bwd gpurun_out/bpmc1 gpurun_out/bpmc2`:", "", "```"] + BWD_CMDS + [
+            "```", "",
+            "The bench's backward leg runs the one-call pair backward (`flare_encdec_backward`) 5 times, then "
+            "the two-call chain (`flare_decode_backward` + `flare_encode_backward`) 5 times, then the one-call "
+            "form 5 times with bf16 dK and dV.  Values are means per dispatch over the dispatches of each group "
+            f"and both passes.  A block is 32 tokens x 32 latents of one head: {blocks} blocks per call.  Cycles "
+            "are GRBM_GUI_ACTIVE / 8 XCDs; SIMD-cycles that times 1024 SIMDs; MFMA busy is "
+            "SQ_VALU_MFMA_BUSY_CYCLES over SIMD-cycles; co-exec is the share of those MFMA-busy cycles in which "
+            "VALU instructions also executed; VALU issue is 4 x (SQ_ACTIVE_INST_VALU - SQ_ACTIVE_INST_VALU2) "
+            "cycles; waiting on operands is SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES (wave-cycles spent waiting for "
+            "an instruction's operands: LDS, memory, or the matrix core's result); waiting (any) is SQ_WAIT_ANY "
+            "over SQ_WAVE_CYCLES (also counting waits at barriers and on counters).", ""] + rows
+    open(out, "w").write("\n".join(text) + "\n")

@@ -62,7 +62,8 @@ def parse():
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     ap.add_argument("--summarize", nargs="+", metavar=("NAME", "INPUT"),
                     help="host only: write profiles/<NAME>.md from rocprofv3 output (NAME: units, "
-                         "units_gemm, units_bwd, clock, stats, issue_rates TIMING.md PMC_DIRS...)")
+                         "units_gemm, units_bwd, clock, stats, xreuse TIMING.md PMC_DIR, issue_rates TIMING.md "
+                         "PMC_DIRS...)")
     return ap.parse_args()
 
 
@@ -84,6 +85,8 @@ def summarize(name, inputs):
         profiling.write_clock(os.path.join(PROFILES, "clock.encdec_n1m.md"), inputs)
     elif name == "units_bwd":
         profiling.write_units_bwd(os.path.join(PROFILES, "units_bwd.encdec_n1m.md"), inputs)
+    elif name == "xreuse":
+        profiling.write_xreuse(os.path.join(PROFILES, "xreuse.block_c5.md"), inputs[0], inputs[1], PROFILES)
     else:
         raise SystemExit(f"unknown summary {name}")
 

@@ -1,7 +1,8 @@
 """Issue-rate probes of the gfx950 instructions the mixer's inner loops use.
 
-Builds ``issue.hip`` (and ``clock.hip``, the shader-clock sampler bench.py
-uses) into ``_build/libflare_probes.so`` (also built by
+Builds ``issue.hip`` (with ``clock.hip``, the shader-clock sampler bench.py
+uses, and ``xreuse.hip``, the X-reuse probe of run_xreuse.py) into
+``_build/libflare_probes.so`` (also built by
 ``__graft_entry__.build()``) and runs each instruction mix on one workgroup
 per compute unit with 1, 2 or 4 waves per SIMD.  Prints a markdown table of
 SIMD cycles per loop iteration (median over waves, from the shader clock each
@@ -49,7 +50,8 @@ def build(verbose=False):
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-x", "hip", os.path.join(HERE, "issue.hip"), os.path.join(HERE, "clock.hip"), "-o", LIB + ".tmp"]
+           "-x", "hip", os.path.join(HERE, "issue.hip"), os.path.join(HERE, "clock.hip"),
+           os.path.join(HERE, "xreuse.hip"), "-o", LIB + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("building the probes failed:\n" + r.stderr)

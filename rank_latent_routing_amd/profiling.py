@@ -70,7 +70,7 @@ def _csvs(dirs, pattern):
 
 def short_name(kernel):
     """'void flare::encode_bf16_kernel<32, 8>(flare::EncodeParams)' -> 'encode_bf16_kernel<32, 8>'."""
-    k = kernel.split("(")[0]
+    k = kernel.replace("(anonymous namespace)::", "").split("(")[0]
     for pre in ("void ", "flare::"):
         k = k.replace(pre, "")
     return k.strip()
@@ -500,4 +500,50 @@ def write_units_bwd(out, dirs):
             "cycles; waiting on operands is SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES (wave-cycles spent waiting for "
             "an instruction's operands: LDS, memory, or the matrix core's result); waiting (any) is SQ_WAIT_ANY "
             "over SQ_WAVE_CYCLES (also counting waits at barriers and on counters).", ""] + rows
+    open(out, "w").write("\n".join(text) + "\n")
+
+
+# ------------------------------------------------------------ X reuse probe
+
+XREUSE_TIMING_CMD = "timeout -k 10 120 python3 -u rank_latent_routing_amd/probes/run_xreuse.py > gpurun_out/xreuse.md"
+XREUSE_PMC_CMD = ("timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex xreuse -f csv -d "
+                  "gpurun_out/xreuse_pmc -o run -- python3 -u rank_latent_routing_amd/probes/run_xreuse.py --reps 3")
+
+
+def write_xreuse(out, timing_md, pmc_dir, profiles_dir):
+    """profiles/xreuse.block_c5.md: bytes fetched past L2 and time of the X-reuse probe per dispatch order."""
+    from rank_latent_routing_amd.probes import run_xreuse as xr
+    fr, _ = _copy_factors(profiles_dir)
+    od = _ordered_dispatches([pmc_dir], ["xreuse"])
+    per_order = collections.defaultdict(list)
+    for k, d in od.items():
+        order = int(k.split("<")[1].split(",")[0])
+        for path, ds in d.items():
+            per_order[order].append(ds)
+    xbytes = xr.B * xr.N * xr.C * 2
+    rows = ["| order | heads | dispatches | fetched past L2 per launch (GB) | per head, over X's bytes |",
+            "|---|---|---|---|---|"]
+    for label, heads, order in xr.RUNS:
+        runs = per_order.get(order, [])
+        vals = []
+        for ds in runs:
+            # order 0 serves two runs: first the one-head read, then the head-major one
+            n = len(ds) // 2 if order == 0 else len(ds)
+            part = ds[:n] if (order == 0 and heads == 1) else (ds[n:] if order == 0 else ds)
+            vals += [c["FETCH_SIZE"] * 1024 * fr for c in part]
+        if not vals:
+            continue
+        gb = sum(vals) / len(vals)
+        rows.append(f"| {label} | {heads} | {len(vals)} | {gb / 1e9:.3f} | {gb / heads / xbytes:.2f} |")
+    timing = open(timing_md).read().strip().splitlines()
+    text = ["# X reuse across heads, FLARE++ block workload's projection input (X [B*N, C] bf16, B=4, N=262144, "
+            "C=256, H=8)", "",
+            "Would workgroups that each project one head's share of a token window (a fused projection-into-"
+            "attention kernel reads all C input features of its tokens for every head) find X in L2?  The probe "
+            "(`rank_latent_routing_amd/probes/xreuse.hip`) reads each 128-row block of X once per head in three "
+            "dispatch orders.", "",
+            "Commands (repo root, one MI355X), then `python bench.py --summarize xreuse gpurun_out/xreuse.md "
+            "gpurun_out/xreuse_pmc`:", "", "```", "export TMPDIR=/tmp", XREUSE_TIMING_CMD, XREUSE_PMC_CMD, "```",
+            "", "Timing:", ""] + timing + ["", "Bytes fetched past L2 (FETCH_SIZE, scaled by the copy calibration of "
+            f"`traffic.encdec_n1m.md`, x{fr:.4f}):", ""] + rows
     open(out, "w").write("\n".join(text) + "\n")

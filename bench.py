@@ -103,12 +103,14 @@ COPY_BYTES = 1 << 30  # bytes read (and written) per launch of the calibration c
 
 
 class ClockSampler:
-    """The shader clock while a kernel runs: a one-wave sampler kernel (the
-    probes library's clock_sample) spins on a second stream for WINDOW_MS of
-    real time, reading the shader clock and the real-time counters, while the
-    kernel is launched back to back on the main stream for about twice that
-    long.  The sampler starts first on an idle GPU, so its window lies inside
-    the kernel launches; it holds one wave slot of one compute unit."""
+    """The shader clock while a kernel runs: a sampler kernel (the probes
+    library's clock_sample, one wave on each XCD) spins on a second stream for
+    WINDOW_MS of real time, reading the shader clock and the real-time
+    counters, while the kernel is launched back to back on the main stream for
+    about twice that long.  The sampler starts first on an idle GPU, so its
+    window lies inside the kernel launches; it holds one wave slot of one
+    compute unit per XCD.  under() returns the mean clock over the XCDs and
+    the spread (min, max)."""
     WINDOW_MS = 2.0
 
     def __init__(self, torch):
@@ -120,7 +122,7 @@ class ClockSampler:
         self.lib = ctypes.CDLL(run_probes.LIB)
         self.lib.clock_sample.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_void_p]
         self.lib.clock_sample.restype = ctypes.c_int
-        self.out = torch.zeros(4, dtype=torch.int64, device="cuda:0")
+        self.out = torch.zeros(32, dtype=torch.int64, device="cuda:0")
         self.side = torch.cuda.Stream()
 
     def under(self, launch, ms_per_launch):
@@ -134,8 +136,9 @@ class ClockSampler:
         for _ in range(n):
             launch()
         torch.cuda.synchronize()
-        r0, r1, c0, c1 = self.out.tolist()
-        return (c1 - c0) / ((r1 - r0) / REALTIME_HZ) / 1e9
+        v = self.out.tolist()
+        ghz = [(v[4 * i + 3] - v[4 * i + 2]) / ((v[4 * i + 1] - v[4 * i]) / REALTIME_HZ) / 1e9 for i in range(8)]
+        return sum(ghz) / len(ghz), (min(ghz), max(ghz))
 
 
 def kernel_source_sha(kernel):
@@ -306,9 +309,9 @@ def main():
     # own pattern (encode and decode alternating); each kernel launched alone
     # back to back draws a different power, so its clock is reported apart.
     sampler = ClockSampler(torch)
-    step_clk = sampler.under(step, ms_step)
-    enc_clk = sampler.under(lambda: rl.flare_encode(q, k, v, z=z, workspace=ws, stream=stream), enc_ms)
-    dec_clk = sampler.under(lambda: rl.flare_decode(k, q, z, y=y, stream=stream), dec_ms)
+    step_clk, step_spread = sampler.under(step, ms_step)
+    enc_clk, enc_spread = sampler.under(lambda: rl.flare_encode(q, k, v, z=z, workspace=ws, stream=stream), enc_ms)
+    dec_clk, dec_spread = sampler.under(lambda: rl.flare_decode(k, q, z, y=y, stream=stream), dec_ms)
     kclk = step_clk
     roofline["clock_GHz"] = round(kclk, 3)
     roofline["frac_at_clock"] = round(achieved / (MFMA_BF16_PEAK_TFLOPS * kclk / PEAK_CLOCK_GHZ), 4)
@@ -316,7 +319,10 @@ def main():
 
     extra = {"encode_ms": round(enc_ms, 4), "decode_ms": round(dec_ms, 4),
              "clock_GHz": {"step": round(step_clk, 3), "encode_alone": round(enc_clk, 3),
-                           "decode_alone": round(dec_clk, 3)},
+                           "decode_alone": round(dec_clk, 3),
+                           "xcd_min_max": {"step": [round(a, 3) for a in step_spread],
+                                           "encode_alone": [round(a, 3) for a in enc_spread],
+                                           "decode_alone": [round(a, 3) for a in dec_spread]}},
              "encode_frac_at_clock": round(enc.flops / (enc_ms / 1e3) / 1e12 /
                                            (MFMA_BF16_PEAK_TFLOPS * step_clk / PEAK_CLOCK_GHZ), 4),
              "encode_exp_pipe_frac": round(enc.exps / (enc_ms / 1e3) / (EXP_PER_CYCLE * step_clk * 1e9), 4),

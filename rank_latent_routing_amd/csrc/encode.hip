@@ -42,6 +42,19 @@ namespace flare {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
+// LDS stages of K/V tiles: four (three tiles in flight) for 8-wave
+// workgroups; two (one in flight) for the narrower workgroups of small M,
+// whose splits are short and which need several workgroups per CU to hide
+// the loads (four stages would hold them at one or two waves per SIMD).
+constexpr int enc_stages(int nw) { return nw >= 8 ? 4 : 2; }
+// Waves per SIMD the LDS of a workgroup allows (at most 4, the 128-register
+// budget): the launch bound asks the compiler for exactly that.
+constexpr int enc_waves_per_simd(int d, int nw) {
+  const int lds = 2 * enc_stages(nw) * kEncT * d * 2 + 4;
+  const int per_simd = (160 * 1024 / lds) * nw / 4;
+  return per_simd < 1 ? 1 : per_simd > 4 ? 4 : per_simd;
+}
+
 template <int D, int NW>
 struct EncodeKernel {
   static constexpr int NT = 64 * NW;
@@ -257,62 +270,89 @@ __device__ __forceinline__ void encode_pass(
       run(std::integral_constant<bool, true>());
   };
 
-  // Tile it lives in stage it % 4.  Step it: start the DMA of tile it + 3,
-  // compute tile it, then wait for this wave's DMA of tile it + 1 (the loads
-  // of tiles it + 2 and it + 3 may still be outstanding) and meet at the
-  // barrier, after which every wave's part of tile it + 1 is in LDS and every
-  // wave is done reading tile it (whose stage the next step refills).
-  auto step = [&](auto stage_tag, int it) {
-    constexpr int S = decltype(stage_tag)::value;
-    if (it + 3 < ntiles) issue(std::integral_constant<int, (S + 3) % 4>(), it + 3);
-    compute_tile(stage_tag, it);
-    const int later = (it + 3 < ntiles) + (it + 2 < ntiles);  // tiles issued after it + 1
-    if (later == 2)
+  constexpr int ST = enc_stages(NW);
+  if constexpr (ST == 4) {
+    // Tile it lives in stage it % 4.  Step it: start the DMA of tile it + 3,
+    // compute tile it, then wait for this wave's DMA of tile it + 1 (the
+    // loads of tiles it + 2 and it + 3 may still be outstanding) and meet at
+    // the barrier, after which every wave's part of tile it + 1 is in LDS and
+    // every wave is done reading tile it (whose stage the next step refills).
+    auto step = [&](auto stage_tag, int it) {
+      constexpr int S = decltype(stage_tag)::value;
+      if (it + 3 < ntiles) issue(std::integral_constant<int, (S + 3) % 4>(), it + 3);
+      compute_tile(stage_tag, it);
+      const int later = (it + 3 < ntiles) + (it + 2 < ntiles);  // tiles issued after it + 1
+      if (later == 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * KC::OPS_PER_WAVE));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KC::OPS_PER_WAVE));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      barrier_keep_loads();
+    };
+
+    issue(std::integral_constant<int, 0>(), 0);
+    if (ntiles > 1) issue(std::integral_constant<int, 1>(), 1);
+    if (ntiles > 2) issue(std::integral_constant<int, 2>(), 2);
+    if (ntiles > 2)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * KC::OPS_PER_WAVE));
-    else if (later == 1)
+    else if (ntiles > 1)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KC::OPS_PER_WAVE));
     else
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     barrier_keep_loads();
-  };
+    for (int it = 0; it < ntiles; it += 4) {
+      step(std::integral_constant<int, 0>(), it);
+      if (it + 1 >= ntiles) break;
+      step(std::integral_constant<int, 1>(), it + 1);
+      if (it + 2 >= ntiles) break;
+      step(std::integral_constant<int, 2>(), it + 2);
+      if (it + 3 >= ntiles) break;
+      step(std::integral_constant<int, 3>(), it + 3);
+    }
+  } else {
+    // Two stages: tile it lives in stage it % 2.  Step it: start the DMA of
+    // tile it + 1 into the other stage (every wave finished reading it, tile
+    // it - 1, before the last barrier), compute tile it, wait for this
+    // wave's DMA and meet at the barrier.
+    auto step = [&](auto stage_tag, int it) {
+      constexpr int S = decltype(stage_tag)::value;
+      if (it + 1 < ntiles) issue(std::integral_constant<int, (S + 1) % 2>(), it + 1);
+      compute_tile(stage_tag, it);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      barrier_keep_loads();
+    };
 
-  issue(std::integral_constant<int, 0>(), 0);
-  if (ntiles > 1) issue(std::integral_constant<int, 1>(), 1);
-  if (ntiles > 2) issue(std::integral_constant<int, 2>(), 2);
-  if (ntiles > 2)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * KC::OPS_PER_WAVE));
-  else if (ntiles > 1)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KC::OPS_PER_WAVE));
-  else
+    issue(std::integral_constant<int, 0>(), 0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-  barrier_keep_loads();
-  for (int it = 0; it < ntiles; it += 4) {
-    step(std::integral_constant<int, 0>(), it);
-    if (it + 1 >= ntiles) break;
-    step(std::integral_constant<int, 1>(), it + 1);
-    if (it + 2 >= ntiles) break;
-    step(std::integral_constant<int, 2>(), it + 2);
-    if (it + 3 >= ntiles) break;
-    step(std::integral_constant<int, 3>(), it + 3);
+    barrier_keep_loads();
+    for (int it = 0; it < ntiles; it += 2) {
+      step(std::integral_constant<int, 0>(), it);
+      if (it + 1 >= ntiles) break;
+      step(std::integral_constant<int, 1>(), it + 1);
+    }
   }
 }
 
 template <int D, int NW>
 // Eight waves (256 latents) run at four waves per SIMD, two workgroups per
-// compute unit (128 VGPRs); narrower workgroups are limited by LDS.
-__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 4 : 3)) void encode_bf16_kernel(EncodeParams p) {
+// compute unit (128 VGPRs); narrower workgroups, with two LDS stages, fit
+// several per compute unit at four waves per SIMD.
+__global__ __launch_bounds__(64 * NW, enc_waves_per_simd(D, NW)) void encode_bf16_kernel(EncodeParams p) {
   using KC = EncodeKernel<D, NW>;
   constexpr int SD = KC::SD;
+  constexpr int ST = enc_stages(NW);
+  constexpr int HI = ST > 2 ? KC::TILE_ELEMS : 8;  // stages 2 and 3 (unused with two stages)
   // Separate arrays per stage, so that the compiler can tell a DMA into one
   // stage from reads of another and adds no waits between them.
   __shared__ __attribute__((aligned(16))) bf16 k0[KC::TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 k1[KC::TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 k2[KC::TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 k3[KC::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 k2[HI];
+  __shared__ __attribute__((aligned(16))) bf16 k3[HI];
   __shared__ __attribute__((aligned(16))) bf16 v0[KC::TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 v1[KC::TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 v2[KC::TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 v3[KC::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v2[HI];
+  __shared__ __attribute__((aligned(16))) bf16 v3[HI];
   __shared__ int need_exact;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31;
@@ -350,10 +390,10 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 4 : 3)) void encode_bf16_kernel
   // Zero the stages once: a lane past the end of the tokens may leave its
   // chunk unwritten, and stale data must be finite (its weight is 0).
   {
-    bf16* stages[8] = {k0, k1, k2, k3, v0, v1, v2, v3};
+    bf16* stages[8] = {k0, k1, v0, v1, k2, k3, v2, v3};
     const bf16x8 z8 = {};
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int st = 0; st < 2 * ST; ++st)
       for (int u = tid; u < KC::TILE_CHUNKS; u += KC::NT) reinterpret_cast<bf16x8*>(stages[st])[u] = z8;
   }
   f32x16 o;

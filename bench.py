@@ -605,23 +605,33 @@ def main():
             wws = torch.empty(rl.mix_workspace_size(ww.B, ww.N, ww.C, ww.H, ww.M, True, ww.has_wo),
                               dtype=torch.uint8, device=dev)
 
-            def run_w():
+            def run_w(flags=0):
                 rl.flare_mix(wm["x"], wm["w_k"], wm["w_v"], wm["qs"], ww.H, w_ek=wm["w_ek"], w_ev=wm["w_ev"],
-                             w_o=wm.get("w_o"), out=wout, workspace=wws, stream=stream)
-            for _ in range(3):
-                run_w()
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(10):
-                run_w()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            wms = e0.elapsed_time(e1) / 10
+                             w_o=wm.get("w_o"), out=wout, workspace=wws, flags=flags, stream=stream)
+
+            def time_w(flags=0):
+                for _ in range(3):
+                    run_w(flags)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(10):
+                    run_w(flags)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) / 10
+            wms = time_w()
             wk = costs.mixer(ww.B, ww.N, ww.C, ww.H, ww.M, dynamic=True, has_wo=ww.has_wo)
             extra[key] = {"config": f"{label}, B={ww.B}, N={ww.N}, C={ww.C}, H={ww.H}, D={ww.D}, M={ww.M}, bf16"
                                     + (", with W_O" if ww.has_wo else ""),
                           "ms": round(wms, 4), "tokens_per_s": ww.B * ww.N / (wms / 1e3),
                           "tflops": round(wk.flops / (wms / 1e3) / 1e12, 1)}
+            if ww.has_wo:
+                # the output projection in the decoder's epilogue instead of a
+                # second pass over Y (FLARE_MIX_FUSED_WO; the faster form is
+                # the default)
+                fms = time_w(rl.FLARE_MIX_FUSED_WO)
+                extra[key]["fused_wo_ms"] = round(fms, 4)
+                extra[key]["fused_over_two_pass"] = round(fms / wms, 3)
             del wm, wout, wws
 
     if not args.no_sweep:

@@ -61,6 +61,15 @@ typedef enum flare_dtype { FLARE_F32 = 0, FLARE_BF16 = 1 } flare_dtype;
  * fp32 rounding. */
 #define FLARE_FLAG_EXACT_SOFTMAX 1u
 
+/* flare_mix only: with W_O, apply the output projection in the decoder's
+ * epilogue ("FLARE++: Low-Rank Attention with Dynamic Attention Routing",
+ * section 3, "Full self-attention": out = [Y_1 ... Y_H] W_O) instead of
+ * writing Y and projecting it in a second pass.  Taken when D = 32 and
+ * C in {128, 256}; other shapes run the two-pass form.  Both give out within
+ * the bf16 tolerance of the same result (they sum the projection in a
+ * different order). */
+#define FLARE_MIX_FUSED_WO 2u
+
 /*
  * A [B, H, L, D] view of device memory: element (b, h, l, d) lives at
  *   data + b*stride_b + h*stride_h + l*stride_l + d     (in elements).
@@ -174,6 +183,7 @@ flare_status flare_project(const void* X, const void* const* W, void* const* Y,
  * All weights [C, C] with y = x W.  dtype must be FLARE_BF16; C = H*D with
  * D in {16, 32} and C in {32, 64, 128, 256} (FLARE_E_UNSUPPORTED otherwise);
  * X and out 16-byte aligned; Q_or_seeds [H, M, D] bf16, contiguous.
+ * flags: FLARE_FLAG_EXACT_SOFTMAX, FLARE_MIX_FUSED_WO.
  * Requires a 256-byte aligned workspace of workspace_bytes >=
  * flare_mix_workspace_size(B, N, C, H, M, W_eK != NULL, W_O != NULL).
  */

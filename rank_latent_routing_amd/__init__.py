@@ -8,7 +8,7 @@ and bf16 matrix-core projections.  This package holds the ctypes binding
 generators and the algorithmic cost model used for roofline accounting.
 """
 from .binding import (  # noqa: F401
-    FLARE_ACCUMULATE_DK, FLARE_ACCUMULATE_DQ, FLARE_BF16, FLARE_F32, FLARE_FLAG_EXACT_SOFTMAX,
+    FLARE_ACCUMULATE_DK, FLARE_ACCUMULATE_DQ, FLARE_BF16, FLARE_F32, FLARE_FLAG_EXACT_SOFTMAX, FLARE_MIX_FUSED_WO,
     FLARE_SUM_DQ_OVER_BATCH,
     FlareError, describe, encode_workspace_size, flare_decode, flare_decode_backward, flare_encdec_backward,
     flare_encode,

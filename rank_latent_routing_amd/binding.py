@@ -17,7 +17,7 @@ import torch
 from .cabi import (EXPORTS, FLARE_ACCUMULATE_DK, FLARE_ACCUMULATE_DQ,  # noqa: F401
                    FLARE_BF16, FLARE_E_HIP, FLARE_E_INVALID, FLARE_E_SCRATCH,
                    FLARE_E_UNSUPPORTED, FLARE_E_WORKSPACE, FLARE_F32,
-                   FLARE_FLAG_EXACT_SOFTMAX, FLARE_OK, FLARE_SUM_DQ_OVER_BATCH,
+                   FLARE_FLAG_EXACT_SOFTMAX, FLARE_MIX_FUSED_WO, FLARE_OK, FLARE_SUM_DQ_OVER_BATCH,
                    LIB_PATH, FlareTensor)
 from . import cabi as _cabi
 

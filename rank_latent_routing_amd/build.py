@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libflare.so")
-SOURCES = ["api.cpp", "plan.cpp", "encode.hip", "decode.hip", "gemm.hip", "bwd.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "encode.hip", "decode.hip", "decode_wo.hip", "gemm.hip", "bwd.hip", "noalloc.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp", "launch_stub.cpp"]
 HOST_LIB = os.path.join(OUT_DIR, "libflare_host.so")
 HOST_SAN_LIB = os.path.join(OUT_DIR, "libflare_host_san.so")

@@ -24,6 +24,7 @@ FLARE_E_SCRATCH = -5
 FLARE_F32 = 0
 FLARE_BF16 = 1
 FLARE_FLAG_EXACT_SOFTMAX = 1
+FLARE_MIX_FUSED_WO = 2
 
 FLARE_ACCUMULATE_DQ = 1
 FLARE_ACCUMULATE_DK = 2

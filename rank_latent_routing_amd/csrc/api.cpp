@@ -357,10 +357,11 @@ flare_status flare_project(const void* X, const void* const* W, void* const* Y, 
 
 // Workspace of flare_mix, in order: K, V (, eK, eV) head-major bf16;
 // Q(X) fp32 (dynamic); Z fp32; Y bf16 (with W_O); swizzled input weights;
-// swizzled W_O; encoder split partials.
+// swizzled W_O; encoder split partials; with W_O, the fused output
+// projection's latent operands and W_O^T.
 namespace {
 struct MixLayout {
-  size_t kv, qx, z, y, wsw, wosw, enc, total;
+  size_t kv, qx, z, y, wsw, wosw, enc, wof, total;
 };
 static MixLayout mix_layout(int B, int64_t N, int C, int H, int M, int dynamic, int has_wo) {
   MixLayout L;
@@ -383,6 +384,10 @@ static MixLayout mix_layout(int B, int64_t N, int C, int H, int M, int dynamic, 
   off += has_wo ? proj_ws(C, C, 1) : 0;
   L.enc = off;
   off += encode_ws(B, H, M, N, D, 0);
+  // the fused output projection's prepared operands (reserved whenever W_O
+  // is given, so the size does not depend on the flags)
+  L.wof = off;
+  off += has_wo ? align_up(decode_wo_scratch(B, H, M)) : 0;
   L.total = off;
   return L;
 }
@@ -408,7 +413,7 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V, const vo
   if (!X || !W_K || !W_V || !Q_or_seeds || !out) return FLARE_E_INVALID;
   if ((W_eK == nullptr) != (W_eV == nullptr)) return FLARE_E_INVALID;
   if (reinterpret_cast<uintptr_t>(X) % 16 || reinterpret_cast<uintptr_t>(out) % 16) return FLARE_E_INVALID;
-  if (!scale_ok(scale) || (flags & ~FLARE_FLAG_EXACT_SOFTMAX)) return FLARE_E_INVALID;
+  if (!scale_ok(scale) || (flags & ~(FLARE_FLAG_EXACT_SOFTMAX | FLARE_MIX_FUSED_WO))) return FLARE_E_INVALID;
   const int dynamic = W_eK != nullptr, has_wo = W_O != nullptr;
   const MixLayout L = mix_layout(B, N, C, H, M, dynamic, has_wo);
   if (!workspace || workspace_bytes < L.total || reinterpret_cast<uintptr_t>(workspace) % 256)
@@ -472,6 +477,23 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V, const vo
   z.sb = lat_sb;
   z.sh = lat_sh;
   z.sl = lat_sl;
+  // (d, e) fused: out = [SDPA(K_h, Q_h, Z_h)]_h W_O in one pass
+  if (has_wo && (flags & FLARE_MIX_FUSED_WO) && D == 32 && (H == 4 || H == 8)) {
+    DecodeWoParams dw;
+    std::memset(&dw, 0, sizeof(dw));
+    dw.k = head_major(kp);
+    dw.q = q;
+    dw.z = z;
+    dw.lat_ops = reinterpret_cast<unsigned char*>(ws + L.wof);
+    dw.wt = dw.lat_ops + (size_t)B * H * ((M + 31) / 32) * 4096;
+    dw.out = out;
+    dw.H = H;
+    dw.M = M;
+    dw.N = N;
+    dw.c = c;
+    dw.exact = (flags & FLARE_FLAG_EXACT_SOFTMAX) ? 1 : 0;
+    return hip_status(launch_decode_wo(dw, B, W_O, st));
+  }
   // (d) Y = SDPA(K, Q, Z), heads concatenated into [B, N, C]
   void* ydst = has_wo ? (void*)(ws + L.y) : out;
   s = decode_impl(head_major(kp), q, z, ydst, 0, N * C, D, C, nullptr, B, H, M, N, D, c, flags, st);

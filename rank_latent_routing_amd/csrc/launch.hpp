@@ -121,6 +121,29 @@ struct LatBwdParams {
   float c;
 };
 
+// Decoder with the output projection in its epilogue (D = 32, C = 32 H with
+// H = 4 or 8, bf16 out [B, N, C] row-major).
+constexpr int kDecWoWaves = 12;  // one workgroup of 12 waves per compute unit, 3 per SIMD
+struct DecodeWoParams {
+  View k;                 // [B, H, N, D] bf16
+  View q, z;              // [B|1, H, M, D] latent side (fp32 or bf16)
+  unsigned char* lat_ops; // scratch: B H (M/32 rounded up) 4 KB, latent operands in LDS order
+  unsigned char* wt;      // scratch: C C 2 bytes, W_O^T in LDS order
+  void* out;              // [B, N, C] bf16
+  int H, M;
+  int64_t N;
+  float c;                // scale * log2(e)
+  int exact;
+  int buf_bytes;          // set by the launcher
+};
+// LDS bytes of one workgroup (two buffers).
+size_t decode_wo_lds(int M, int C);
+// Bytes of scratch the two prepared operands need.
+inline size_t decode_wo_scratch(int B, int H, int M) {
+  return (size_t)B * H * ((M + 31) / 32) * 4096 + (size_t)(32 * H) * (32 * H) * 2;
+}
+hipError_t launch_decode_wo(const DecodeWoParams& p, int B, const void* w_o, hipStream_t s);
+
 struct GemmParams {
   const void* x;      // [R, Cin] bf16 row-major
   const void* wt[5];  // transposed weights [Cout, Cin] bf16

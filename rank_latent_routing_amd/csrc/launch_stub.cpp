@@ -24,6 +24,8 @@ enum RangeTag {
   kGemmOut = 7,    // projection outputs (written)
   kEncK = 8,       // encoder K rows (read)
   kEncV = 9,       // encoder V rows (read)
+  kWoLat = 10,     // fused output projection: prepared latent operands (written)
+  kWoT = 11,       // fused output projection: prepared W_O^T (written)
 };
 
 struct Range {
@@ -93,6 +95,11 @@ hipError_t launch_sum_splits(const float* part, float*, int B, int H, int S, int
 hipError_t launch_swizzle_weights(const SwizzleParams& p, int n, hipStream_t) {
   for (int i = 0; i < n; ++i) add_range(p.wsw[i], (unsigned long long)p.Cin * p.Cout * 2, kSwizzled);
   return record("swizzle_weights");
+}
+hipError_t launch_decode_wo(const DecodeWoParams& p, int B, const void*, hipStream_t) {
+  add_range(p.lat_ops, (unsigned long long)B * p.H * ((p.M + 31) / 32) * 4096, kWoLat);
+  add_range(p.wt, (unsigned long long)(32 * p.H) * (32 * p.H) * 2, kWoT);
+  return record("decode_wo");
 }
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t) {
   for (int i = 0; i < p.n_proj; ++i) add_range(p.y[i], (unsigned long long)p.R * p.Cout * 2, kGemmOut);

@@ -38,8 +38,8 @@ BF16, F32 = cabi.FLARE_BF16, cabi.FLARE_F32
 FAKE = 0x7F0000000000   # fake tensor base (256-byte aligned)
 WS = 0x100000000000     # fake workspace base, far from the tensors
 OUT = FAKE + (1 << 36)  # the mixer's output
-ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SUM_PART, SWIZZLED, GEMM_OUT, ENC_K, ENC_V = range(1, 10)
-WRITTEN = (ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SWIZZLED, GEMM_OUT)
+ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SUM_PART, SWIZZLED, GEMM_OUT, ENC_K, ENC_V, WO_LAT, WO_T = range(1, 12)
+WRITTEN = (ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SWIZZLED, GEMM_OUT, WO_LAT, WO_T)
 HIP_ERRORS = (1, 2, 98, 719)  # invalid value, out of memory, invalid device function, launch failure
 
 
@@ -107,7 +107,7 @@ def project(L, R, Cin, Cout, n, head_major=0, B=1, hd=0, ws=WS, ws_bytes=None):
                            need if ws_bytes is None else ws_bytes, None)
 
 
-def mix(L, B, N, C, H, M, dynamic=True, shared=False, wo=True, ws=WS, ws_bytes=None):
+def mix(L, B, N, C, H, M, dynamic=True, shared=False, wo=True, ws=WS, ws_bytes=None, flags=0):
     need = L.flare_mix_workspace_size(B, N, C, H, M, int(dynamic), int(wo))
     p = lambda i: vp(FAKE + i * (1 << 24))
     wk, wv = p(1), p(2)
@@ -115,7 +115,7 @@ def mix(L, B, N, C, H, M, dynamic=True, shared=False, wo=True, ws=WS, ws_bytes=N
     if not dynamic:
         ek = ev = None
     return L.flare_mix(p(0), wk, wv, ek, ev, p(5), p(6) if wo else None, vp(OUT), BF16, B, N, C,
-                       H, M, 0.0, 0, vp(ws), need if ws_bytes is None else ws_bytes, None)
+                       H, M, 0.0, flags, vp(ws), need if ws_bytes is None else ws_bytes, None)
 
 
 def decode_backward(L, B, H, M, N, D, ws=WS, ws_bytes=None, **kw):
@@ -160,6 +160,7 @@ def valid_calls(B=2, H=4, M=64, N=1000, D=32):
         ("mix_dynamic", lambda L, **kw: mix(L, B, N, C, H, M, **kw)),
         ("mix_shared", lambda L, **kw: mix(L, B, N, C, H, M, shared=True, **kw)),
         ("mix_static_no_wo", lambda L, **kw: mix(L, B, N, C, H, M, dynamic=False, wo=False, **kw)),
+        ("mix_fused_wo", lambda L, **kw: mix(L, B, N, C, H, M, flags=cabi.FLARE_MIX_FUSED_WO, **kw)),
         ("decode_backward", lambda L, **kw: decode_backward(L, B, H, M, N, D, **kw)),
         ("encode_backward", lambda L, **kw: encode_backward(L, B, H, M, N, D, **kw)),
         ("encdec_backward", lambda L, **kw: encdec_backward(L, B, H, M, N, D, **kw)),
@@ -167,10 +168,12 @@ def valid_calls(B=2, H=4, M=64, N=1000, D=32):
 
 
 NEEDS_WORKSPACE = {"encode", "route_queries", "encode_f32", "project", "project_head_major", "mix_dynamic",
-                   "mix_shared", "mix_static_no_wo", "decode_backward", "encode_backward", "encdec_backward"}
+                   "mix_shared", "mix_static_no_wo", "mix_fused_wo", "decode_backward", "encode_backward",
+                   "encdec_backward"}
 LAST_LAUNCH = {"encode": "merge", "route_queries": "merge", "encode_f32": "merge", "decode": "decode_bf16",
                "decode_f32": "decode_f32", "project": "gemm_bf16", "project_head_major": "gemm_bf16",
-               "mix_dynamic": "gemm_bf16", "mix_shared": "gemm_bf16", "mix_static_no_wo": "decode_bf16"}
+               "mix_dynamic": "gemm_bf16", "mix_shared": "gemm_bf16", "mix_static_no_wo": "decode_bf16",
+               "mix_fused_wo": "decode_wo"}
 
 
 def _workspace_need(L, name, B, H, M, N, D):
@@ -184,6 +187,7 @@ def _workspace_need(L, name, B, H, M, N, D):
         "mix_dynamic": lambda: L.flare_mix_workspace_size(B, N, C, H, M, 1, 1),
         "mix_shared": lambda: L.flare_mix_workspace_size(B, N, C, H, M, 1, 1),
         "mix_static_no_wo": lambda: L.flare_mix_workspace_size(B, N, C, H, M, 0, 0),
+        "mix_fused_wo": lambda: L.flare_mix_workspace_size(B, N, C, H, M, 1, 1),
         "decode_backward": lambda: L.flare_decode_backward_workspace_size(B, H, M, N, D),
         "encode_backward": lambda: L.flare_encode_backward_workspace_size(B, H, M, N, D),
         "encdec_backward": lambda: L.flare_encdec_backward_workspace_size(B, H, M, N, D),
@@ -242,6 +246,10 @@ def check_mix_and_project_reject_bad_arguments(L):
     # workspace too small, or not 256-byte aligned
     assert L.flare_mix(p, p, p, p, p, p, n, p, 1, 1, 10, 64, 2, 8, 0.0, 0, p, 64, n) == E_WORKSPACE
     assert L.flare_mix(p, p, p, p, p, p, n, p, 1, 1, 10, 64, 2, 8, 0.0, 0, vp(WS + 16), 1 << 40, n) == E_WORKSPACE
+    # flag bits other than the exact softmax and the fused output projection
+    assert mix(L, 1, 10, 64, 2, 8, flags=4) == E_INVALID
+    assert mix(L, 1, 10, 64, 2, 8, flags=cabi.FLARE_MIX_FUSED_WO | 1) == OK
+    assert encode(L, 1, 2, 32, 100, 32, flags=cabi.FLARE_MIX_FUSED_WO) == E_INVALID  # a mixer-only flag
     warr = (vp * 1)(FAKE)
     assert L.flare_project(p, warr, warr, 1, 10, 48, 64, 0, 1, 0, p, 1 << 30, n) == E_UNSUPPORTED
     assert L.flare_project(p, warr, warr, 1, 10, 64, 64, 1, 3, 32, p, 1 << 30, n) == E_INVALID
@@ -354,7 +362,7 @@ def workspace_carving(L, B, H, M, N, D):
         rs = ranges(L)
         inside = lambda x: WS <= x[0] and x[0] + x[1] <= WS + need
         for addr, nbytes, launch, tag in rs:
-            in_ws = tag in (ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SUM_PART, SWIZZLED)
+            in_ws = tag in (ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SUM_PART, SWIZZLED, WO_LAT, WO_T)
             if name.startswith("mix"):
                 # projections and encoder inputs live in the workspace, except
                 # the output projection's result, which is the caller's

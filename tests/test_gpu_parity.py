@@ -279,6 +279,38 @@ def test_mix_block_reduced(dynamic, has_wo, qm, flags):
     check_bf16(_gpu_mix(m, w.H, flags), _oracle_mix(m, w.H), f"mix dyn={dynamic} wo={has_wo}")
 
 
+FUSED = rl.FLARE_MIX_FUSED_WO
+
+
+# (B, N, C, H, M, dynamic, q_mult, flags): the output projection in the
+# decoder's epilogue; ragged token windows (N not a multiple of 384), M not a
+# multiple of 32, C = 128 (4 heads), sharp seeds that send heads to the exact
+# fallback, and the exact softmax forced.
+FUSED_CASES = [
+    (2, 3000, 256, 8, 512, True, 1.0, FUSED),
+    (2, 3000, 256, 8, 512, True, 8.0, FUSED),
+    (1, 777, 128, 4, 200, False, 2.0, FUSED),
+    (2, 1000, 256, 8, 100, True, 30.0, FUSED),
+    (1, 500, 256, 8, 64, False, 1.0, FUSED | EXACT),
+    (3, 1, 256, 8, 32, True, 1.0, FUSED),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "B{}N{}C{}H{}M{}-dyn{}-q{}-f{}".format(*c))
+def test_mix_fused_output_projection(case):
+    B, N, C, H, M, dyn, qm, flags = case
+    w = inputs.Workload("t", "mix", B, N, H, C // H, M, "bf16", dynamic=dyn, has_wo=True)
+    m = inputs.make_mix(w, seed=N + M, q_mult=qm)
+    fused = _gpu_mix(m, H, flags)
+    check_bf16(fused, _oracle_mix(m, H), f"fused W_O mix {case}")
+    # the two-pass form computes the same Y (bf16) and sums the projection in
+    # another order
+    plain = _gpu_mix(m, H, flags & ~FUSED)
+    e = rel_l2(fused, plain)
+    say(f"  fused vs two-pass: rel-L2 {e:.2e}")
+    assert e <= 1e-2
+
+
 @pytest.mark.parametrize("qm", [1.0, 8.0])
 def test_mix_shared_projections(qm):
     # FLARE++ with shared projections (the synthesis attends over K and V):
@@ -329,14 +361,15 @@ def test_metric_workload_full_size_sampled():
         check_bf16(f64(y[0, h])[rows], yr, f"Y head {h} (4096 sampled tokens)")
 
 
-def test_block_workload_full_size_sampled():
+@pytest.mark.parametrize("flags", [0, rl.FLARE_MIX_FUSED_WO], ids=["two-pass", "fused-wo"])
+def test_block_workload_full_size_sampled(flags):
     # FLARE++ block with all projections (B=4, N=262,144, C=256, H=8, M=512)
     # at full size; the oracle computes batch element 3 at 2048 sampled output
     # tokens from oracle primitives (projections, the three SDPA calls per
     # head, the output projection).
     w = inputs.WORKLOADS["block_bf16_n256k"]
     m = inputs.make_mix(w, seed=0)
-    got = _gpu_mix(m, w.H)
+    got = _gpu_mix(m, w.H, flags)
     b = 3
     X = f64(m["x"][b])
     K, V, eK, eV = (oracle.matmul(X, f64(m[n])) for n in ("w_k", "w_v", "w_ek", "w_ev"))

@@ -165,16 +165,31 @@ def stored_traffic(kernels):
     return total
 
 
-def counter_means(path, counter):
+# Launches of each bench kernel in the timed steps of a counter run's metric
+# step loop (`--steps 3 --warmup 1`: launches 1 .. 3); the warm-up and later
+# launches of the same kernels (the clock samples, the sharp-score and
+# FLARE++ extras, the backward leg's forward pass) are left out of the
+# forward figures.
+TRAFFIC_STEP_LAUNCHES = (1, 4)
+
+
+def counter_means(path, counter, launches=None):
     """Mean over dispatches of one counter, per kernel (full demangled name),
-    from a rocprofv3 counter_collection csv (rows of one dispatch are summed)."""
+    from a rocprofv3 counter_collection csv (rows of one dispatch are summed);
+    with `launches` = (lo, hi), over dispatches lo .. hi - 1 of each kernel."""
     import csv
     import collections
     per = collections.defaultdict(lambda: collections.defaultdict(float))
     for row in csv.DictReader(open(path)):
         if row["Counter_Name"] == counter:
-            per[row["Kernel_Name"]][row["Dispatch_Id"]] += float(row["Counter_Value"])
-    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+            per[row["Kernel_Name"]][int(row["Dispatch_Id"])] += float(row["Counter_Value"])
+    out = {}
+    for k, v in per.items():
+        vals = [x for _, x in sorted(v.items())]
+        if launches is not None:
+            vals = vals[launches[0]:launches[1]] or vals
+        out[k] = sum(vals) / len(vals)
+    return out
 
 
 def library_kernel(means, kernel):
@@ -187,7 +202,8 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """HBM bytes per launch of the bench kernels from FETCH_SIZE / WRITE_SIZE
     (KiB per dispatch), each scaled by what the same counter reads for a
     plain 1 GiB device copy."""
-    fetch, write = counter_means(fetch_csv, "FETCH_SIZE"), counter_means(write_csv, "WRITE_SIZE")
+    fetch = counter_means(fetch_csv, "FETCH_SIZE", TRAFFIC_STEP_LAUNCHES)
+    write = counter_means(write_csv, "WRITE_SIZE", TRAFFIC_STEP_LAUNCHES)
     cf, cw = counter_means(copy_fetch_csv, "FETCH_SIZE"), counter_means(copy_write_csv, "WRITE_SIZE")
     copy_kernel = max(cf, key=cf.get)
     f_read = COPY_BYTES / (cf[copy_kernel] * 1024.0)
@@ -210,6 +226,9 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
             json.dump(d, fh, indent=1)
         print(f"{kernel}: {d['bytes_per_launch'] / 1e9:.3f} GB per launch "
               f"(read {d['bytes_read_per_launch'] / 1e9:.3f}, written {d['bytes_written_per_launch'] / 1e9:.3f})")
+    from rank_latent_routing_amd import profiling
+    profiling.write_traffic_md(os.path.join(PROFILES, "traffic.encdec_n1m.md"), fetch_csv, write_csv, f_read, f_write,
+                               (cf[copy_kernel], cw[copy_kernel]), TRAFFIC_STEP_LAUNCHES)
 
 
 def copy_calibration():

@@ -34,6 +34,7 @@ SIMDS = 1024  # 256 compute units x 4
 BLOCK_FLOOR_QUADS = 4 + 16 + 32 + 8 + 8
 
 BENCH_ARGS = "--steps 2 --warmup 1 --no-cpu --no-mix --no-bwd --no-sweep"
+BENCH_STEP_LAUNCHES = (1, 3)  # the timed steps of BENCH_ARGS among each kernel's launches (after 1 warm-up)
 PASSES = [
     "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
     "SQ_ACTIVE_INST_VALU2 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE",
@@ -96,10 +97,17 @@ def dispatch_counters(dirs, select=None, by_pass=False):
     return {k: list(d.values()) for k, d in per.items()}
 
 
-def counter_means(dirs, select=None):
-    """{kernel: {counter: mean over the dispatches that read it}}."""
+def counter_means(dirs, select=None, launches=None):
+    """{kernel: {counter: mean over the dispatches that read it}}; with
+    `launches` = (lo, hi), over dispatches lo .. hi - 1 of each kernel in each
+    run only."""
     out = {}
-    for k, ds in dispatch_counters(dirs, select).items():
+    if launches is not None:
+        od = _ordered_dispatches(dirs, select)
+        per = {k: [d for ds in byp.values() for d in ds[launches[0]:launches[1]]] for k, byp in od.items()}
+    else:
+        per = dispatch_counters(dirs, select)
+    for k, ds in per.items():
         acc = collections.defaultdict(list)
         for d in ds:
             for c, v in d.items():
@@ -149,14 +157,16 @@ def write_units(out, dirs):
     """profiles/units.encdec_n1m.md: the per-block cycle budget of the bench's
     encode and decode kernels."""
     blocks = 8 * (1 << 20) * 256 // (32 * 32)
-    means = counter_means(dirs, ["encode_bf16", "decode_bf16"])
+    means = counter_means(dirs, ["encode_bf16", "decode_bf16"], launches=BENCH_STEP_LAUNCHES)
     rows, b = _budget_rows(means, blocks, BLOCK_FLOOR_QUADS)
     text = ["# Cycle budget of the encode and decode kernels, bench workload (FLARE encode+decode, B=1, H=8, D=32, "
             "N=1048576, M=256, bf16)", "",
             "Commands (repo root, one MI355X; three counter passes, each a run of its own), then "
             "`python bench.py --summarize units gpurun_out/pmc/bench1 gpurun_out/pmc/bench2 gpurun_out/pmc/bench3`:",
             "", "```"] + BUDGET_CMDS + ["```", "",
-            f"Values are means over every dispatch of a kernel in the three runs.  A block is 32 tokens x 32 "
+            f"Values are means over the timed steps' launches of each kernel (launches "
+            f"{BENCH_STEP_LAUNCHES[0]} .. {BENCH_STEP_LAUNCHES[1] - 1}, after the warm-up) in the three runs.  "
+            "A block is 32 tokens x 32 "
             f"latents of one head ({blocks} per dispatch).  Cycles are SIMD cycles at the clock the kernel ran "
             "at: GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs, per block.  The counter readings are calibrated on "
             "probe kernels of known instruction mix in `issue_rates.gfx950.md`.", ""] + rows + ["",
@@ -361,6 +371,7 @@ def write_stats(out, trace_dir):
 
 # ---------------------------------------------------------------- shader clock
 
+CLOCK_STEP_LAUNCHES = (2, 7)  # the timed steps of the clock run among each kernel's launches
 CLOCK_CMD = ("timeout -s KILL 120 rocprofv3 --pmc GRBM_GUI_ACTIVE --kernel-trace --kernel-include-regex "
              "\"encode_bf16|decode_bf16|merge_kernel\" -f csv -d gpurun_out/clk_bench -o run -- python3 -u "
              "bench.py --steps 5 --warmup 2 --no-cpu --no-mix --no-bwd --no-sweep")
@@ -370,7 +381,8 @@ def kernel_trace(dirs, select=None):
     """{kernel: [duration ns per dispatch]} and {(kernel, dispatch id): duration ns} from kernel traces."""
     per, by_id = collections.defaultdict(list), {}
     for path in _csvs(dirs, "*kernel_trace.csv"):
-        for r in csv.DictReader(open(path)):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
             k = short_name(r["Kernel_Name"])
             if select and not any(s in k for s in select):
                 continue
@@ -385,8 +397,10 @@ def write_clock(out, dirs):
     from GRBM_GUI_ACTIVE (summed over the XCDs) over each dispatch's traced duration."""
     sel = ["encode_bf16", "decode_bf16", "merge_kernel"]
     per, _ = kernel_trace(dirs, sel)
-    grbm = {k: [d["GRBM_GUI_ACTIVE"] for d in ds if "GRBM_GUI_ACTIVE" in d]
-            for k, ds in dispatch_counters(dirs, sel).items()}
+    per = {k: v[CLOCK_STEP_LAUNCHES[0]:CLOCK_STEP_LAUNCHES[1]] for k, v in per.items()}
+    od = _ordered_dispatches(dirs, sel)
+    grbm = {k: [d["GRBM_GUI_ACTIVE"] for ds in byp.values() for d in ds[CLOCK_STEP_LAUNCHES[0]:CLOCK_STEP_LAUNCHES[1]]
+                if "GRBM_GUI_ACTIVE" in d] for k, byp in od.items()}
     lines = ["# Shader clock under load, bench workload (FLARE encode+decode, B=1, H=8, D=32, N=1048576, M=256, "
              "bf16)", "", "Command (repo root, one MI355X), then `python bench.py --summarize clock "
              "gpurun_out/clk_bench`:", "", "```", "export TMPDIR=/tmp", CLOCK_CMD, "```", "",
@@ -546,4 +560,105 @@ def write_xreuse(out, timing_md, pmc_dir, profiles_dir):
             "gpurun_out/xreuse_pmc`:", "", "```", "export TMPDIR=/tmp", XREUSE_TIMING_CMD, XREUSE_PMC_CMD, "```",
             "", "Timing:", ""] + timing + ["", "Bytes fetched past L2 (FETCH_SIZE, scaled by the copy calibration of "
             f"`traffic.encdec_n1m.md`, x{fr:.4f}):", ""] + rows
+    open(out, "w").write("\n".join(text) + "\n")
+
+
+# ------------------------------------------------------------- HBM traffic
+
+TRAFFIC_ARGS = "--steps 3 --warmup 1 --no-cpu --no-mix --no-sweep"
+TRAFFIC_RE = "encode_bf16|decode_bf16|merge_kernel|tok_bwd|lat_bwd|sum_splits|tok_pair"
+TRAFFIC_CMDS = [
+    "export TMPDIR=/tmp",
+    f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"{TRAFFIC_RE}\" -f csv -d "
+    f"gpurun_out/pmc_fetch -o run -- python3 -u bench.py {TRAFFIC_ARGS}",
+    f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"{TRAFFIC_RE}\" -f csv -d "
+    f"gpurun_out/pmc_write -o run -- python3 -u bench.py {TRAFFIC_ARGS}",
+    "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_copy_fetch -o run -- "
+    "python3 -u bench.py --copy-calibration",
+    "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_copy_write -o run -- "
+    "python3 -u bench.py --copy-calibration",
+    "python bench.py --write-traffic gpurun_out/pmc_fetch/run_counter_collection.csv "
+    "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc_copy_fetch/run_counter_collection.csv "
+    "gpurun_out/pmc_copy_write/run_counter_collection.csv",
+]
+
+
+def _csv_ordered(path, counter, select):
+    """{kernel: [counter value per dispatch, in dispatch order]} from one counter CSV."""
+    per = collections.defaultdict(dict)
+    for row in csv.DictReader(open(path)):
+        if row["Counter_Name"] != counter:
+            continue
+        k = short_name(row["Kernel_Name"])
+        if select and not any(s in k for s in select):
+            continue
+        i = int(row["Dispatch_Id"])
+        per[k][i] = per[k].get(i, 0.0) + float(row["Counter_Value"])
+    return {k: [v for _, v in sorted(d.items())] for k, d in per.items()}
+
+
+def write_traffic_md(out, fetch_csv, write_csv, f_read, f_write, copy_kib, step_launches):
+    """profiles/traffic.encdec_n1m.md: bytes per launch of the forward and backward kernels of the bench
+    workload against their algorithmic bytes."""
+    B, H, N, D, M = 1, 8, 1 << 20, 32, 256
+    S = min(max(1, (1024 + B * H - 1) // (B * H)), ((N + 127) // 128) // 2)  # encoder splits (plan)
+    tok = B * H * N
+    sel = TRAFFIC_RE.split("|")
+    fe, wr = _csv_ordered(fetch_csv, "FETCH_SIZE", sel), _csv_ordered(write_csv, "WRITE_SIZE", sel)
+    rows_fwd = [
+        ("encode_bf16_kernel<32, 8>", None, 2 * tok * D * 2, "K and V read: 2 x 8 x 1048576 x 32 x 2 B"),
+        ("merge_kernel", None, B * H * S * M * (D + 1) * 4,
+         f"split partials: 8 x S x 256 x (32 + 1) x 4 B, S = {S}"),
+        ("decode_bf16_kernel<32>", None, 2 * tok * D * 2, "K read, Y written: 8 x 1048576 x 32 x 2 B each"),
+    ]
+    rows_bwd = [
+        ("lat_bwd_kernel<32, false, 8>", (0, 5), " (one call)", 3 * tok * D * 2 + 2 * tok * 4,
+         "K, dY, Y read in bf16, lse read, delta written"),
+        ("lat_bwd_kernel<32, false, 8>", (5, 10), " (two calls)", 2 * tok * D * 2 + 2 * tok * 4,
+         "K, dY read in bf16, lse and delta read"),
+        ("lat_bwd_kernel<32, true, 8>", None, "", 2 * tok * D * 2, "K, V read in bf16"),
+        ("tok_pair_kernel<32>", (0, 5), " (fp32 gradients)", 3 * tok * D * 2 + 2 * tok * 4 + 2 * tok * D * 4,
+         "K, V, dY read in bf16, lse and delta read, dK and dV written in fp32"),
+        ("tok_pair_kernel<32>", (5, 10), " (bf16 gradients)", 3 * tok * D * 2 + 2 * tok * 4 + 2 * tok * D * 2,
+         "the same with dK and dV written in bf16"),
+        ("tok_bwd_kernel<32, false>", None, "", 3 * tok * D * 2 + tok * D * 4 + 2 * tok * 4,
+         "K, dY, Y read in bf16, dK written in fp32, lse read and delta written"),
+        ("tok_bwd_kernel<32, true>", None, "", 2 * tok * D * 2 + 3 * tok * D * 4,
+         "K, V read in bf16, dK read and written, dV written, all fp32"),
+    ]
+
+    def line(kernel, rng, label, alg, what, fwd=False):
+        if kernel not in fe or kernel not in wr:
+            return None
+        f, w = fe[kernel], wr[kernel]
+        if rng:
+            f, w = f[rng[0]:rng[1]], w[rng[0]:rng[1]]
+        if fwd:
+            f, w = f[step_launches[0]:step_launches[1]], w[step_launches[0]:step_launches[1]]
+        if not f or not w:
+            return None
+        fk, wk = sum(f) / len(f), sum(w) / len(w)
+        rd, wb = fk * 1024 * f_read, wk * 1024 * f_write
+        return (f"| `{kernel}`{label} | {fk:.0f} | {wk:.0f} | {rd / 1e9:.4f} | {wb / 1e9:.4f} | {alg / 1e9:.4f} "
+                f"({what}) | {(rd + wb) / alg:.3f} |")
+
+    head = ["| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (GB) | written (GB) | algorithmic bytes (GB) "
+            "| ratio |", "|---|---|---|---|---|---|---|"]
+    text = ["# HBM traffic per launch, bench workload (FLARE encode+decode, B=1, H=8, D=32, N=1048576, M=256, bf16)",
+            "", "Commands (repo root, one MI355X; each counter in a run of its own):", "", "```"] + TRAFFIC_CMDS + [
+            "```", "",
+            f"Calibration: the 1 GiB device copy reads FETCH_SIZE = {copy_kib[0]:.0f} KiB and WRITE_SIZE = "
+            f"{copy_kib[1]:.0f} KiB per launch, so read counts are scaled by {f_read:.4f} and write counts by "
+            f"{f_write:.4f}.", "", "Forward (the bench step: means over each kernel's launches in the timed steps of the "
+            "metric step loop, after its warm-up):", ""] + head
+    text += [x for x in (line(k, r, "", a, w, True) for k, r, a, w in rows_fwd) if x]
+    text += ["", "The encoder's write column is its split partials (read back by the merge); the decoder's write "
+             "column is Y.", "",
+             "Backward (the bench's backward leg, 5 calls of each form: the one-call pair gradient, then the two-"
+             "call chain, then the one-call form with bf16 dK and dV; a kernel that runs in several forms is "
+             "listed per form):", ""] + head
+    text += [x for x in (line(k, r, lab, a, w) for k, r, lab, a, w in rows_bwd) if x]
+    text += ["", "The latent passes' writes are their fp32 split partials.  The per-kernel JSON files beside this "
+             "one hold the forward figures for bench.py (its `roofline.traffic`), keyed to the kernel sources "
+             "they were taken on."]
     open(out, "w").write("\n".join(text) + "\n")

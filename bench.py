@@ -62,7 +62,8 @@ def parse():
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     ap.add_argument("--summarize", nargs="+", metavar=("NAME", "INPUT"),
                     help="host only: write profiles/<NAME>.md from rocprofv3 output (NAME: units, "
-                         "units_gemm, units_bwd, clock, stats, xreuse TIMING.md PMC_DIR, issue_rates TIMING.md "
+                         "units_gemm, units_bwd, clock, stats TRACE_DIR [BENCH_LOG], xreuse TIMING.md PMC_DIR, "
+                         "issue_rates TIMING.md "
                          "PMC_DIRS...)")
     return ap.parse_args()
 
@@ -80,7 +81,8 @@ def summarize(name, inputs):
     elif name == "issue_rates":
         profiling.write_issue_rates(os.path.join(PROFILES, "issue_rates.gfx950.md"), inputs[1:], inputs[0])
     elif name == "stats":
-        profiling.write_stats(os.path.join(PROFILES, "kernel_stats.encdec_n1m.md"), inputs[0])
+        profiling.write_stats(os.path.join(PROFILES, "kernel_stats.encdec_n1m.md"), inputs[0],
+                              inputs[1] if len(inputs) > 1 else None)
     elif name == "clock":
         profiling.write_clock(os.path.join(PROFILES, "clock.encdec_n1m.md"), inputs)
     elif name == "units_bwd":

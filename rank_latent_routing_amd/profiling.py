@@ -253,7 +253,7 @@ def write_kernel_stats(out, trace_dir, title, command, notes=()):
     rows = list(csv.DictReader(open(path)))
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     lines = [f"# {title}", "", "Command (repo root, one MI355X), then `python bench.py --summarize stats "
-             f"{trace_dir}`:", "", "```", "export TMPDIR=/tmp", command, "```", "",
+             f"{trace_dir} gpurun_out/prof_bench.log`:", "", "```", "export TMPDIR=/tmp", command, "```", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} "
@@ -349,7 +349,7 @@ def write_units_gemm(out, dirs, profiles_dir):
 # ---------------------------------------------------------------- kernel time
 
 STATS_CMD = ("timeout -k 10 900 rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_bench -o run "
-             "-- python3 -u bench.py")
+             "-- python3 -u bench.py > gpurun_out/prof_bench.log")
 STATS_NOTES = [
     "The run is the default bench: 5 warm-up and 20 timed encode+decode steps; the FLARE++ attention extra "
     "at the same sizes; the sharp-score extra (Q x 40: default and exact softmax); the backward leg (the "
@@ -363,10 +363,40 @@ STATS_NOTES = [
     "metric workload's launches alone, with HIP events on the launching stream."]
 
 
-def write_stats(out, trace_dir):
-    """profiles/kernel_stats.encdec_n1m.md from a --kernel-trace --stats run of the default bench."""
+STATS_STEP_LAUNCHES = (5, 25)  # the default bench's 20 timed steps, after 5 warm-up steps
+
+
+def write_stats(out, trace_dir, bench_log=None):
+    """profiles/kernel_stats.encdec_n1m.md from a --kernel-trace --stats run of the default bench, with
+    the metric step's own launches (the timed steps) beside the bench line's live timing of them."""
+    import json
+    per, _ = kernel_trace([trace_dir], ["encode_bf16_kernel<32, 8>", "merge_kernel", "decode_bf16_kernel<32>"])
+    lo, hi = STATS_STEP_LAUNCHES
+    steps = {k: v[lo:hi] for k, v in per.items()}
+    live = {}
+    if bench_log and os.path.exists(bench_log):
+        for l in open(bench_log):
+            if l.startswith("{"):
+                e = json.loads(l)
+                live = {"encode": e["extra"]["encode_ms"] * 1e3, "decode": e["extra"]["decode_ms"] * 1e3,
+                        "kernel": e["roofline"]["kernel"]}
+    notes = list(STATS_NOTES) + ["", f"The metric step's launches alone (dispatches {lo} .. {hi - 1} of each "
+                                 "kernel: the 20 timed steps after 5 warm-up steps), from the same trace:", "",
+                                 "| kernel | launches | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for k in ("encode_bf16_kernel<32, 8>", "merge_kernel", "decode_bf16_kernel<32>"):
+        v = steps.get(k, [])
+        if v:
+            notes.append(f"| `{k}` | {len(v)} | {sum(v) / len(v) / 1e3:.1f} | {min(v) / 1e3:.1f} | {max(v) / 1e3:.1f} |")
+    if live and steps.get("decode_bf16_kernel<32>") and steps.get("encode_bf16_kernel<32, 8>"):
+        enc = (sum(steps["encode_bf16_kernel<32, 8>"]) / len(steps["encode_bf16_kernel<32, 8>"])
+               + sum(steps.get("merge_kernel", [0])) / max(1, len(steps.get("merge_kernel", [0])))) / 1e3
+        dec = sum(steps["decode_bf16_kernel<32>"]) / len(steps["decode_bf16_kernel<32>"]) / 1e3
+        notes += ["", f"The bench line of this traced run timed the encode call (encode + merge) at "
+                  f"{live['encode']:.1f} us and the decode call at {live['decode']:.1f} us with HIP events on the "
+                  f"launch stream, against {enc:.1f} and {dec:.1f} us of kernel time here; the events also take "
+                  f"in the gap between launches.  Its roofline kernel: `{live['kernel']}`."]
     write_kernel_stats(out, trace_dir, "Kernel time, default bench run (metric workload: FLARE encode+decode, "
-                       "B=1, H=8, D=32, N=1048576, M=256, bf16; plus every extra)", STATS_CMD, STATS_NOTES)
+                       "B=1, H=8, D=32, N=1048576, M=256, bf16; plus every extra)", STATS_CMD, notes)
 
 
 # ---------------------------------------------------------------- shader clock

@@ -134,14 +134,17 @@ def cycle_budget(c, units, floor_quads):
         "mfma": c.get("SQ_INSTS_MFMA", nan) / units, "lds": c.get("SQ_INSTS_LDS", nan) / units,
         "salu": c.get("SQ_INSTS_SALU", nan) / units,
         "se_busy": c["SQ_BUSY_CYCLES"] / c["SQ_CYCLES"] if "SQ_BUSY_CYCLES" in c and "SQ_CYCLES" in c else nan,
+        "wait_inst": c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"] if "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c
+        else nan,
+        "wait_any": c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"] if "SQ_WAIT_ANY" in c and "SQ_WAVE_CYCLES" in c else nan,
     }
 
 
 def _budget_rows(means, units, floor_quads):
     rows = ["| kernel | SIMD cycles per block | VALU issue | of which the method's floor | other VALU "
             "| no VALU issued | dual issue (quads) | MFMA busy | MFMA busy while VALU issues | VALU instr. "
-            "| exp | MFMA | LDS instr. | SALU instr. | engines busy |",
-            "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+            "| exp | MFMA | LDS instr. | SALU instr. | engines busy | waves waiting on operands | waves waiting (any) |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     budgets = {}
     for k in sorted(means):
         b = cycle_budget(means[k], units, floor_quads)
@@ -149,7 +152,8 @@ def _budget_rows(means, units, floor_quads):
         rows.append(f"| `{k}` | {b['cycles']:.0f} | {b['issue']:.0f} ({b['valu_quads']:.1f} quads) "
                     f"| {b['floor']:.0f} | {b['extra']:.0f} | {b['idle']:.0f} | {b['dual_quads']:.2f} "
                     f"| {b['mfma_busy']:.0f} | {b['coexec']:.0f} | {b['valu']:.1f} | {b['trans']:.1f} "
-                    f"| {b['mfma']:.1f} | {b['lds']:.1f} | {b['salu']:.1f} | {100 * b['se_busy']:.0f}% |")
+                    f"| {b['mfma']:.1f} | {b['lds']:.1f} | {b['salu']:.1f} | {100 * b['se_busy']:.0f}% "
+                    f"| {100 * b['wait_inst']:.0f}% | {100 * b['wait_any']:.0f}% |")
     return rows, budgets
 
 
@@ -179,7 +183,11 @@ def write_units(out, dirs):
             "- *No VALU issued* is the kernel's cycles minus the issue time: cycles in which no wave of the SIMD "
             "had a VALU instruction ready (waiting on LDS, on the tile barrier, on the matrix core's result or "
             "its issue), plus the time a SIMD holds fewer waves (workgroup start-up and the tail; *engines busy* "
-            "is SQ_BUSY_CYCLES / SQ_CYCLES).",
+            "is SQ_BUSY_CYCLES / SQ_CYCLES).  The two waiting columns are SQ_WAIT_INST_ANY and SQ_WAIT_ANY over "
+            "SQ_WAVE_CYCLES: the share of wave-cycles in which a wave waited for an instruction's operands "
+            "(LDS, memory, the matrix core's result), and for anything (also barriers and counters).  With four "
+            "(encoder) or three (decoder) waves per SIMD a wave may wait while another issues, so these shares "
+            "are not cycles lost by the SIMD; *no VALU issued* is.",
             "- *MFMA busy* overlaps the VALU issue only in part (the co-execution column), and no dual issue "
             "happens while the matrix core is busy. A block's time answers to both: timed variants of the two "
             "kernels (not kept) that fold the scale into bf16 Q, 16 multiplies fewer (-64 issue cycles), took "

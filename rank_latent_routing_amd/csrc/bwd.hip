@@ -481,9 +481,13 @@ __device__ __forceinline__ int lat_chunk_pos(int token, int dc) {
 // into LDS, shared by all waves; per tile a wave forms S^T and dP^T for its
 // latents, the weights and score gradients, and adds dQ (and in the decode
 // role dZ) by products with the staged tokens.  It ends by writing its
-// split's fp32 partials.
+// split's fp32 partials.  The encoder role takes 4-wave workgroups from
+// M = 128 on, three per compute unit (168 VGPRs): with one 8-wave workgroup
+// per unit, each tile's barrier left its SIMDs idle.  The decoder role needs
+// 199 VGPRs and keeps 8 waves at M = 256 (4-wave workgroups, two per unit,
+// timed slower).
 template <int D, bool ENC, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void lat_bwd_kernel(LatBwdParams p) {
+__global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_kernel(LatBwdParams p) {
   constexpr int SD = D / 16;
   constexpr int T = kLatBwdTile;
   __shared__ __attribute__((aligned(16))) bf16 kt[T * D];
@@ -842,8 +846,8 @@ hipError_t launch_tok_pair(const TokPairParams& p, int D, int B, hipStream_t st)
 }
 
 hipError_t launch_lat_bwd(const LatBwdParams& p, int D, int B, bool encode_role, hipStream_t st) {
-  const int lat_blocks = (p.M + 255) / 256;
-  const int NW = p.M <= 64 ? 2 : p.M <= 128 ? 4 : 8;
+  const int NW = p.M <= 64 ? 2 : (encode_role || p.M <= 128) ? 4 : 8;
+  const int lat_blocks = (p.M + 32 * NW - 1) / (32 * NW);
   dim3 grid(p.S, B * p.H, lat_blocks);
 #define FLARE_LAT(DD, EE, WW) hipLaunchKernelGGL((lat_bwd_kernel<DD, EE, WW>), grid, dim3(64 * WW), 0, st, p)
 #define FLARE_LAT_W(DD, EE) \

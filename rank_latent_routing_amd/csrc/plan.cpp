@@ -53,12 +53,15 @@ int64_t plan_decode_bf16(int B, int H, int M, int64_t N, int D) {
   return per_bh;
 }
 
-// Token splits of the backward latent passes: about 1024 workgroups in all,
-// at most one split per 64-token tile.
+// Token splits of the backward latent passes: about 768 workgroups of 256
+// latents in all, at most one split per 64-token tile.  At M = 256 the
+// decoder role runs one 8-wave workgroup per compute unit (three even
+// rounds) and the encoder role two 4-wave workgroups per (split, head), three
+// per compute unit (two even rounds); 1024 workgroups timed 2-3 % slower.
 int plan_bwd_splits(int B, int H, int M, int64_t N) {
   const int64_t bh = (int64_t)B * H * ((M + 255) / 256);
   const int64_t tiles = (N + kLatBwdTile - 1) / kLatBwdTile;
-  int64_t S = (1024 + bh - 1) / bh;
+  int64_t S = (768 + bh - 1) / bh;
   if (S > tiles) S = tiles;
   if (S < 1) S = 1;
   return (int)S;

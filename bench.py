@@ -97,9 +97,9 @@ def summarize(name, inputs):
 # (the kernel itself, shared device code, and the host code that picks its
 # grid).
 KERNEL_SOURCES = {
-    "encode_bf16_kernel": ["encode.hip", "common.hpp", "launch.hpp", "api.cpp"],
-    "merge_kernel": ["encode.hip", "common.hpp", "launch.hpp", "api.cpp"],
-    "decode_bf16_kernel": ["decode.hip", "common.hpp", "launch.hpp", "api.cpp"],
+    "encode_bf16_kernel": ["encode.hip", "common.hpp", "launch.hpp", "api.cpp", "plan.cpp"],
+    "merge_kernel": ["encode.hip", "common.hpp", "launch.hpp", "api.cpp", "plan.cpp"],
+    "decode_bf16_kernel": ["decode.hip", "common.hpp", "launch.hpp", "api.cpp", "plan.cpp"],
 }
 COPY_BYTES = 1 << 30  # bytes read (and written) per launch of the calibration copy
 

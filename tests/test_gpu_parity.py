@@ -269,6 +269,36 @@ def test_mix_seq_b32_sampled_batches():
     check_bf16(got[[0, 31]], _oracle_mix(m, w.H, batches=[0, 31]), "FLARE++ seq mix")
 
 
+# (B, N, C, H, M, q_mult): the small mixer itself, M not a multiple of 32 with
+# 4-wave encoder workgroups, and 300 latents in two latent blocks.
+WORKSPACE_CASES = [(8, 4096, 128, 8, 64, 8.0), (3, 1000, 64, 4, 100, 2.0), (2, 700, 256, 8, 300, 1.0)]
+
+
+@pytest.mark.parametrize("case", WORKSPACE_CASES, ids=lambda c: "B{}N{}C{}H{}M{}-q{}".format(*c))
+def test_mix_ignores_workspace_contents(case):
+    # Nothing the mixer reads from its workspace is left over from before the
+    # call: a workspace full of stale bytes, and one reused by the next call,
+    # give the same output bit for bit as a zeroed one, and that output
+    # matches the oracle.
+    B, N, C, H, M, qm = case
+    w = inputs.Workload("t", "mix", B, N, H, C // H, M, "bf16", dynamic=True, has_wo=False)
+    m = inputs.make_mix(w, seed=N + M, q_mult=qm)
+    g = {n: t.to(DEV) for n, t in m.items()}
+    need = rl.mix_workspace_size(B, N, C, H, M, True, False)
+    outs = []
+    ws = None
+    for fill in (0, 0x7F, 0xFF, None):  # None: the previous call's workspace as it was left
+        if fill is not None:
+            ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+        say(f"  workspace fill {fill}")
+        outs.append(rl.flare_mix(g["x"], g["w_k"], g["w_v"], g["qs"], H, w_ek=g["w_ek"], w_ev=g["w_ev"],
+                                 workspace=ws))
+        torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    check_bf16(f64(outs[0]), _oracle_mix(m, H), f"mix on a stale workspace {case}")
+
+
 @pytest.mark.parametrize("dynamic,has_wo,qm,flags", [
     (True, True, 1.0, 0), (True, True, 8.0, 0), (False, True, 2.0, 0), (False, False, 1.0, EXACT),
     (True, False, 8.0, EXACT)])

@@ -572,8 +572,10 @@ def main():
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
+        h0 = time.perf_counter()
         for _ in range(reps):
             small_mix()
+        eager_host_us = (time.perf_counter() - h0) / reps * 1e6
         e1.record(stream)
         torch.cuda.synchronize()
         eager_ms = e0.elapsed_time(e1) / reps
@@ -586,9 +588,11 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         e0.record(stream)
+        h0 = time.perf_counter()
         with torch.cuda.stream(stream):
             for _ in range(reps):
                 graph.replay()
+        graph_host_us = (time.perf_counter() - h0) / reps * 1e6
         e1.record(stream)
         torch.cuda.synchronize()
         graph_ms = e0.elapsed_time(e1) / reps
@@ -613,6 +617,9 @@ def main():
             "config": "FLARE++ mixer, B=8, N=4096, C=128, H=8, D=16, M=64, bf16, no W_O",
             "eager_ms": round(eager_ms, 4), "graph_ms": round(graph_ms, 4),
             "graph_10_calls_per_replay_ms": round(graph10_ms, 4),
+            # host time to issue one call / one replay: both below the GPU
+            # time per call, so the launch loop never starves the GPU
+            "eager_host_us_per_call": round(eager_host_us, 1), "graph_host_us_per_replay": round(graph_host_us, 1),
             "tokens_per_s_graph": sw.B * sw.N / (graph_ms / 1e3)}
         del graph, graph10, sm, sout, sws
 

@@ -187,6 +187,8 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
       aug_lds[m] = e;
     }
   }
+  __shared__ unsigned next_grp;  // the workgroup's next unclaimed token group
+  if (tid == 0) next_grp = NW;
   __syncthreads();
 
   // B operand of the extra K step: -1 in K rows 0..2 (lane half 0), else 0
@@ -200,8 +202,19 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
   // base + 32 tb + c): every LDS read of a latent chunk serves two score
   // tiles, and the products of the second block run under the first block's
   // exponentials.
-  const int64_t stride = (int64_t)gridDim.x * NW * 64;
-  for (int64_t base = ((int64_t)blockIdx.x * NW + wave) * 64; base < p.N; base += stride) {
+  // Workgroup b owns the 64-token groups of the (NW x 64)-token passes b,
+  // b + G, ... (G = gridDim.x); wave w starts with group w and then claims
+  // the next unclaimed group from an LDS counter (a SIMD favours its oldest
+  // wave: with fixed shares the youngest waves finished last, alone).
+  auto grp = [&](unsigned j) -> int64_t {
+    return ((int64_t)blockIdx.x + (int64_t)(j / NW) * gridDim.x) * (NW * 64) + (int64_t)(j % NW) * 64;
+  };
+  auto claim = [&]() -> unsigned {
+    unsigned jn = 0;
+    if (lane == 0) jn = atomicAdd(&next_grp, 1u);
+    return __builtin_amdgcn_readfirstlane(jn);
+  };
+  for (int64_t base = grp(wave); base < p.N; base = grp(claim())) {
     // B operands: token n, features 16sd + 8h .. +7 of K and of X
     bf16x8 kb[2][SD], xb[2][SD];
     float l2n[2] = {0.f, 0.f}, dln[2] = {0.f, 0.f};
@@ -367,6 +380,8 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
     }
     aug_lds[m] = e;
   }
+  __shared__ unsigned next_grp;  // the workgroup's next unclaimed token group
+  if (tid == 0) next_grp = NW;
   __syncthreads();
 
   bf16x8 bneg = {};
@@ -375,7 +390,6 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
   const bf16* vbase = reinterpret_cast<const bf16*>(p.v.data) + b * p.v.sb + hd * p.v.sh;
   const bf16* gbase = reinterpret_cast<const bf16*>(p.dy.data) + b * p.dy.sb + hd * p.dy.sh;
   const float cs = p.c;
-  const int64_t stride = (int64_t)gridDim.x * NW * 32;
   // The wave's next 32 tokens are loaded while the current ones are
   // computed: lane (h, c) holds token n, B operands with features
   // 16sd + 8h .. +7 of K, V and dY, and the token's normaliser and delta.
@@ -398,9 +412,16 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
     nl2 = valid ? p.lse_d[(int64_t)bh * p.N + n] : 0.f;
     ndd = valid ? p.delta_d[(int64_t)bh * p.N + n] : 0.f;
   };
-  int64_t base = ((int64_t)blockIdx.x * NW + wave) * 32;
+  // Workgroup b owns the 32-token groups of the (NW x 32)-token passes b,
+  // b + G, ... (G = gridDim.x); wave w starts with group w and then claims
+  // the next unclaimed group from an LDS counter, so that the waves a SIMD
+  // favours (its oldest) take more groups and all finish together.
+  auto grp = [&](unsigned j) -> int64_t {
+    return ((int64_t)blockIdx.x + (int64_t)(j / NW) * gridDim.x) * (NW * 32) + (int64_t)(j % NW) * 32;
+  };
+  int64_t base = grp(wave), nbase = 0;
   if (base < p.N) fetch(base);
-  for (; base < p.N; base += stride) {
+  for (; base < p.N; base = nbase) {
     const int64_t n = base + c;
     const bool valid = n < p.N;
     bf16x8 kb[SD], vb[SD], gb[SD];
@@ -412,7 +433,10 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
     }
     const float l2d = nl2 * kLog2e;
     const float dd = ndd;
-    if (base + stride < p.N) fetch(base + stride);
+    unsigned jn = 0;
+    if (lane == 0) jn = atomicAdd(&next_grp, 1u);
+    nbase = grp(__builtin_amdgcn_readfirstlane(jn));
+    if (nbase < p.N) fetch(nbase);
 
     f32x16 dk = zero16(), dv = zero16();
     for (int ch = 0; ch < MC; ++ch) {

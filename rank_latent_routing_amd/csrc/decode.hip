@@ -109,15 +109,25 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
   // Each weight is at most the normaliser l it sums into, so with every
   // |Z| < 2^26 and l <= 2^100 the unnormalised outputs stay below 2^126:
   // only l needs checking before the fast result is kept.
+  __shared__ unsigned next_group;  // the workgroup's next unclaimed 64-token group
+  if (tid == 0) next_group = NW;
   const bool z_small = __syncthreads_and(z_bounded) != 0;
 
   const float cs = p.c;
   const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + hd * p.k.sh;
-  // Workgroup b takes the (NW x 64)-token passes b, b + G, b + 2G, ... of its
-  // head (G = gridDim.x), so the resident workgroups sweep one window of K;
-  // wave w takes tokens 64w .. 64w + 63 of each pass.
+  // Workgroup b owns the (NW x 64)-token passes b, b + G, b + 2G, ... of its
+  // head (G = gridDim.x), so the resident workgroups sweep one window of K.
+  // Its 64-token groups (group j: slot j % NW of its pass j / NW) go to the
+  // waves in order: wave w starts with group w and then claims the next
+  // unclaimed one from an LDS counter.  A SIMD favours its oldest wave, so
+  // with fixed shares the oldest waves finished far ahead of the youngest
+  // (at 50 %, 75 % and 100 % of the kernel's time at the bench size) and each
+  // SIMD ran the rest with fewer waves; claimed groups keep all three waves
+  // busy to the end.  The outputs do not depend on which wave takes a group.
   const int64_t n_end = p.N;
-  const int64_t pass_stride = (int64_t)gridDim.x * kDecGroup * NW;
+  auto group_base = [&](unsigned j) -> int64_t {
+    return ((int64_t)blockIdx.x + (int64_t)(j / NW) * gridDim.x) * (kDecGroup * NW) + (int64_t)(j % NW) * kDecGroup;
+  };
 
   // K of a 64-token group comes by buffer loads into the wave's LDS slot
   // (a uniform descriptor covering exactly the group's valid rows, and
@@ -144,9 +154,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(kslot + t * 512), 16, k_off0 + t * k_step, 0, 0, 0);
   };
 
-  int64_t base = (int64_t)blockIdx.x * kDecGroup * NW + kDecGroup * wave;
+  int64_t base = group_base(wave), nbase = 0;
   if (base < n_end) issue_k(base);
-  for (; base < n_end; base += pass_stride) {
+  for (; base < n_end; base = nbase) {
     // B operands of S^T = Q K^T: lane (h, c) holds token base + 32tb + c,
     // features 16sd + 8h .. +7.
     bf16x8 kb[2][SD];
@@ -158,7 +168,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
         kb[tb][sd] = *reinterpret_cast<const bf16x8*>(kslot + 8 * dec_k_pos<D>(32 * tb + c, 2 * sd + h));
     // the slot is read before the next group's load may overwrite it
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    if (base + pass_stride < n_end) issue_k(base + pass_stride);
+    unsigned jn = 0;
+    if (lane == 0) jn = atomicAdd(&next_group, 1u);
+    nbase = group_base(__builtin_amdgcn_readfirstlane(jn));
+    if (nbase < n_end) issue_k(nbase);
 
     f32x16 yacc[2];
     float lsum[2], mx[2];

@@ -481,7 +481,7 @@ BWD_GROUPS = [
      "latent pass, decoder role, computing delta from Y (`lat_bwd_kernel<32, false, 8>`, one-call)"),
     ("lat_bwd_kernel<32, false, 8>", 5, 10, "latent pass, decoder role (`lat_bwd_kernel<32, false, 8>`, two-call chain)"),
     ("lat_bwd_kernel<32, false, 8>", 10, 15, "the one-call form's latent pass again, in the bf16 dK, dV calls"),
-    ("lat_bwd_kernel<32, true, 8>", 0, 15, "latent pass, encoder role (`lat_bwd_kernel<32, true, 8>`, all forms)"),
+    ("lat_bwd_kernel<32, true, 4>", 0, 15, "latent pass, encoder role (`lat_bwd_kernel<32, true, 4>`, all forms)"),
     ("tok_bwd_kernel<32, false>", 0, 5, "token pass, decoder role (`tok_bwd_kernel<32, false>`, two-call chain)"),
     ("tok_bwd_kernel<32, true>", 0, 5, "token pass, encoder role (`tok_bwd_kernel<32, true>`, two-call chain)"),
 ]
@@ -654,7 +654,7 @@ def write_traffic_md(out, fetch_csv, write_csv, f_read, f_write, copy_kib, step_
          "K, dY, Y read in bf16, lse read, delta written"),
         ("lat_bwd_kernel<32, false, 8>", (5, 10), " (two calls)", 2 * tok * D * 2 + 2 * tok * 4,
          "K, dY read in bf16, lse and delta read"),
-        ("lat_bwd_kernel<32, true, 8>", None, "", 2 * tok * D * 2, "K, V read in bf16"),
+        ("lat_bwd_kernel<32, true, 4>", None, "", 2 * tok * D * 2, "K, V read in bf16 once; each of the two 128-latent blocks of a split reads them"),
         ("tok_pair_kernel<32>", (0, 5), " (fp32 gradients)", 3 * tok * D * 2 + 2 * tok * 4 + 2 * tok * D * 4,
          "K, V, dY read in bf16, lse and delta read, dK and dV written in fp32"),
         ("tok_pair_kernel<32>", (5, 10), " (bf16 gradients)", 3 * tok * D * 2 + 2 * tok * 4 + 2 * tok * D * 2,

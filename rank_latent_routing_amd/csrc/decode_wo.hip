@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void swizzle_wo_kernel(const bf16* __restrict_
 template <int HH>
 __global__ __launch_bounds__(64 * kDecWoWaves, 3) void decode_wo_kernel(DecodeWoParams p) {
   constexpr int NW = kDecWoWaves;
-  constexpr int D = 32, SD = 2;
+  constexpr int SD = 2;  // head width 32: two 16-wide feature slices
   constexpr int C = 32 * HH, KC = C / 8;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 

@@ -87,6 +87,7 @@ flare_status encode_impl(const View& q, const View& k, const View& v, void* z, i
   const EncodePlan pl = plan_encode(B, H, M, N, D, k.is_f32, max_splits);
   const size_t parts = (size_t)B * H * pl.S * M;
   EncodeParams ep;
+  std::memset(&ep, 0, sizeof(ep));
   ep.q = q;
   ep.k = k;
   ep.v = v;
@@ -117,11 +118,41 @@ flare_status encode_impl(const View& q, const View& k, const View& v, void* z, i
   return hip_status(launch_merge(mp, B, st));
 }
 
+// The mixer's split encoder without its merge launch: the decoder merges the
+// split results (written at ws) while it stages them.
+flare_status encode_splits(const View& q, const View& k, const View& v, int B, int H, int M, int64_t N, int D,
+                           float c, unsigned flags, void* ws, hipStream_t st) {
+  const EncodePlan pl = plan_encode(B, H, M, N, D, 0);
+  const size_t parts = (size_t)B * H * pl.S * M;
+  EncodeParams ep;
+  std::memset(&ep, 0, sizeof(ep));
+  ep.q = q;
+  ep.k = k;
+  ep.v = v;
+  ep.part_o = reinterpret_cast<float*>(ws);
+  ep.part_l = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align_up(parts * D * sizeof(float)));
+  ep.H = H;
+  ep.M = M;
+  ep.S = pl.S;
+  ep.N = N;
+  ep.tokens_per_split = pl.tokens_per_split;
+  ep.c = c;
+  ep.exact = (flags & FLARE_FLAG_EXACT_SOFTMAX) ? 1 : 0;
+  return hip_status(launch_encode_bf16(ep, D, B, pl.waves, pl.lat_blocks, st));
+}
+
+// zm_o / zm_l / zm_S (bf16 path only): merge Z from the encoder's split results
+// while staging it instead of reading z.
 flare_status decode_impl(const View& k, const View& q, const View& z, void* y, int y_f32,
                          int64_t y_sb, int64_t y_sh, int64_t y_sl, float* lse, int B, int H, int M,
-                         int64_t N, int D, float c, unsigned flags, hipStream_t st) {
+                         int64_t N, int D, float c, unsigned flags, hipStream_t st,
+                         const float* zm_o = nullptr, const float* zm_l = nullptr, int zm_S = 0) {
   DecodeParams dp;
+  std::memset(&dp, 0, sizeof(dp));
   dp.lse = lse;
+  dp.zm_part_o = zm_o;
+  dp.zm_part_l = zm_l;
+  dp.zm_S = zm_S;
   dp.k = k;
   dp.q = q;
   dp.z = z;
@@ -362,6 +393,7 @@ flare_status flare_project(const void* X, const void* const* W, void* const* Y, 
 namespace {
 struct MixLayout {
   size_t kv, qx, z, y, wsw, wosw, enc, wof, total;
+  bool fold;  // the encoder's split results are small enough for the decoder to merge
 };
 static MixLayout mix_layout(int B, int64_t N, int C, int H, int M, int dynamic, int has_wo) {
   MixLayout L;
@@ -384,6 +416,14 @@ static MixLayout mix_layout(int B, int64_t N, int C, int H, int M, int dynamic, 
   off += has_wo ? proj_ws(C, C, 1) : 0;
   L.enc = off;
   off += encode_ws(B, H, M, N, D, 0);
+  // Small split sets (at most kConsumerMergeBytes of split results per batch
+  // x head, and room for the merged Z in the decoder's LDS): the decoder
+  // merges the encoder's split results while staging Z, in place of a merge
+  // launch.  (The synthesis keeps its merge launch: every split workgroup of
+  // the encoder would merge the same queries again.)
+  const EncodePlan pl = plan_encode(B, H, M, N, D, 0);
+  L.fold = (int64_t)pl.S * M * (D + 1) * 4 <= kConsumerMergeBytes &&
+           decode_bf16_lds(M, D) + decode_merge_lds(M, D) <= 160 * 1024;
   // the fused output projection's prepared operands (reserved whenever W_O
   // is given, so the size does not depend on the flags)
   L.wof = off;
@@ -456,6 +496,13 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V, const vo
   qs.sl = D;
   View q = qs;
   const int64_t lat_sb = (int64_t)H * M * D, lat_sh = (int64_t)M * D, lat_sl = D;
+  const bool fused_wo = has_wo && (flags & FLARE_MIX_FUSED_WO) && D == 32 && (H == 4 || H == 8);
+  View z;
+  z.data = ws + L.z;
+  z.is_f32 = 1;
+  z.sb = lat_sb;
+  z.sh = lat_sh;
+  z.sl = lat_sl;
   // (b) FLARE++: Q(X) = SDPA(seeds, eK, eV), kept in fp32
   if (dynamic) {
     s = encode_impl(qs, head_major(ekp), head_major(evp), ws + L.qx, 1, lat_sb, lat_sh, lat_sl, nullptr,
@@ -467,18 +514,30 @@ flare_status flare_mix(const void* X, const void* W_K, const void* W_V, const vo
     q.sh = lat_sh;
     q.sl = lat_sl;
   }
-  // (c) Z = SDPA(Q, K, V)
+  // (c) Z = SDPA(Q, K, V); for small split sets the decoder merges the split
+  // results while staging Z (no merge launch)
+  if (L.fold && !fused_wo) {
+    s = encode_splits(q, head_major(kp), head_major(vp), B, H, M, N, D, c, flags, ws + L.enc, st);
+    if (s != FLARE_OK) return s;
+    const EncodePlan pl = plan_encode(B, H, M, N, D, 0);
+    const float* part_o = reinterpret_cast<const float*>(ws + L.enc);
+    const float* part_l = reinterpret_cast<const float*>(ws + L.enc + align_up((size_t)B * H * pl.S * M * D * 4));
+    void* ydst = has_wo ? (void*)(ws + L.y) : out;
+    s = decode_impl(head_major(kp), q, z, ydst, 0, N * C, D, C, nullptr, B, H, M, N, D, c, flags, st, part_o, part_l,
+                    pl.S);
+    if (s != FLARE_OK) return s;
+    if (has_wo) {
+      const void* wo[1] = {W_O};
+      void* yo[1] = {out};
+      s = project_impl(ws + L.y, wo, yo, 1, (int64_t)B * N, C, C, 0, B, D, ws + L.wosw, st);
+    }
+    return s;
+  }
   s = encode_impl(q, head_major(kp), head_major(vp), ws + L.z, 1, lat_sb, lat_sh, lat_sl, nullptr, B,
                   H, M, N, D, c, flags, ws + L.enc, st);
   if (s != FLARE_OK) return s;
-  View z;
-  z.data = ws + L.z;
-  z.is_f32 = 1;
-  z.sb = lat_sb;
-  z.sh = lat_sh;
-  z.sl = lat_sl;
   // (d, e) fused: out = [SDPA(K_h, Q_h, Z_h)]_h W_O in one pass
-  if (has_wo && (flags & FLARE_MIX_FUSED_WO) && D == 32 && (H == 4 || H == 8)) {
+  if (fused_wo) {
     DecodeWoParams dw;
     std::memset(&dw, 0, sizeof(dw));
     dw.k = head_major(kp);

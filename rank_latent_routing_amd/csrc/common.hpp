@@ -147,6 +147,47 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0
 // no swizzle; reads past num_records return zero.
 constexpr int kBufferFlags = 0x00020000;
 
+// The exact combination of split encoders for four features of one latent
+// ("FLARE++", section 3, "Multi-GPU context parallelism": partial results
+// merge by their log-normalisers): with L_s the log2-normaliser of split s
+// (at pl[s * lstride]; -inf for an empty split) and O_s its normalised output
+// (at po[s * ostride]), returns sum_s 2^{L_s - L} O_s, L = log2 sum_s 2^{L_s},
+// folded in split order with a running maximum.  Sixteen splits' values are
+// loaded before any is folded (one memory round trip for up to 16 splits).
+__device__ __forceinline__ f32x4 merge_splits4(const float* pl, int64_t lstride, const f32x4* po, int64_t ostride,
+                                               int S) {
+  constexpr int kBatch = 16;
+  float mx = -INFINITY, sum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float lsv[kBatch];
+    f32x4 osv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int s = s0 + j;
+      lsv[j] = s < S ? pl[(int64_t)s * lstride] : -INFINITY;
+      osv[j] = s < S ? po[(int64_t)s * ostride] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float ls = lsv[j];
+      if (ls == -INFINITY) continue;
+      if (ls > mx) {
+        const float a = exp2f(mx - ls);
+        sum *= a;
+        acc *= a;
+        mx = ls;
+      }
+      const float w = exp2f(ls - mx);
+      sum += w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, osv[j][i], acc[i]);
+    }
+  }
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  return acc * inv;
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }

@@ -65,55 +65,18 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
   bf16x8* q_lds = reinterpret_cast<bf16x8*>(smem);                                          // [MC][SD][64]
   bf16x8* z_lds = reinterpret_cast<bf16x8*>(smem + (size_t)MC * SD * 64 * sizeof(bf16x8));  // [MC][2][64]
   bf16* kslot = reinterpret_cast<bf16*>(smem + (size_t)MC * (SD + 2) * 64 * sizeof(bf16x8)) + wave * KSLOT;
+  // merged Z [32 MC][D] in fp32, only when Z is merged here from the split results
+  float* zm = reinterpret_cast<float*>(smem + (size_t)MC * (SD + 2) * 64 * sizeof(bf16x8) +
+                                       (size_t)NW * KSLOT * sizeof(bf16));
 
-  // Stage Q: lane (h, c) of chunk ch, slice sd holds latent 32ch + c,
-  // features 16sd + 8h .. +7 in bf16; the scale multiplies the fp32 scores.
-  for (int u = tid; u < MC * SD * 64; u += NT) {
-    const int ch = u / (SD * 64), sd = (u >> 6) % SD, ln = u & 63, hh = ln >> 5, cc = ln & 31;
-    const int m = 32 * ch + cc;
-    float qv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qv[j] = 0.f;
-    if (m < p.M) load_as_f32<8>(p.q.data, p.q.is_f32, b * p.q.sb + hd * p.q.sh + (int64_t)m * p.q.sl + 16 * sd + 8 * hh, qv);
-    bf16x8 qb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qb[j] = (bf16)qv[j];
-    q_lds[(ch * SD + sd) * 64 + ln] = qb;
-  }
-  // Stage Z^T: row r (lane c = r) of the A operand is feature
-  // sigma(r) = 16((r >> 2) & 1) + 4(r >> 3) + (r & 3), chosen so that the
-  // output rows lane half h receives (8q + 4h + i%4) are the 16 contiguous
-  // features 16h .. 16h + 15 of its token; rows with sigma(r) >= D are zero.
-  // z_bounded: every staged value below 2^26 in magnitude (false for NaN).
-  bool z_bounded = true;
-  for (int u = tid; u < MC * 2 * 64; u += NT) {
-    const int ch = u >> 7, ug = (u >> 6) & 1, ln = u & 63, hh = ln >> 5, r = ln & 31;
-    const int d = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
-    bf16x8 val;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = chunk_latent(ch, ug, hh, j);
-      float zv = 0.f;
-      if (m < p.M && d < D) load_as_f32<1>(p.z.data, p.z.is_f32, b * p.z.sb + hd * p.z.sh + (int64_t)m * p.z.sl + d, &zv);
-      val[j] = (bf16)zv;
-      z_bounded = z_bounded && fabsf((float)val[j]) < 67108864.0f;
-    }
-    z_lds[(ch * 2 + ug) * 64 + ln] = val;
-  }
   // Zero this wave's K slot: lanes past the last token may leave their chunk
   // unwritten, and the stale data must be finite (its scores are discarded).
   {
     const bf16x8 z8 = {};
     for (int u = lane; u < KSLOT / 8; u += 64) reinterpret_cast<bf16x8*>(kslot)[u] = z8;
   }
-  // Each weight is at most the normaliser l it sums into, so with every
-  // |Z| < 2^26 and l <= 2^100 the unnormalised outputs stay below 2^126:
-  // only l needs checking before the fast result is kept.
-  __shared__ unsigned next_group;  // the workgroup's next unclaimed 64-token group
-  if (tid == 0) next_group = NW;
-  const bool z_small = __syncthreads_and(z_bounded) != 0;
-
-  const float cs = p.c;
+  // the zeros are in LDS before the first group's loads can land in the slot
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   const bf16* kbase = reinterpret_cast<const bf16*>(p.k.data) + b * p.k.sb + hd * p.k.sh;
   // Workgroup b owns the (NW x 64)-token passes b, b + G, b + 2G, ... of its
   // head (G = gridDim.x), so the resident workgroups sweep one window of K.
@@ -156,6 +119,71 @@ __global__ __launch_bounds__(64 * kDecWaves, 3) void decode_bf16_kernel(DecodePa
 
   int64_t base = group_base(wave), nbase = 0;
   if (base < n_end) issue_k(base);
+  // The first group's K loads are in flight while Q and Z are staged below.
+
+  // Stage Q: lane (h, c) of chunk ch, slice sd holds latent 32ch + c,
+  // features 16sd + 8h .. +7 in bf16; the scale multiplies the fp32 scores.
+  for (int u = tid; u < MC * SD * 64; u += NT) {
+    const int ch = u / (SD * 64), sd = (u >> 6) % SD, ln = u & 63, hh = ln >> 5, cc = ln & 31;
+    const int m = 32 * ch + cc;
+    float qv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qv[j] = 0.f;
+    if (m < p.M) load_as_f32<8>(p.q.data, p.q.is_f32, b * p.q.sb + hd * p.q.sh + (int64_t)m * p.q.sl + 16 * sd + 8 * hh, qv);
+    bf16x8 qb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qb[j] = (bf16)qv[j];
+    q_lds[(ch * SD + sd) * 64 + ln] = qb;
+  }
+  // With zm_part_o, Z is first merged from the encoder's split results (the
+  // same fold as the merge kernel, splits in order) into LDS, four features
+  // per thread, and staged from there.
+  const bool z_merge = p.zm_part_o != nullptr;
+  if (z_merge) {
+    const int64_t MD = (int64_t)p.M * D;
+    for (int u = tid; u < p.M * (D / 4); u += NT) {
+      const int m = u / (D / 4), d4 = 4 * (u % (D / 4));
+      const f32x4 v = merge_splits4(p.zm_part_l + (int64_t)bh * p.zm_S * p.M + m, p.M,
+                                    reinterpret_cast<const f32x4*>(p.zm_part_o + (int64_t)bh * p.zm_S * MD +
+                                                                   (int64_t)m * D + d4),
+                                    MD / 4, p.zm_S);
+      *reinterpret_cast<f32x4*>(zm + m * D + d4) = v;
+    }
+    __syncthreads();
+  }
+  // Stage Z^T: row r (lane c = r) of the A operand is feature
+  // sigma(r) = 16((r >> 2) & 1) + 4(r >> 3) + (r & 3), chosen so that the
+  // output rows lane half h receives (8q + 4h + i%4) are the 16 contiguous
+  // features 16h .. 16h + 15 of its token; rows with sigma(r) >= D are zero.
+  // z_bounded: every staged value below 2^26 in magnitude (false for NaN).
+  bool z_bounded = true;
+  for (int u = tid; u < MC * 2 * 64; u += NT) {
+    const int ch = u >> 7, ug = (u >> 6) & 1, ln = u & 63, hh = ln >> 5, r = ln & 31;
+    const int d = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+    bf16x8 val;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = chunk_latent(ch, ug, hh, j);
+      float zv = 0.f;
+      if (m < p.M && d < D) {
+        if (z_merge)
+          zv = zm[m * D + d];
+        else
+          load_as_f32<1>(p.z.data, p.z.is_f32, b * p.z.sb + hd * p.z.sh + (int64_t)m * p.z.sl + d, &zv);
+      }
+      val[j] = (bf16)zv;
+      z_bounded = z_bounded && fabsf((float)val[j]) < 67108864.0f;
+    }
+    z_lds[(ch * 2 + ug) * 64 + ln] = val;
+  }
+  // Each weight is at most the normaliser l it sums into, so with every
+  // |Z| < 2^26 and l <= 2^100 the unnormalised outputs stay below 2^126:
+  // only l needs checking before the fast result is kept.
+  __shared__ unsigned next_group;  // the workgroup's next unclaimed 64-token group
+  if (tid == 0) next_group = NW;
+  const bool z_small = __syncthreads_and(z_bounded) != 0;
+
+  const float cs = p.c;
   for (; base < n_end; base = nbase) {
     // B operands of S^T = Q K^T: lane (h, c) holds token base + 32tb + c,
     // features 16sd + 8h .. +7.
@@ -398,7 +426,7 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
 hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t st) {
   const int64_t blocks = p.tokens_per_block;  // workgroups per head
   dim3 grid((unsigned)blocks, B * p.H);
-  const size_t lds = decode_bf16_lds(p.M, D);
+  const size_t lds = decode_bf16_lds(p.M, D) + (p.zm_part_o ? decode_merge_lds(p.M, D) : 0);
   hipError_t e;
   if (D == 32) {
     if ((e = allow_lds(decode_bf16_kernel<32>, lds)) != hipSuccess) return e;

@@ -245,6 +245,98 @@ __global__ __launch_bounds__(64 * kGemmWaves, 4) void gemm_bf16_kernel(GemmParam
   }
 }
 
+// Weight sets of at most kGemmPreloadBytes (all blocks of every projection,
+// e.g. four 128 x 128 weights): every block is loaded into LDS once at the
+// start and the blocks are then computed with no further waits.  In the
+// streamed kernel above, each block's wait for its weights also waits for the
+// output stores issued before that load (one counter covers both), so with
+// short blocks the store latency sets the pace.
+constexpr int kGemmPreloadBytes = 128 * 1024;
+
+template <int CIN, bool PAIR>
+__global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_preload_kernel(GemmParams p) {
+  constexpr int NW = kGemmWaves;
+  constexpr int KS = CIN / 32;
+  constexpr int BLK = KS * 2 * 512;  // bf16 elements of one 32-column block
+  constexpr int OPS = BLK / 512;     // 1 KB loads per block
+  extern __shared__ __attribute__((aligned(16))) bf16 wl[];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t row = (int64_t)blockIdx.x * 16 * NW + wave * 16 + r;
+  const bf16* xin = reinterpret_cast<const bf16*>(p.x);
+  const int pairs = p.Cout / 32;
+  const int nblk = p.n_proj * pairs;
+
+  // every block of every projection, 1 KB per load, spread over the waves
+  for (int op = wave; op < nblk * OPS; op += NW) {
+    const int b = op / OPS, o = op - b * OPS;
+    const int pr = b / pairs, pb = b - pr * pairs;
+    const bf16* src = reinterpret_cast<const bf16*>(p.wt[pr]) + (int64_t)pb * BLK;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(src), (short)0, BLK * (int)sizeof(bf16), kBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(wl + (int64_t)b * BLK + o * 512), 16, lane * 16,
+                                             o * 1024, 0, 0);
+  }
+  bf16x8 xb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (row < p.R) {
+      xb[ks] = *reinterpret_cast<const bf16x8*>(xin + row * CIN + 32 * ks + 8 * g);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xb[ks][j] = (bf16)0.0f;
+    }
+  }
+  int64_t row_off;
+  {
+    const int64_t rr = min(row, p.R - 1);
+    if (p.head_major) {
+      const int64_t bi = rr / p.N, n = rr - bi * p.N;
+      row_off = (bi * (p.Cout / p.D) * p.N + n) * p.D;
+    } else {
+      row_off = rr * p.Cout;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  barrier_keep_loads();
+
+  bf16x8 carry = {};
+  for (int b = 0; b < nblk; ++b) {
+    const bf16* st = wl + (int64_t)b * BLK;
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + ((ks * 2 + t) * 64 + lane) * 8);
+        acc[t] = mfma_16x16x32(a, xb[ks], acc[t]);
+      }
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = (bf16)acc[0][i];
+      v[4 + i] = (bf16)acc[1][i];
+    }
+    const int pr = b / pairs, pb = b - pr * pairs;
+    const int col = 32 * pb + 8 * g;
+    int64_t col_off = col;
+    if (p.head_major) {
+      const int hd = col / p.D;
+      col_off = (int64_t)hd * p.N * p.D + (col - hd * p.D);
+    }
+    bf16* yp = reinterpret_cast<bf16*>(p.y[pr]) + row_off + col_off;
+    if constexpr (PAIR) {
+      if ((pb & 1) == 0) {
+        carry = v;
+        continue;
+      }
+      if (row < p.R) *reinterpret_cast<bf16x8*>(yp - 32) = carry;
+    }
+    if (row < p.R) *reinterpret_cast<bf16x8*>(yp) = v;
+  }
+}
+
 hipError_t launch_swizzle_weights(const SwizzleParams& p, int n, hipStream_t st) {
   const int64_t groups = (int64_t)p.Cin * p.Cout / 8;
   hipLaunchKernelGGL(swizzle_weights_kernel, dim3((unsigned)((groups + 255) / 256), (unsigned)n), dim3(256), 0,
@@ -261,6 +353,34 @@ hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t st) {
   // whole 128-byte output lines per wave for row-major outputs of an even
   // number of 32-column blocks
   const bool pair = !p.head_major && (p.Cout / 32) % 2 == 0;
+  const size_t wbytes = (size_t)p.n_proj * p.Cin * p.Cout * sizeof(bf16);
+  if (rb == 1 && wbytes <= (size_t)kGemmPreloadBytes) {
+    dim3 pgrid((unsigned)((p.R + 16 * kGemmWaves - 1) / (16 * kGemmWaves)));
+#define FLARE_GEMM_PRE(C)                                                                                  \
+  {                                                                                                        \
+    hipError_t e;                                                                                          \
+    if (pair) {                                                                                            \
+      if ((e = hipFuncSetAttribute((const void*)gemm_bf16_preload_kernel<C, true>,                         \
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)wbytes)) != hipSuccess) \
+        return e;                                                                                          \
+      hipLaunchKernelGGL((gemm_bf16_preload_kernel<C, true>), pgrid, block, wbytes, st, p);                \
+    } else {                                                                                               \
+      if ((e = hipFuncSetAttribute((const void*)gemm_bf16_preload_kernel<C, false>,                        \
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)wbytes)) != hipSuccess) \
+        return e;                                                                                          \
+      hipLaunchKernelGGL((gemm_bf16_preload_kernel<C, false>), pgrid, block, wbytes, st, p);               \
+    }                                                                                                      \
+  }
+    switch (p.Cin) {
+      case 32: FLARE_GEMM_PRE(32); break;
+      case 64: FLARE_GEMM_PRE(64); break;
+      case 128: FLARE_GEMM_PRE(128); break;
+      case 256: FLARE_GEMM_PRE(256); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef FLARE_GEMM_PRE
+    return hipGetLastError();
+  }
 #define FLARE_GEMM(C)                                                                  \
   if (rb == 2 && pair)                                                               \
     hipLaunchKernelGGL((gemm_bf16_kernel<C, 2, true>), grid, block, 0, st, p);       \

@@ -55,6 +55,12 @@ struct DecodeParams {
   float c;
   int exact;
   float* lse;         // [B, H, N] natural-log row normalisers, may be null
+  // When zm_part_o is set, Z is not read from z but merged from the
+  // encoder's split results ([B*H, zm_S, M, D] and [B*H, zm_S, M]) while it
+  // is staged: the mixer's encoder without a merge launch.
+  const float* zm_part_o;
+  const float* zm_part_l;
+  int zm_S;
 };
 
 // Backward, token-parallel pass (decoder layout): per token, dK (and dV).
@@ -174,6 +180,11 @@ hipError_t launch_merge(const MergeParams& p, int B, hipStream_t s);
 int64_t plan_decode_bf16(int B, int H, int M, int64_t N, int D);
 // LDS bytes of one decoder workgroup.
 size_t decode_bf16_lds(int M, int D);
+// Extra LDS of a decoder that merges Z from split results while staging it.
+inline size_t decode_merge_lds(int M, int D) { return (size_t)((M + 31) / 32) * 32 * D * sizeof(float); }
+// Split results (per batch*head) that a consumer kernel may merge itself
+// while staging them, in place of a merge launch.
+constexpr int64_t kConsumerMergeBytes = 128 * 1024;
 hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams& p, int D, int B, hipStream_t s);
 int plan_bwd_splits(int B, int H, int M, int64_t N);

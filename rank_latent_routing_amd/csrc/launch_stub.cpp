@@ -26,6 +26,7 @@ enum RangeTag {
   kEncV = 9,       // encoder V rows (read)
   kWoLat = 10,     // fused output projection: prepared latent operands (written)
   kWoT = 11,       // fused output projection: prepared W_O^T (written)
+  kDecZPart = 12,  // decoder: the encoder's split results, merged into Z while staged (read)
 };
 
 struct Range {
@@ -77,7 +78,14 @@ hipError_t launch_encode_f32(const EncodeParams& p, int D, int B, hipStream_t s)
   return e;
 }
 hipError_t launch_merge(const MergeParams&, int, hipStream_t) { return record("merge"); }
-hipError_t launch_decode_bf16(const DecodeParams&, int, int, hipStream_t) { return record("decode_bf16"); }
+hipError_t launch_decode_bf16(const DecodeParams& p, int D, int B, hipStream_t) {
+  if (p.zm_part_o) {
+    const unsigned long long zparts = (unsigned long long)B * p.H * p.zm_S * p.M;
+    add_range(p.zm_part_o, zparts * D * 4, kDecZPart);
+    add_range(p.zm_part_l, zparts * 4, kDecZPart);
+  }
+  return record("decode_bf16");
+}
 hipError_t launch_decode_f32(const DecodeParams&, int, int, hipStream_t) { return record("decode_f32"); }
 hipError_t launch_tok_bwd(const TokBwdParams&, int, int, bool, hipStream_t) { return record("tok_bwd"); }
 hipError_t launch_lat_bwd(const LatBwdParams& p, int D, int B, bool, hipStream_t) {

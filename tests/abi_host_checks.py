@@ -38,7 +38,8 @@ BF16, F32 = cabi.FLARE_BF16, cabi.FLARE_F32
 FAKE = 0x7F0000000000   # fake tensor base (256-byte aligned)
 WS = 0x100000000000     # fake workspace base, far from the tensors
 OUT = FAKE + (1 << 36)  # the mixer's output
-ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SUM_PART, SWIZZLED, GEMM_OUT, ENC_K, ENC_V, WO_LAT, WO_T = range(1, 12)
+(ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SUM_PART, SWIZZLED, GEMM_OUT, ENC_K, ENC_V, WO_LAT, WO_T,
+ DEC_ZPART) = range(1, 13)
 WRITTEN = (ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SWIZZLED, GEMM_OUT, WO_LAT, WO_T)
 HIP_ERRORS = (1, 2, 98, 719)  # invalid value, out of memory, invalid device function, launch failure
 
@@ -342,6 +343,26 @@ def check_short_workspace_is_refused(L):
         assert L.flare_stub_launches() == 0, name
 
 
+def check_small_mixer_merges_in_the_decoder(L):
+    """The mixer lets the decoder merge small split sets of its encoder (no
+    merge launch for them: rearrangement, projections, synthesis encoder and
+    merge, encoder, decoder), the decoder reads exactly the split results that
+    encoder wrote, and large split sets keep their merge launch."""
+    for (B, H, M, N, D), fold in (((2, 4, 64, 1000, 16), True), ((8, 8, 64, 4096, 16), True),
+                                  ((32, 8, 128, 4096, 32), True), ((1, 8, 512, 1 << 20, 32), False)):
+        L.flare_stub_reset()
+        assert mix(L, B, N, H * D, H, M, wo=False) == OK, (B, H, M, N, D)
+        rs = ranges(L)
+        assert L.flare_stub_launches() == (6 if fold else 7), (B, H, M, N, D, L.flare_stub_launches())
+        zp = [x for x in rs if x[3] == DEC_ZPART]
+        assert bool(zp) == fold, (B, H, M, N, D, rs)
+        if fold:
+            enc_o = [x for x in rs if x[3] == ENC_PART_O]
+            enc_l = [x for x in rs if x[3] == ENC_PART_L]
+            assert zp[0][:2] == enc_o[-1][:2] and zp[1][:2] == enc_l[-1][:2], (zp, enc_o, enc_l)
+            assert zp[0][2] == enc_o[-1][2] + 1  # the launch right after that encoder
+
+
 def _overlap(a, b):
     return a[0] < b[0] + b[1] and b[0] < a[0] + a[1]
 
@@ -362,7 +383,7 @@ def workspace_carving(L, B, H, M, N, D):
         rs = ranges(L)
         inside = lambda x: WS <= x[0] and x[0] + x[1] <= WS + need
         for addr, nbytes, launch, tag in rs:
-            in_ws = tag in (ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SUM_PART, SWIZZLED, WO_LAT, WO_T)
+            in_ws = tag in (ENC_PART_O, ENC_PART_L, BWD_DQ, BWD_DZ, SUM_PART, SWIZZLED, WO_LAT, WO_T, DEC_ZPART)
             if name.startswith("mix"):
                 # projections and encoder inputs live in the workspace, except
                 # the output projection's result, which is the caller's

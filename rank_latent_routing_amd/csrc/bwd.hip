@@ -514,9 +514,13 @@ template <int D, bool ENC, int NW>
 __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_kernel(LatBwdParams p) {
   constexpr int SD = D / 16;
   constexpr int T = kLatBwdTile;
-  __shared__ __attribute__((aligned(16))) bf16 kt[T * D];
-  __shared__ __attribute__((aligned(16))) bf16 xt[T * D];
-  __shared__ __attribute__((aligned(16))) bf16x8 augt[T + 1];  // decode role: per token, and a zero slot
+  constexpr int NB = ENC ? 1 : 2;  // token tile buffers (the decode role double-buffers)
+  __shared__ __attribute__((aligned(16))) bf16 kt_s[NB * T * D];
+  __shared__ __attribute__((aligned(16))) bf16 xt_s[NB * T * D];
+  __shared__ __attribute__((aligned(16))) bf16x8 aug_s[NB * (T + 1)];  // decode role: per token, and a zero slot
+  const bf16* kt = kt_s;  // the buffer being computed
+  const bf16* xt = xt_s;
+  const bf16x8* augt = aug_s;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, c = lane & 31, i16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -658,35 +662,82 @@ __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_ker
     finish(1, sc1, dp1);
   };
 
-  // Token tiles t = s, s + S, ... of this split, staged through registers:
-  // the next tile's loads are in flight while the current one is computed.
-  constexpr int UNITS = T * D / 8;                           // 16-byte chunks per tensor
-  constexpr int UPT = (UNITS + 64 * NW - 1) / (64 * NW);     // per thread
+  constexpr int UNITS = T * D / 8;  // 16-byte chunks per tensor and tile
   const int64_t tiles = (p.N + T - 1) / T;
-  bf16x8 kv[UPT], xv[UPT], yv[UPT];
-  // decode role, held by the first thread of each token (chunk 0): the
-  // token's L / c and delta (read; or, when p.y is given, computed as dY . Y
-  // from the staged chunks once they have arrived)
-  float l2s[UPT], dls[UPT];
-  const bool self_delta = !ENC && p.y.data != nullptr;
-  const bf16* ybase = self_delta ? reinterpret_cast<const bf16*>(p.y.data) + b * p.y.sb + hd * p.y.sh : nullptr;
-  auto fetch = [&](int64_t t) {
-    const int64_t t0 = t * T;
+  if constexpr (ENC) {
+    // Token tiles t = s, s + S, ... of this split, staged through registers:
+    // the next tile's loads are in flight while the current one is computed.
+    constexpr int UPT = (UNITS + 64 * NW - 1) / (64 * NW);  // per thread
+    bf16x8 kv[UPT], xv[UPT];
+    auto fetch = [&](int64_t t) {
 #pragma unroll
-    for (int q = 0; q < UPT; ++q) {
-      const int u = tid + q * 64 * NW;
-      const int tok = u / (D / 8), dc = u % (D / 8);
-      const int64_t n = t0 + tok;
-      const bool valid = u < UNITS && n < p.N;
-      if (valid) {
-        kv[q] = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 8 * dc);
-        xv[q] = *reinterpret_cast<const bf16x8*>(xbase + n * p.x.sl + 8 * dc);
-      } else {
+      for (int q = 0; q < UPT; ++q) {
+        const int u = tid + q * 64 * NW;
+        const int tok = u / (D / 8), dc = u % (D / 8);
+        const int64_t n = t * T + tok;
+        if (u < UNITS && n < p.N) {
+          kv[q] = *reinterpret_cast<const bf16x8*>(kbase + n * p.k.sl + 8 * dc);
+          xv[q] = *reinterpret_cast<const bf16x8*>(xbase + n * p.x.sl + 8 * dc);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kv[q][j] = xv[q][j] = zero;
+          for (int j = 0; j < 8; ++j) kv[q][j] = xv[q][j] = zero;
+        }
       }
-      if constexpr (!ENC) {
-        if (self_delta) {
+    };
+    if (s < tiles) fetch(s);
+    for (int64_t t = s; t < tiles; t += p.S) {
+      __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+      for (int q = 0; q < UPT; ++q) {
+        const int u = tid + q * 64 * NW;
+        if (u < UNITS) {
+          const int pos = lat_chunk_pos<D>(u / (D / 8), u % (D / 8));
+          reinterpret_cast<bf16x8*>(kt_s)[pos] = kv[q];
+          reinterpret_cast<bf16x8*>(xt_s)[pos] = xv[q];
+        }
+      }
+      __syncthreads();
+      if (t + p.S < tiles) fetch(t + p.S);
+      const int rem = (int)min((int64_t)T, p.N - t * T);
+      if (rem < T)
+        tile(std::integral_constant<bool, true>(), rem);
+      else
+        tile(std::integral_constant<bool, false>(), rem);
+    }
+  } else {
+    // Decode role: two tile buffers and one barrier per tile.  The next
+    // tile's loads are in flight while the current one is computed; each
+    // wave then prepares its share and writes it into the other buffer as it
+    // finishes, while the other waves still compute.  The 2 UNITS units of a
+    // tile are spread over all threads: units below UNITS take a dY chunk
+    // (with its Y chunk when delta is computed here) and, for the token's
+    // first chunk, its delta; the rest take a K chunk and the token's
+    // normaliser.  Per token the two terms sit in the two halves of its
+    // 16-byte slot: L / c in bf16 0..2, delta in bf16 4..6.
+    constexpr int UPT = (2 * UNITS + 64 * NW - 1) / (64 * NW);
+    bf16x8 cv[UPT], yv[UPT];
+    float sv[UPT];
+    const bool self_delta = p.y.data != nullptr;
+    const bf16* ybase = self_delta ? reinterpret_cast<const bf16*>(p.y.data) + b * p.y.sb + hd * p.y.sh : nullptr;
+    auto fetch = [&](int64_t t) {
+#pragma unroll
+      for (int q = 0; q < UPT; ++q) {
+        // the side is uniform in the wave (UNITS is a multiple of 64)
+        const int w2 = wave * 64 + q * 64 * NW;
+        const bool xs = w2 < UNITS;
+        const int u = tid + q * 64 * NW - (xs ? 0 : UNITS);
+        const int tok = u / (D / 8), dc = u % (D / 8);
+        const int64_t n = t * T + tok;
+        const bool valid = w2 < 2 * UNITS && n < p.N;
+        const bf16* sbase = xs ? xbase : kbase;
+        const int64_t sl = xs ? p.x.sl : p.k.sl;
+        if (valid) {
+          cv[q] = *reinterpret_cast<const bf16x8*>(sbase + n * sl + 8 * dc);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) cv[q][j] = zero;
+        }
+        if (xs && self_delta) {
           if (valid) {
             yv[q] = *reinterpret_cast<const bf16x8*>(ybase + n * p.y.sl + 8 * dc);
           } else {
@@ -694,60 +745,69 @@ __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_ker
             for (int j = 0; j < 8; ++j) yv[q][j] = zero;
           }
         }
-        l2s[q] = pad_offset(p.c);
-        dls[q] = 0.f;
-        if (valid && dc == 0) {
-          l2s[q] = p.lse[(int64_t)bh * p.N + n] * kLog2e / p.c;
-          if (!self_delta) dls[q] = p.delta[(int64_t)bh * p.N + n];
+        sv[q] = 0.f;
+        if (!xs || !self_delta) {
+          const float* sp = xs ? p.delta : p.lse;
+          if (valid && dc == 0) sv[q] = sp[(int64_t)bh * p.N + n];
         }
       }
-    }
-  };
-  if constexpr (!ENC) {
-    if (tid == 0) augt[T] = bf16x8{};  // zero slot for the lanes of the second K half
-  }
-  if (s < tiles) fetch(s);
-  for (int64_t t = s; t < tiles; t += p.S) {
-    __syncthreads();  // every wave is done with the previous tile
+    };
+    auto stage = [&](int64_t t, int buf) {
 #pragma unroll
-    for (int q = 0; q < UPT; ++q) {
-      const int u = tid + q * 64 * NW;
-      const int tok = u / (D / 8), dc = u % (D / 8);
-      if constexpr (!ENC) {
-        if (self_delta) {
-          float part = 0.f;
+      for (int q = 0; q < UPT; ++q) {
+        const int w2 = wave * 64 + q * 64 * NW;
+        if (w2 >= 2 * UNITS) continue;
+        const bool xs = w2 < UNITS;
+        const int u = tid + q * 64 * NW - (xs ? 0 : UNITS);
+        const int tok = u / (D / 8), dc = u % (D / 8);
+        const int64_t n = t * T + tok;
+        const bool valid = n < p.N;
+        float v = sv[q];
+        if (xs && self_delta) {
+          // delta_n = dY_n . Y_n: the D / 8 chunks of a token sit in
+          // adjacent lanes of one wave
+          float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) part = fmaf((float)xv[q][j], (float)yv[q][j], part);
-          // the D / 8 chunks of a token sit in adjacent lanes of one wave
-          part += shfl_xor_f(part, 1);
-          if constexpr (D == 32) part += shfl_xor_f(part, 2);
-          dls[q] = part;
-          const int64_t n = t * T + tok;
-          if (u < UNITS && dc == 0 && n < p.N && p.delta_out && blockIdx.z == 0)
-            p.delta_out[(int64_t)bh * p.N + n] = part;
+          for (int j = 0; j < 8; j += 2) {
+            a0 = fmaf((float)cv[q][j], (float)yv[q][j], a0);
+            a1 = fmaf((float)cv[q][j + 1], (float)yv[q][j + 1], a1);
+          }
+          v = a0 + a1;
+          v += shfl_xor_f(v, 1);
+          if constexpr (D == 32) v += shfl_xor_f(v, 2);
+          if (dc == 0 && valid && p.delta_out && blockIdx.z == 0) p.delta_out[(int64_t)bh * p.N + n] = v;
         }
-      }
-      if (u < UNITS) {
+        if (!xs) v = valid ? v * kLog2e / p.c : pad_offset(p.c);  // tokens past the end: weight 0
         const int pos = lat_chunk_pos<D>(tok, dc);
-        reinterpret_cast<bf16x8*>(kt)[pos] = kv[q];
-        reinterpret_cast<bf16x8*>(xt)[pos] = xv[q];
-        if (!ENC && dc == 0) {
-          // per token: L_n / c and delta_n as three bf16 terms each (tokens
-          // past the end get a huge finite offset: weight 0)
+        reinterpret_cast<bf16x8*>((xs ? xt_s : kt_s) + buf * T * D)[pos] = cv[q];
+        if (dc == 0) {
           bf16x8 e = {};
-          split3_bf16(l2s[q], e, 0);
-          split3_bf16(dls[q], e, 4);
-          augt[tok] = e;
+          split3_bf16(v, e, 0);
+          const u32x4 eb = __builtin_bit_cast(u32x4, e);
+          reinterpret_cast<u32x2*>(aug_s + buf * (T + 1) + tok)[xs ? 1 : 0] = u32x2{eb[0], eb[1]};
         }
       }
+    };
+    if (tid == 0) aug_s[T] = aug_s[2 * T + 1] = bf16x8{};  // zero slots for the lanes of the second K half
+    if (s < tiles) {
+      fetch(s);
+      stage(s, 0);
     }
     __syncthreads();
-    if (t + p.S < tiles) fetch(t + p.S);
-    const int rem = (int)min((int64_t)T, p.N - t * T);
-    if (ENC && rem < T)
-      tile(std::integral_constant<bool, true>(), rem);
-    else
-      tile(std::integral_constant<bool, false>(), rem);
+    int cur = 0;
+    for (int64_t t = s; t < tiles; t += p.S) {
+      const bool more = t + p.S < tiles;
+      if (more) fetch(t + p.S);
+      kt = kt_s + cur * T * D;
+      xt = xt_s + cur * T * D;
+      augt = aug_s + cur * (T + 1);
+      tile(std::integral_constant<bool, false>(), T);
+      if (more) stage(t + p.S, cur ^ 1);
+      // this wave's LDS writes have landed; the loads stay in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+      barrier_keep_loads();
+      cur ^= 1;
+    }
   }
 
   // Partials of this split: accumulator row i of lane (h, c) is latent

@@ -116,6 +116,18 @@ constexpr int tok_bwd_waves() { return ENC ? 8 : 4; }
 // for either sign of the exponent scale c, so the row's weight is exactly 0.
 __device__ __forceinline__ float pad_offset(float c) { return c > 0.f ? 1e30f : -1e30f; }
 
+// In the encode role dP = dZ . V is reduced against delta_m = dZ . Z, and
+// when the encoder's weights are concentrated the two nearly cancel.  Below
+// kDzSplitBelowM latents dZ enters the product as bf16 high and low parts
+// (about 16 mantissa bits) and delta_m is formed from the fp32 dZ.  From
+// kDzSplitBelowM latents on dZ enters in bf16 alone and delta_m is formed
+// from the same bf16 values, so that dP - delta_m = bf16(dZ) . (V_n - Z_m)
+// carries only the rounding of dZ itself.  (A seeded sweep of sharp cases
+// put the single-part form within 10 % of the two-part error from 8 latents
+// on, and up to 55 % above it at 1 to 3 latents.)
+constexpr int kDzSplitBelowM = 32;
+__device__ __forceinline__ float dz_for_delta(float dz, bool split) { return split ? dz : (float)(bf16)dz; }
+
 // v as three bf16 terms, written to e[at], e[at + 1], e[at + 2], whose sum
 // carries v to about fp32 precision.
 __device__ __forceinline__ void split3_bf16(float v, bf16x8& e, int at) {
@@ -138,7 +150,7 @@ __device__ __forceinline__ void split3_bf16(float v, bf16x8& e, int at) {
 // latent, so this replaces a per-element LDS read of the row's normaliser
 // and delta by one 16-byte read per lane and chunk.
 
-template <int D, bool ENC>
+template <int D, bool ENC, bool DZS>
 __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(TokBwdParams p) {
   constexpr int NW = tok_bwd_waves<ENC>();
   constexpr int SD = D / 16;
@@ -155,17 +167,17 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
   bf16x8* qt_lds = w_lds + MC * SD * 64;
   bf16x8* wt_lds = qt_lds + MC * 2 * 64;           // encode role
   bf16x8* aug_lds = wt_lds + MC * 2 * 64;          // encode role: MC * 32 latents + a zero slot
-  bf16x8* wlo_lds = aug_lds + (MC * 32 + 1);        // encode role: dZ - bf16(dZ)
+  bf16x8* wlo_lds = aug_lds + (MC * 32 + 1);        // encode role, few latents: dZ - bf16(dZ)
+  constexpr bool dz_split = ENC && DZS;  // dZ as high and low parts (fewer than kDzSplitBelowM latents)
 
   stage_latent_block<D>(qv, b, hd, p.mb, MC, q_lds, qt_lds, tid, 64 * NW);
-  // In the encode role W = dZ is an fp32 gradient whose dP = dZ . V is then
-  // reduced against delta = dZ . Z: with concentrated weights the two nearly
-  // cancel, so dZ enters the product as bf16 high and low parts.
+  // In the encode role W = dZ is an fp32 gradient (its high and low bf16
+  // parts with few latents)
   stage_latent_block<D>(wv, b, hd, p.mb, MC, w_lds, ENC ? wt_lds : nullptr, tid, 64 * NW,
-                        ENC ? wlo_lds : nullptr);
+                        dz_split ? wlo_lds : nullptr);
   if constexpr (ENC) {
     // per latent m: L_m / c (base-2 normaliser over the exponent scale) and
-    // delta_m = dZ_m . Z_m, three bf16 terms each: (t1, t2, t3, 0, d1, d2, d3,
+    // delta_m = dZ_m . Z_m (dZ as it enters dP), three bf16 terms each: (t1, t2, t3, 0, d1, d2, d3,
     // 0).  Padded latents get a huge finite offset (weight exactly 0); the
     // slot after the last latent stays zero for the lanes of the second K half.
     for (int m = tid; m <= MC * 32; m += 64 * NW) {
@@ -178,7 +190,7 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
             float a, z;
             load_as_f32<1>(wv.data, wv.is_f32, b * wv.sb + hd * wv.sh + (int64_t)m * wv.sl + d, &a);
             load_as_f32<1>(zv.data, zv.is_f32, b * zv.sb + hd * zv.sh + (int64_t)m * zv.sl + d, &z);
-            dl = fmaf(a, z, dl);
+            dl = fmaf(dz_for_delta(a, dz_split), z, dl);
           }
         }
         split3_bf16(v, e, 0);
@@ -263,7 +275,7 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
         for (int sd = 0; sd < SD; ++sd) {
           qa[sd] = q_lds[(ch * SD + sd) * 64 + lane];
           wa[sd] = w_lds[(ch * SD + sd) * 64 + lane];
-          if constexpr (ENC) wl[sd] = wlo_lds[(ch * SD + sd) * 64 + lane];
+          if constexpr (dz_split) wl[sd] = wlo_lds[(ch * SD + sd) * 64 + lane];
         }
         bf16x8 as = {}, ad = {};
         if constexpr (ENC) {
@@ -279,7 +291,7 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
           for (int sd = 0; sd < SD; ++sd) {
             sc[tb] = mfma_32x32x16(qa[sd], kb[tb][sd], sc[tb]);
             dp[tb] = mfma_32x32x16(wa[sd], xb[tb][sd], dp[tb]);
-            if constexpr (ENC) dp[tb] = mfma_32x32x16(wl[sd], xb[tb][sd], dp[tb]);
+            if constexpr (dz_split) dp[tb] = mfma_32x32x16(wl[sd], xb[tb][sd], dp[tb]);
           }
           if constexpr (ENC) {
             sc[tb] = mfma_32x32x16(as, bneg, sc[tb]);
@@ -339,7 +351,7 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
 // the encoder.  dK is written once, with no second pass reading it back.
 constexpr int kTokPairWaves = 8;
 
-template <int D>
+template <int D, bool DZS>
 __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPairParams p) {
   constexpr int NW = kTokPairWaves;
   constexpr int SD = D / 16;
@@ -355,13 +367,13 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
   bf16x8* qt_lds = dz_lds + MC * SD * 64;           // A of dK^T += Q^T dS^T
   bf16x8* dzt_lds = qt_lds + MC * 2 * 64;           // A of dV^T += dZ^T P_e^T
   bf16x8* aug_lds = dzt_lds + MC * 2 * 64;          // per latent L_m / c and delta_m; zero slot
-  bf16x8* dzlo_lds = aug_lds + (MC * 32 + 1);       // dZ - bf16(dZ), the low part of dP_e's A
+  bf16x8* dzlo_lds = aug_lds + (MC * 32 + 1);       // few latents: dZ - bf16(dZ), the low part of dP_e's A
+  constexpr bool dz_split = DZS;  // dZ as high and low parts (fewer than kDzSplitBelowM latents)
 
   stage_latent_block<D>(p.q, b, hd, p.M, MC, q_lds, qt_lds, tid, 64 * NW);
   stage_latent_block<D>(p.z, b, hd, p.M, MC, z_lds, nullptr, tid, 64 * NW);
-  // dZ enters dP_e = dZ . V as bf16 high and low parts (dP_e nearly cancels
-  // against delta_m when the encoder's weights are concentrated)
-  stage_latent_block<D>(p.dz, b, hd, p.M, MC, dz_lds, dzt_lds, tid, 64 * NW, dzlo_lds);
+  // dZ enters dP_e = dZ . V in bf16 (as high and low parts with few latents)
+  stage_latent_block<D>(p.dz, b, hd, p.M, MC, dz_lds, dzt_lds, tid, 64 * NW, dz_split ? dzlo_lds : nullptr);
   for (int m = tid; m <= MC * 32; m += 64 * NW) {
     bf16x8 e = {};
     if (m < MC * 32) {
@@ -372,7 +384,7 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
           float a, z;
           load_as_f32<1>(p.dz.data, p.dz.is_f32, b * p.dz.sb + hd * p.dz.sh + (int64_t)m * p.dz.sl + d, &a);
           load_as_f32<1>(p.z.data, p.z.is_f32, b * p.z.sb + hd * p.z.sh + (int64_t)m * p.z.sl + d, &z);
-          dl = fmaf(a, z, dl);
+          dl = fmaf(dz_for_delta(a, dz_split), z, dl);
         }
       }
       split3_bf16(v, e, 0);
@@ -447,7 +459,7 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
         sc = mfma_32x32x16(q_lds[(ch * SD + sd) * 64 + lane], kb[sd], sc);
         dpd = mfma_32x32x16(z_lds[(ch * SD + sd) * 64 + lane], gb[sd], dpd);
         dpe = mfma_32x32x16(dz_lds[(ch * SD + sd) * 64 + lane], vb[sd], dpe);
-        dpe = mfma_32x32x16(dzlo_lds[(ch * SD + sd) * 64 + lane], vb[sd], dpe);
+        if constexpr (dz_split) dpe = mfma_32x32x16(dzlo_lds[(ch * SD + sd) * 64 + lane], vb[sd], dpe);
       }
       // the encoder's per-latent normaliser and delta as one more K step
       const u32x4 e = __builtin_bit_cast(u32x4, aug_lds[h == 0 ? 32 * ch + c : MC * 32]);
@@ -510,7 +522,7 @@ __device__ __forceinline__ int lat_chunk_pos(int token, int dc) {
 // per unit, each tile's barrier left its SIMDs idle.  The decoder role needs
 // 199 VGPRs and keeps 8 waves at M = 256 (4-wave workgroups, two per unit,
 // timed slower).
-template <int D, bool ENC, int NW>
+template <int D, bool ENC, int NW, bool DZS = false>
 __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_kernel(LatBwdParams p) {
   constexpr int SD = D / 16;
   constexpr int T = kLatBwdTile;
@@ -527,6 +539,7 @@ __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_ker
   const int s = blockIdx.x, bh = blockIdx.y, b = bh / p.H, hd = bh - b * p.H;
   const int lat0 = blockIdx.z * 32 * NW;
   const int m_lane = lat0 + wave * 32 + c;
+  constexpr bool dz_split = ENC && DZS;  // dZ as high and low parts (fewer than kDzSplitBelowM latents)
 
   // B operands of the two products against this lane's latent: Q and W
   bf16x8 qop[SD], wop[SD], wlo[SD];
@@ -543,19 +556,19 @@ __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_ker
         float zv[8];
         load_as_f32<8>(p.z.data, p.z.is_f32, b * p.z.sb + hd * p.z.sh + (int64_t)m_lane * p.z.sl + 16 * sd + 8 * h, zv);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dpart = fmaf(wv[j], zv[j], dpart);
+        for (int j = 0; j < 8; ++j) dpart = fmaf(dz_for_delta(wv[j], dz_split), zv[j], dpart);
       }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       qop[sd][j] = (bf16)qv[j];
       wop[sd][j] = (bf16)wv[j];
-      // encode role: W = dZ also as its bf16 rounding residual (dP = dZ . V
-      // nearly cancels against delta_m when the weights are concentrated)
+      // encode role with few latents: W = dZ also as its bf16 rounding residual
       wlo[sd][j] = (bf16)(wv[j] - (float)wop[sd][j]);
     }
   }
   // encode role: this lane's latent's base-2 normaliser and delta_m = dZ . Z
+  // (dZ as it enters dP)
   float l2m = INFINITY, dlm = 0.f;
   if constexpr (ENC) {
     dlm = dpart + shfl_xor_f(dpart, 32);
@@ -590,7 +603,7 @@ __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_ker
         const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xt + slot);
         sc = mfma_32x32x16(ka, qop[sd], sc);
         dp = mfma_32x32x16(xa, wop[sd], dp);
-        if constexpr (ENC) dp = mfma_32x32x16(xa, wlo[sd], dp);
+        if constexpr (dz_split) dp = mfma_32x32x16(xa, wlo[sd], dp);
       }
       if constexpr (!ENC) {
         const u32x4 e = __builtin_bit_cast(u32x4, augt[h == 0 ? 32 * qt + c : T]);
@@ -868,10 +881,11 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict
 
 // ---------------------------------------------------------------- launchers
 
-static size_t tok_bwd_lds(int M, int D, bool enc) {
+static size_t tok_bwd_lds(int M, int D, bool enc, bool dz_split) {
   const int MC = (M + 31) / 32;
   size_t bytes = (size_t)MC * (D / 16) * 64 * 16 * 2 + (size_t)MC * 2 * 64 * 16;
-  if (enc) bytes += (size_t)MC * 2 * 64 * 16 + (size_t)(MC * 32 + 1) * 16 + (size_t)MC * (D / 16) * 64 * 16;
+  if (enc) bytes += (size_t)MC * 2 * 64 * 16 + (size_t)(MC * 32 + 1) * 16;
+  if (enc && dz_split) bytes += (size_t)MC * (D / 16) * 64 * 16;
   return bytes;
 }
 
@@ -883,9 +897,8 @@ static hipError_t allow_lds_bwd(K kernel, size_t bytes) {
 
 hipError_t launch_tok_bwd(const TokBwdParams& p, int D, int B, bool encode_role, hipStream_t st) {
   dim3 grid((unsigned)p.blocks_per_head, B * p.H);
-  // The encode role stages five latent blocks: above 256 latents they would
-  // exceed one CU's LDS, so it runs per block of 256, later blocks adding
-  // into dK and dV.
+  // The encode role stages four latent blocks (five with few latents): it
+  // runs per block of 256 latents, later blocks adding into dK and dV.
   const int step = encode_role ? 256 : p.M;
   hipError_t e = hipSuccess;
   for (int m0 = 0; m0 < p.M; m0 += step) {
@@ -894,14 +907,15 @@ hipError_t launch_tok_bwd(const TokBwdParams& p, int D, int B, bool encode_role,
     q.mb = std::min(step, p.M - m0);
     q.accumulate = m0 > 0 ? 1 : p.accumulate;
     q.accumulate_v = m0 > 0 ? 1 : 0;
-    const size_t lds = tok_bwd_lds(q.mb, D, encode_role);
-#define FLARE_TOK(DD, EE)                                                                  \
-  if ((e = allow_lds_bwd(tok_bwd_kernel<DD, EE>, lds)) != hipSuccess) return e;              \
-  hipLaunchKernelGGL((tok_bwd_kernel<DD, EE>), grid, dim3(64 * tok_bwd_waves<EE>()), lds, st, q)
+    const size_t lds = tok_bwd_lds(q.mb, D, encode_role, p.M < kDzSplitBelowM);
+#define FLARE_TOK(DD, EE, SS)                                                              \
+  if ((e = allow_lds_bwd(tok_bwd_kernel<DD, EE, SS>, lds)) != hipSuccess) return e;          \
+  hipLaunchKernelGGL((tok_bwd_kernel<DD, EE, SS>), grid, dim3(64 * tok_bwd_waves<EE>()), lds, st, q)
+    const bool split = p.M < kDzSplitBelowM;
     if (D == 32) {
-      if (encode_role) { FLARE_TOK(32, true); } else { FLARE_TOK(32, false); }
+      if (!encode_role) { FLARE_TOK(32, false, false); } else if (split) { FLARE_TOK(32, true, true); } else { FLARE_TOK(32, true, false); }
     } else {
-      if (encode_role) { FLARE_TOK(16, true); } else { FLARE_TOK(16, false); }
+      if (!encode_role) { FLARE_TOK(16, false, false); } else if (split) { FLARE_TOK(16, true, true); } else { FLARE_TOK(16, true, false); }
     }
 #undef FLARE_TOK
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -911,7 +925,8 @@ hipError_t launch_tok_bwd(const TokBwdParams& p, int D, int B, bool encode_role,
 
 static size_t tok_pair_lds(int M, int D) {
   const int MC = (M + 31) / 32;
-  return (size_t)MC * (D / 16) * 64 * 16 * 4 + (size_t)MC * 2 * 64 * 16 * 2 + (size_t)(MC * 32 + 1) * 16;
+  return (size_t)MC * (D / 16) * 64 * 16 * (M < kDzSplitBelowM ? 4 : 3) + (size_t)MC * 2 * 64 * 16 * 2 +
+         (size_t)(MC * 32 + 1) * 16;
 }
 
 hipError_t launch_tok_pair(const TokPairParams& p, int D, int B, hipStream_t st) {
@@ -919,13 +934,16 @@ hipError_t launch_tok_pair(const TokPairParams& p, int D, int B, hipStream_t st)
   dim3 grid((unsigned)p.blocks_per_head, B * p.H);
   const size_t lds = tok_pair_lds(p.M, D);
   hipError_t e;
+#define FLARE_PAIR(DD, SS)                                                                  \
+  if ((e = allow_lds_bwd(tok_pair_kernel<DD, SS>, lds)) != hipSuccess) return e;              \
+  hipLaunchKernelGGL((tok_pair_kernel<DD, SS>), grid, dim3(64 * kTokPairWaves), lds, st, p)
+  const bool split = p.M < kDzSplitBelowM;
   if (D == 32) {
-    if ((e = allow_lds_bwd(tok_pair_kernel<32>, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((tok_pair_kernel<32>), grid, dim3(64 * kTokPairWaves), lds, st, p);
+    if (split) { FLARE_PAIR(32, true); } else { FLARE_PAIR(32, false); }
   } else {
-    if ((e = allow_lds_bwd(tok_pair_kernel<16>, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL((tok_pair_kernel<16>), grid, dim3(64 * kTokPairWaves), lds, st, p);
+    if (split) { FLARE_PAIR(16, true); } else { FLARE_PAIR(16, false); }
   }
+#undef FLARE_PAIR
   return hipGetLastError();
 }
 
@@ -936,10 +954,15 @@ hipError_t launch_lat_bwd(const LatBwdParams& p, int D, int B, bool encode_role,
 #define FLARE_LAT(DD, EE, WW) hipLaunchKernelGGL((lat_bwd_kernel<DD, EE, WW>), grid, dim3(64 * WW), 0, st, p)
 #define FLARE_LAT_W(DD, EE) \
   if (NW == 2) FLARE_LAT(DD, EE, 2); else if (NW == 4) FLARE_LAT(DD, EE, 4); else FLARE_LAT(DD, EE, 8)
+  // with fewer than kDzSplitBelowM latents the encode role takes dZ in two
+  // parts (and 2-wave workgroups)
+  const bool split = encode_role && p.M < kDzSplitBelowM;
   if (D == 32) {
-    if (encode_role) { FLARE_LAT_W(32, true); } else { FLARE_LAT_W(32, false); }
+    if (split) { hipLaunchKernelGGL((lat_bwd_kernel<32, true, 2, true>), grid, dim3(128), 0, st, p); }
+    else if (encode_role) { FLARE_LAT_W(32, true); } else { FLARE_LAT_W(32, false); }
   } else {
-    if (encode_role) { FLARE_LAT_W(16, true); } else { FLARE_LAT_W(16, false); }
+    if (split) { hipLaunchKernelGGL((lat_bwd_kernel<16, true, 2, true>), grid, dim3(128), 0, st, p); }
+    else if (encode_role) { FLARE_LAT_W(16, true); } else { FLARE_LAT_W(16, false); }
   }
 #undef FLARE_LAT_W
 #undef FLARE_LAT

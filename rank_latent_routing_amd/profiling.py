@@ -475,15 +475,15 @@ BWD_CMDS = ["export TMPDIR=/tmp"] + [
 # one-call pair backward with fp32 dK, dV; the two-call chain; the one-call form with bf16 dK, dV.
 # Each kernel's dispatches, in order, split into the forms it runs in.
 BWD_GROUPS = [
-    ("tok_pair_kernel<32>", 0, 5, "token pass, both roles (`tok_pair_kernel<32>`, one-call backward, fp32 dK, dV)"),
-    ("tok_pair_kernel<32>", 5, 10, "the same with bf16 dK, dV"),
-    ("lat_bwd_kernel<32, false, 8>", 0, 5,
-     "latent pass, decoder role, computing delta from Y (`lat_bwd_kernel<32, false, 8>`, one-call)"),
-    ("lat_bwd_kernel<32, false, 8>", 5, 10, "latent pass, decoder role (`lat_bwd_kernel<32, false, 8>`, two-call chain)"),
-    ("lat_bwd_kernel<32, false, 8>", 10, 15, "the one-call form's latent pass again, in the bf16 dK, dV calls"),
-    ("lat_bwd_kernel<32, true, 4>", 0, 15, "latent pass, encoder role (`lat_bwd_kernel<32, true, 4>`, all forms)"),
-    ("tok_bwd_kernel<32, false>", 0, 5, "token pass, decoder role (`tok_bwd_kernel<32, false>`, two-call chain)"),
-    ("tok_bwd_kernel<32, true>", 0, 5, "token pass, encoder role (`tok_bwd_kernel<32, true>`, two-call chain)"),
+    ("tok_pair_kernel<32, false>", 0, 5, "token pass, both roles (`tok_pair_kernel<32, false>`, one-call backward, fp32 dK, dV)"),
+    ("tok_pair_kernel<32, false>", 5, 10, "the same with bf16 dK, dV"),
+    ("lat_bwd_kernel<32, false, 8, false>", 0, 5,
+     "latent pass, decoder role, computing delta from Y (`lat_bwd_kernel<32, false, 8, false>`, one-call)"),
+    ("lat_bwd_kernel<32, false, 8, false>", 5, 10, "latent pass, decoder role (`lat_bwd_kernel<32, false, 8, false>`, two-call chain)"),
+    ("lat_bwd_kernel<32, false, 8, false>", 10, 15, "the one-call form's latent pass again, in the bf16 dK, dV calls"),
+    ("lat_bwd_kernel<32, true, 4, false>", 0, 15, "latent pass, encoder role (`lat_bwd_kernel<32, true, 4, false>`, all forms)"),
+    ("tok_bwd_kernel<32, false, false>", 0, 5, "token pass, decoder role (`tok_bwd_kernel<32, false, false>`, two-call chain)"),
+    ("tok_bwd_kernel<32, true, false>", 0, 5, "token pass, encoder role (`tok_bwd_kernel<32, true, false>`, two-call chain)"),
 ]
 
 
@@ -650,18 +650,18 @@ def write_traffic_md(out, fetch_csv, write_csv, f_read, f_write, copy_kib, step_
         ("decode_bf16_kernel<32>", None, 2 * tok * D * 2, "K read, Y written: 8 x 1048576 x 32 x 2 B each"),
     ]
     rows_bwd = [
-        ("lat_bwd_kernel<32, false, 8>", (0, 5), " (one call)", 3 * tok * D * 2 + 2 * tok * 4,
+        ("lat_bwd_kernel<32, false, 8, false>", (0, 5), " (one call)", 3 * tok * D * 2 + 2 * tok * 4,
          "K, dY, Y read in bf16, lse read, delta written"),
-        ("lat_bwd_kernel<32, false, 8>", (5, 10), " (two calls)", 2 * tok * D * 2 + 2 * tok * 4,
+        ("lat_bwd_kernel<32, false, 8, false>", (5, 10), " (two calls)", 2 * tok * D * 2 + 2 * tok * 4,
          "K, dY read in bf16, lse and delta read"),
-        ("lat_bwd_kernel<32, true, 4>", None, "", 2 * tok * D * 2, "K, V read in bf16 once; each of the two 128-latent blocks of a split reads them"),
-        ("tok_pair_kernel<32>", (0, 5), " (fp32 gradients)", 3 * tok * D * 2 + 2 * tok * 4 + 2 * tok * D * 4,
+        ("lat_bwd_kernel<32, true, 4, false>", None, "", 2 * tok * D * 2, "K, V read in bf16 once; each of the two 128-latent blocks of a split reads them"),
+        ("tok_pair_kernel<32, false>", (0, 5), " (fp32 gradients)", 3 * tok * D * 2 + 2 * tok * 4 + 2 * tok * D * 4,
          "K, V, dY read in bf16, lse and delta read, dK and dV written in fp32"),
-        ("tok_pair_kernel<32>", (5, 10), " (bf16 gradients)", 3 * tok * D * 2 + 2 * tok * 4 + 2 * tok * D * 2,
+        ("tok_pair_kernel<32, false>", (5, 10), " (bf16 gradients)", 3 * tok * D * 2 + 2 * tok * 4 + 2 * tok * D * 2,
          "the same with dK and dV written in bf16"),
-        ("tok_bwd_kernel<32, false>", None, "", 3 * tok * D * 2 + tok * D * 4 + 2 * tok * 4,
+        ("tok_bwd_kernel<32, false, false>", None, "", 3 * tok * D * 2 + tok * D * 4 + 2 * tok * 4,
          "K, dY, Y read in bf16, dK written in fp32, lse read and delta written"),
-        ("tok_bwd_kernel<32, true>", None, "", 2 * tok * D * 2 + 3 * tok * D * 4,
+        ("tok_bwd_kernel<32, true, false>", None, "", 2 * tok * D * 2 + 3 * tok * D * 4,
          "K, V read in bf16, dK read and written, dV written, all fp32"),
     ]
 

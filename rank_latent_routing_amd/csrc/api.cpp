@@ -245,10 +245,12 @@ flare_status project_impl(const void* X, const void* const* W, void* const* Y, i
     void* wt = reinterpret_cast<char*>(ws) + i * align_up((size_t)Cin * Cout * 2);
     sp.w[i] = W[i];
     sp.wsw[i] = wt;
+    gp.w[i] = W[i];
     gp.wt[i] = wt;
     gp.y[i] = Y[i];
   }
-  if (launch_swizzle_weights(sp, n_proj, st) != hipSuccess) return FLARE_E_HIP;
+  if (!gemm_preloads(R, n_proj, Cin, Cout) && launch_swizzle_weights(sp, n_proj, st) != hipSuccess)
+    return FLARE_E_HIP;
   return hip_status(launch_gemm_bf16(gp, st));
 }
 

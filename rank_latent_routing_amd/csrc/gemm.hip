@@ -246,19 +246,20 @@ __global__ __launch_bounds__(64 * kGemmWaves, 4) void gemm_bf16_kernel(GemmParam
 }
 
 // Weight sets of at most kGemmPreloadBytes (all blocks of every projection,
-// e.g. four 128 x 128 weights): every block is loaded into LDS once at the
-// start and the blocks are then computed with no further waits.  In the
-// streamed kernel above, each block's wait for its weights also waits for the
-// output stores issued before that load (one counter covers both), so with
-// short blocks the store latency sets the pace.
-constexpr int kGemmPreloadBytes = 128 * 1024;
-
+// e.g. four 128 x 128 weights): every block is laid out in LDS once at the
+// start, from the row-major weights, and the blocks are then computed with no
+// further waits.  In the streamed kernel above, each block's wait for its
+// weights also waits for the output stores issued before that load (one
+// counter covers both), so with short blocks the store latency sets the pace.
+// A thread takes 8 x 8 tiles of a weight (eight inputs of one k-step and
+// lane group, eight consecutive output columns), transposes each in
+// registers and writes it as eight 16-byte operand slots, in the order
+// swizzle_weights_kernel gives the streamed kernel.
 template <int CIN, bool PAIR>
 __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_preload_kernel(GemmParams p) {
   constexpr int NW = kGemmWaves;
   constexpr int KS = CIN / 32;
   constexpr int BLK = KS * 2 * 512;  // bf16 elements of one 32-column block
-  constexpr int OPS = BLK / 512;     // 1 KB loads per block
   extern __shared__ __attribute__((aligned(16))) bf16 wl[];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
@@ -268,15 +269,27 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_preload_kernel(G
   const int pairs = p.Cout / 32;
   const int nblk = p.n_proj * pairs;
 
-  // every block of every projection, 1 KB per load, spread over the waves
-  for (int op = wave; op < nblk * OPS; op += NW) {
-    const int b = op / OPS, o = op - b * OPS;
-    const int pr = b / pairs, pb = b - pr * pairs;
-    const bf16* src = reinterpret_cast<const bf16*>(p.wt[pr]) + (int64_t)pb * BLK;
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(src), (short)0, BLK * (int)sizeof(bf16), kBufferFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(wl + (int64_t)b * BLK + o * 512), 16, lane * 16,
-                                             o * 1024, 0, 0);
+  // every block of every projection
+  const int cchunks = p.Cout / 8;              // 8-column chunks of a weight row
+  const int tiles = (CIN / 8) * cchunks;        // 8 x 8 tiles per weight
+  for (int u = tid; u < p.n_proj * tiles; u += 64 * NW) {
+    const int pr = u / tiles, t8 = u - pr * tiles;
+    const int rg = t8 / cchunks, cc = t8 - rg * cchunks;  // rows 8 rg .. +7, columns 8 cc .. +7
+    const bf16* src = reinterpret_cast<const bf16*>(p.w[pr]) + (int64_t)(8 * rg) * p.Cout + 8 * cc;
+    bf16x8 rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rows[j] = *reinterpret_cast<const bf16x8*>(src + (int64_t)j * p.Cout);
+    // column 8 cc + e sits in block (pr, cc / 4), k-step rg / 4, tile e / 4,
+    // lane 16 (rg % 4) + 4 (cc % 4) + e % 4; row 8 rg + j is element j
+    bf16* blk = wl + (int64_t)(pr * pairs + cc / 4) * BLK;
+    const int ks = rg >> 2, lg = 16 * (rg & 3) + 4 * (cc & 3);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bf16x8 col;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) col[j] = rows[j][e];
+      *reinterpret_cast<bf16x8*>(blk + ((ks * 2 + (e >> 2)) * 64 + lg + (e & 3)) * 8) = col;
+    }
   }
   bf16x8 xb[KS];
 #pragma unroll
@@ -298,8 +311,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 2) void gemm_bf16_preload_kernel(G
       row_off = rr * p.Cout;
     }
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-  barrier_keep_loads();
+  __syncthreads();  // the weight blocks are in LDS
 
   bf16x8 carry = {};
   for (int b = 0; b < nblk; ++b) {
@@ -354,7 +366,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t st) {
   // number of 32-column blocks
   const bool pair = !p.head_major && (p.Cout / 32) % 2 == 0;
   const size_t wbytes = (size_t)p.n_proj * p.Cin * p.Cout * sizeof(bf16);
-  if (rb == 1 && wbytes <= (size_t)kGemmPreloadBytes) {
+  if (gemm_preloads(p.R, p.n_proj, p.Cin, p.Cout)) {
     dim3 pgrid((unsigned)((p.R + 16 * kGemmWaves - 1) / (16 * kGemmWaves)));
 #define FLARE_GEMM_PRE(C)                                                                                  \
   {                                                                                                        \

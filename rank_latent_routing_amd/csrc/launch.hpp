@@ -152,7 +152,8 @@ hipError_t launch_decode_wo(const DecodeWoParams& p, int B, const void* w_o, hip
 
 struct GemmParams {
   const void* x;      // [R, Cin] bf16 row-major
-  const void* wt[5];  // transposed weights [Cout, Cin] bf16
+  const void* w[5];   // weights [Cin, Cout] bf16 row-major (read by the preloading kernel)
+  const void* wt[5];  // the weights in operand order (launch_swizzle_weights; the streaming kernel)
   void* y[5];         // outputs
   int n_proj;
   int64_t R;
@@ -203,5 +204,16 @@ struct SwizzleParams {
 };
 hipError_t launch_swizzle_weights(const SwizzleParams& p, int n, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
+
+// The projection kernel's two forms.  With one 16-row tile per wave (fewer
+// than 512 workgroups of two) and at most kGemmPreloadBytes of weights, each
+// workgroup lays out every weight block in LDS itself, from the row-major
+// weights, before computing.  Otherwise the weights are first rearranged into
+// operand order in the workspace (launch_swizzle_weights) and streamed.
+constexpr int64_t kGemmPreloadBytes = 128 * 1024;
+inline bool gemm_preloads(int64_t R, int n_proj, int Cin, int Cout) {
+  const bool one_tile = (R + 16 * 2 * 8 - 1) / (16 * 2 * 8) < 512;
+  return one_tile && (int64_t)n_proj * Cin * Cout * 2 <= kGemmPreloadBytes;
+}
 
 }  // namespace flare

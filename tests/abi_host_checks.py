@@ -345,15 +345,22 @@ def check_short_workspace_is_refused(L):
 
 def check_small_mixer_merges_in_the_decoder(L):
     """The mixer lets the decoder merge small split sets of its encoder (no
-    merge launch for them: rearrangement, projections, synthesis encoder and
-    merge, encoder, decoder), the decoder reads exactly the split results that
-    encoder wrote, and large split sets keep their merge launch."""
+    merge launch for them: weight rearrangement, projections, synthesis
+    encoder and merge, encoder, decoder), the decoder reads exactly the split
+    results that encoder wrote, and large split sets keep their merge launch.
+    Small weight sets on few rows need no rearrangement launch: the
+    projection kernel lays them out itself."""
     for (B, H, M, N, D), fold in (((2, 4, 64, 1000, 16), True), ((8, 8, 64, 4096, 16), True),
                                   ((32, 8, 128, 4096, 32), True), ((1, 8, 512, 1 << 20, 32), False)):
         L.flare_stub_reset()
         assert mix(L, B, N, H * D, H, M, wo=False) == OK, (B, H, M, N, D)
         rs = ranges(L)
-        assert L.flare_stub_launches() == (6 if fold else 7), (B, H, M, N, D, L.flare_stub_launches())
+        C = H * D
+        preload = (B * N + 255) // 256 < 512 and 4 * C * C * 2 <= 128 * 1024
+        assert preload == (C <= 128), (B, H, M, N, D)
+        assert bool([x for x in rs if x[3] == SWIZZLED]) != preload, (B, H, M, N, D)
+        expected = (6 if fold else 7) - (1 if preload else 0)
+        assert L.flare_stub_launches() == expected, (B, H, M, N, D, L.flare_stub_launches())
         zp = [x for x in rs if x[3] == DEC_ZPART]
         assert bool(zp) == fold, (B, H, M, N, D, rs)
         if fold:

@@ -261,6 +261,14 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
         if (h == 0 && valid) p.delta[(int64_t)bh * p.N + n] = dln[tb];
       }
     }
+    // decode role: dP - delta_n, with the token's -delta_n starting every
+    // chunk's dP product
+    f32x16 ddneg[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ddneg[tb][i] = -dln[tb];
+    }
 
     f32x16 dk[2], dv[2];
 #pragma unroll
@@ -286,7 +294,10 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           sc[tb] = zero16();
-          dp[tb] = zero16();
+          if constexpr (ENC)
+            dp[tb] = zero16();
+          else
+            dp[tb] = ddneg[tb];
 #pragma unroll
           for (int sd = 0; sd < SD; ++sd) {
             sc[tb] = mfma_32x32x16(qa[sd], kb[tb][sd], sc[tb]);
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
             ds[i] = pw[i] * dp[tb][i];
           } else {
             pw[i] = exp2_fast(sc[tb][i] * cs - l2n[tb]);
-            ds[i] = pw[i] * (dp[tb][i] - dln[tb]);
+            ds[i] = pw[i] * dp[tb][i];
           }
         }
 #pragma unroll
@@ -444,7 +455,10 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
       gb[sd] = ng[sd];
     }
     const float l2d = nl2 * kLog2e;
-    const float dd = ndd;
+    // dP_d - delta_n: the token's -delta_n starts every chunk's dP_d product
+    f32x16 ddneg;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ddneg[i] = -ndd;
     unsigned jn = 0;
     if (lane == 0) jn = atomicAdd(&next_grp, 1u);
     nbase = grp(__builtin_amdgcn_readfirstlane(jn));
@@ -453,7 +467,7 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
     f32x16 dk = zero16(), dv = zero16();
     for (int ch = 0; ch < MC; ++ch) {
       // element i of a tile: latent 32ch + 8(i/4) + 4h + i%4 of token n
-      f32x16 sc = zero16(), dpd = zero16(), dpe = zero16();
+      f32x16 sc = zero16(), dpd = ddneg, dpe = zero16();
 #pragma unroll
       for (int sd = 0; sd < SD; ++sd) {
         sc = mfma_32x32x16(q_lds[(ch * SD + sd) * 64 + lane], kb[sd], sc);
@@ -470,7 +484,7 @@ __global__ __launch_bounds__(64 * kTokPairWaves, 2) void tok_pair_kernel(TokPair
       for (int i = 0; i < 16; ++i) {
         const float pd = exp2_fast(sc[i] * cs - l2d);
         pe[i] = exp2_fast(se[i] * cs);
-        ds[i] = fmaf(pe[i], dpe[i], pd * (dpd[i] - dd));
+        ds[i] = fmaf(pe[i], dpe[i], pd * dpd[i]);
       }
 #pragma unroll
       for (int ug = 0; ug < 2; ++ug) {

@@ -597,6 +597,12 @@ __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_ker
   // B operand of the extra K step: -1 in K rows 0..2 (lane half 0), else 0
   bf16x8 bneg = {};
   if (h == 0) bneg[0] = bneg[1] = bneg[2] = (bf16)-1.0f;
+  // encode role: delta_m as one more K step on dP (B: its three bf16 terms in
+  // K rows 0..2 of the latent's column; A: -1 there for every token row)
+  bf16x8 dlmop = {};
+  if constexpr (ENC) {
+    if (h == 0) split3_bf16(dlm, dlmop, 0);
+  }
 
   // The staged tile's products for this wave's 32 latents.  RAGGED (encode
   // role, last tile only) gives tokens past the end weight 0 through an
@@ -619,6 +625,7 @@ __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_ker
         dp = mfma_32x32x16(xa, wop[sd], dp);
         if constexpr (dz_split) dp = mfma_32x32x16(xa, wlo[sd], dp);
       }
+      if constexpr (ENC) dp = mfma_32x32x16(bneg, dlmop, dp);
       if constexpr (!ENC) {
         const u32x4 e = __builtin_bit_cast(u32x4, augt[h == 0 ? 32 * qt + c : T]);
         sc = mfma_32x32x16(__builtin_bit_cast(bf16x8, u32x4{e[0], e[1], 0u, 0u}), bneg, sc);
@@ -635,7 +642,7 @@ __global__ __launch_bounds__(64 * NW, (ENC && NW == 4) ? 3 : 2) void lat_bwd_ker
           const int row = 32 * qt + 8 * (i >> 2) + 4 * h + (i & 3);
           const float l2 = (!RAGGED || row < rem) ? l2m : INFINITY;
           pw[i] = exp2_fast(sc[i] * cs - l2);
-          ds[i] = pw[i] * (dp[i] - dlm);
+          ds[i] = pw[i] * dp[i];
         } else {
           pw[i] = exp2_fast(sc[i] * cs);
           ds[i] = pw[i] * dp[i];

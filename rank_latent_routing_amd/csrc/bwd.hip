@@ -261,14 +261,6 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
         if (h == 0 && valid) p.delta[(int64_t)bh * p.N + n] = dln[tb];
       }
     }
-    // decode role: dP - delta_n, with the token's -delta_n starting every
-    // chunk's dP product
-    f32x16 ddneg[2];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ddneg[tb][i] = -dln[tb];
-    }
 
     f32x16 dk[2], dv[2];
 #pragma unroll
@@ -294,10 +286,7 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           sc[tb] = zero16();
-          if constexpr (ENC)
-            dp[tb] = zero16();
-          else
-            dp[tb] = ddneg[tb];
+          dp[tb] = zero16();
 #pragma unroll
           for (int sd = 0; sd < SD; ++sd) {
             sc[tb] = mfma_32x32x16(qa[sd], kb[tb][sd], sc[tb]);
@@ -320,7 +309,7 @@ __global__ __launch_bounds__(64 * tok_bwd_waves<ENC>(), 2) void tok_bwd_kernel(T
             ds[i] = pw[i] * dp[tb][i];
           } else {
             pw[i] = exp2_fast(sc[tb][i] * cs - l2n[tb]);
-            ds[i] = pw[i] * dp[tb][i];
+            ds[i] = pw[i] * (dp[tb][i] - dln[tb]);
           }
         }
 #pragma unroll

@@ -30,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -143,11 +144,20 @@ class ClockSampler:
         return sum(ghz) / len(ghz), (min(ghz), max(ghz))
 
 
+def _code_only(text):
+    """The source without its comments, trailing blanks and empty lines: what
+    a counter reading depends on.  (None of these sources has "//" or "/*"
+    inside a string literal.)"""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", l).rstrip() for l in text.splitlines())
+    return "\n".join(l for l in lines if l)
+
+
 def kernel_source_sha(kernel):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "rank_latent_routing_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "rank_latent_routing_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

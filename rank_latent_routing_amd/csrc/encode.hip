@@ -23,8 +23,9 @@
 // v_exp_f32, a v_cvt_pk_bf16_f32 per pair (which is directly the A operand of
 // P V), and v_dot2c_f32_bf16 row sums of those packed weights (the
 // normaliser sums exactly the rounded weights the numerator uses).  On gfx950
-// matrix-core and vector work largely add up rather than overlap, so this
-// per-score instruction count is what the design minimises.
+// that vector work (a v_exp_f32 alone takes 8 cycles of a SIMD) outlasts the
+// four products, which run under it, so this per-score instruction count is
+// what the design minimises.
 //
 // The first pass runs without a running maximum (weights relative to 2^0).
 // A split of n tokens is accepted when every latent's normaliser l lies in

@@ -98,8 +98,10 @@ def summarize(name, inputs):
 # (the kernel itself, shared device code, and the host code that picks its
 # grid).
 KERNEL_SOURCES = {
-    "encode_bf16_kernel": ["encode.hip", "common.hpp", "launch.hpp", "api.cpp", "plan.cpp"],
-    "merge_kernel": ["encode.hip", "common.hpp", "launch.hpp", "api.cpp", "plan.cpp"],
+    "encode_bf16_kernel": ["encode_kernel.hpp", "encode_wide.hip", "encode.hip", "common.hpp", "launch.hpp", "api.cpp",
+                           "plan.cpp"],
+    "merge_kernel": ["encode_kernel.hpp", "encode_wide.hip", "encode.hip", "common.hpp", "launch.hpp", "api.cpp",
+                     "plan.cpp"],
     "decode_bf16_kernel": ["decode.hip", "common.hpp", "launch.hpp", "api.cpp", "plan.cpp"],
 }
 COPY_BYTES = 1 << 30  # bytes read (and written) per launch of the calibration copy
@@ -154,10 +156,13 @@ def _code_only(text):
 
 
 def kernel_source_sha(kernel):
+    """Hash of a kernel's sources (code only) and of their per-source build flags."""
+    from rank_latent_routing_amd import build as lib_build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "rank_latent_routing_amd", "csrc", f)) as fh:
             h.update(_code_only(fh.read()).encode())
+        h.update(" ".join(lib_build.SOURCE_FLAGS.get(f, [])).encode())
     return h.hexdigest()[:16]
 
 

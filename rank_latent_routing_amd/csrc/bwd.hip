@@ -16,7 +16,7 @@
 // encode/decode pair at once); sums over tokens (dQ, dZ) run latent-parallel
 // over token splits in the encoder's layout (lat_bwd_kernel), with fp32
 // partials per split added by sum_splits_kernel.  The operand layouts are
-// those of the forward kernels: see encode.hip and decode.hip.
+// those of the forward kernels: see encode_kernel.hpp and decode.hip.
 #include <algorithm>
 
 #include "common.hpp"

@@ -175,6 +175,8 @@ struct EncodePlan {
 EncodePlan plan_encode(int B, int H, int M, int64_t N, int D, int is_f32, int max_splits = 0);
 
 hipError_t launch_encode_bf16(const EncodeParams& p, int D, int B, int waves, int lat_blocks, hipStream_t s);
+// The 8-wave, 32-feature encoder (encode_wide.hip) on the given grid.
+hipError_t launch_encode_bf16_wide(const EncodeParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_encode_f32(const EncodeParams& p, int D, int B, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int B, hipStream_t s);
 // Workgroups per (batch, head) of the bf16 decoder.
